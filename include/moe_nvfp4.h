@@ -1,0 +1,171 @@
+/*
+ * moe_nvfp4.h -- C ABI of the routed NVFP4 W4A4 mixture-of-experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages cited by title and section):
+ *   - router logits over E experts, top-k routed experts plus one always-on
+ *     shared expert (capy-flash README v0.5.4, synthetic test-artifact script:
+ *     "512 NVFP4 experts top-10 + shared"; Richland article, "What shipped");
+ *   - expert weights in NVFP4: E2M1 codes, UE4M3 block scales, an FP32
+ *     per-expert scale, used as published (Richland article, "What shipped");
+ *   - activations quantized the same way (W4A4) wherever an expert runs
+ *     (capy-flash README v0.5.4, "What it does" and "Serve");
+ *   - FP32 accumulation of partials (Richland article, "Why it matters");
+ *   - every selected expert is computed and combined with its router weight
+ *     (none is skipped; capy-flash README v0.7.7, "Benchmarks").
+ * Readings where the pages are silent: 16-element blocks, block scale =
+ * RNE(amax/6) on the UE4M3 grid, element codes RNE onto E2M1 with
+ * saturation, SwiGLU (h = silu(gate) * up), softmax over the k selected
+ * logits, shared-expert weight 1, element 2i in the low nibble of byte i.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer, including the workspace; the library never allocates or
+ *     frees device memory and keeps no mutable global state.
+ *   - Calls are asynchronous on `stream`; none synchronizes the host, so a
+ *     sequence of calls may be captured into a HIP graph.
+ *   - Arguments are validated on the host only; a kernel fault surfaces at
+ *     the caller's next synchronization.
+ *   - All device pointers must be 16-byte aligned (MOE_EINVAL otherwise).
+ *   - T == 0 is a successful no-op.
+ *   - Results are deterministic run to run (no floating-point atomics).
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code; moe_strerror()
+ *     names it.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* null required pointer, misaligned pointer, bad dtype   */
+  MOE_ESHAPE = -2,     /* H or I not a multiple of 32, k outside [1, min(E,32)],
+                          E outside [1, 1024], T < 0, H > 16384, I > 4096       */
+  MOE_EWORKSPACE = -3, /* workspace smaller than moe_workspace_bytes()          */
+  MOE_ELAUNCH = -4     /* a kernel launch failed (hipGetLastError)              */
+};
+
+/* One bank of NVFP4 matrices, n_exp matrices of N rows by K columns:
+ *   codes  [n_exp][N][K/2]  E2M1 codes, element 2i of a row in the low nibble
+ *                           of byte i, element 2i+1 in the high nibble
+ *   scales [n_exp][N][K/16] UE4M3 scale per 16 consecutive elements of a row
+ *                           (bit 7 must be 0; 0x7F is never used)
+ *   gscale [n_exp]          FP32 per-matrix scale
+ * A weight's value is e2m1(code) * ue4m3(scale) * gscale.                    */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+} moe_nvfp4_bank;
+
+/* One MoE layer.  Host struct; the pointers inside are device pointers.
+ *   w13 : routed experts, n_exp = E, N = 2I, K = H; rows 0..I-1 are the gate
+ *         projection, rows I..2I-1 the up projection
+ *   w2  : routed experts, n_exp = E, N = H, K = I (down projection)
+ *   sh13, sh2 : the shared expert (n_exp = 1), same shapes; ignored when
+ *         has_shared == 0
+ *   router_w : [E][H] FP32 router weights
+ *   a_gscale_in, a_gscale_mid : global scales of the activation encodings of
+ *         x and of h; powers of two (1.0 by default)                          */
+typedef struct {
+  int32_t H, I, E, k, has_shared;
+  const float* router_w;
+  moe_nvfp4_bank w13, w2, sh13, sh2;
+  float a_gscale_in, a_gscale_mid;
+} moe_layer;
+
+/* Optional dumps of intermediate values (all nullable, device pointers).
+ *   xq [T][H/2], xs [T][H/16] : A4 encoding of x (codes, UE4M3 scales)
+ *   h  [R][I] FP32            : h = silu(gate) * up before its A4 encoding
+ *   hq [R][I/2], hs [R][I/16] : A4 encoding of h
+ * R = T*k routed rows in permuted-row order, followed by T shared-expert rows
+ * (token order) when has_shared.                                              */
+typedef struct {
+  uint8_t* xq;
+  uint8_t* xs;
+  float* h;
+  uint8_t* hq;
+  uint8_t* hs;
+} moe_debug;
+
+int moe_abi_version(void);
+const char* moe_strerror(int code);
+
+/* Bytes of workspace that moe_route, moe_permute and moe_expert_ffn need for
+ * up to T_max tokens of layer L (one workspace may serve all three calls, not
+ * concurrently).  Returns 0 if L or T_max is invalid.  Host call.             */
+size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max);
+
+/* Router: logits l[t][e] = sum_h x[t][h] * router_w[e][h] (FP32 accumulation),
+ * the k largest per token in descending order (equal logits: lower expert id
+ * first), and w[t][j] = softmax over the k selected logits.
+ *   x        [T][H] BF16 hidden states (bit patterns)
+ *   logits_in [T][E] FP32, nullable: when given, these logits are used as is
+ *             (test hook for tie-breaking rules)
+ *   topk_idx [T][k] int32 out; topk_w [T][k] FP32 out
+ * Pages: capy-flash README v0.5.4, "Measured" footnote (router on tensor cores
+ * for prompt chunks; reordered sums may pick another of two tied experts).   */
+int moe_route(const moe_layer* L, const uint16_t* x, int64_t T, const float* logits_in, int32_t* topk_idx,
+              float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permutation: groups the T*k (token, slot) pairs by expert, expert id
+ * ascending and token ascending within an expert (pair id p = t*k + j).
+ *   topk_idx   [T][k] int32 in (each row: k distinct ids in [0, E))
+ *   expert_off [E+1] int32 out: exclusive prefix sum of per-expert counts
+ *   row2pair   [T*k] int32 out: pair id held by permuted row r
+ *   pair2row   [T*k] int32 out: inverse of row2pair
+ * Pages: capy-flash README v0.5.4, "What it does" (experts partitioned by id). */
+int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t* expert_off, int32_t* row2pair,
+                int32_t* pair2row, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFN, routed and shared:
+ *   (xq, xs) = A4(x) per 16-element block of H with a_gscale_in
+ *   for permuted row r (pair p = row2pair[r], token t = p / k, expert e):
+ *     gate_i, up_i = W13_e . dequant(xq, xs) in FP32, h_i = silu(gate_i)*up_i
+ *     (hq, hs) = A4(h) per 16-block of I with a_gscale_mid
+ *     y_rows[r][n] = W2_e[n] . dequant(hq, hs) in FP32
+ *   y_shared[t][n]: the same with the shared expert for every token
+ *   expert_off, row2pair as produced by moe_permute
+ *   y_rows [T*k][H] FP32 out (permuted-row order)
+ *   y_shared [T][H] FP32 out; nullable iff has_shared == 0
+ *   dbg nullable (see moe_debug)
+ * Pages: Richland article, "What shipped" (NVFP4 format) and "Why it matters"
+ * (FP32 accumulation); capy-flash README v0.5.4, "Serve" (W4A4).              */
+int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                   const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Combine: out[t] = RNE_BF16( sum_j topk_w[t][j] * y_rows[pair2row[t*k+j]]
+ *                             + y_shared[t] + residual[t] ), summed in FP32 in
+ * that order (j ascending).  y_shared nullable iff has_shared == 0; residual
+ * [T][H] BF16 nullable; out [T][H] BF16.  Needs no workspace.
+ * Pages: capy-flash README v0.7.7, "Benchmarks" (every selected expert is
+ * computed); Richland article, "Why it matters" (FP32 partials).             */
+int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared, const int32_t* pair2row,
+                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
+/* A4 encoding of a row-major [rows][cols] matrix (cols % 16 == 0):
+ *   dtype MOE_DTYPE_BF16 (x is uint16 BF16 patterns) or MOE_DTYPE_F32
+ *   gscale: power-of-two global scale (host)
+ *   codes [rows][cols/2], scales [rows][cols/16] out
+ * Per 16-element block: scale = RNE(amax/(6*gscale)) on the UE4M3 grid,
+ * saturating at 448; codes = RNE(|x|/(scale*gscale)) on the E2M1 grid,
+ * saturating at 6, sign bit = sign of x.  Exact (decided by comparisons).
+ * Pages: capy-flash README v0.5.4, "Serve" (the GPU's W4A4 quantization).    */
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
+int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
+                     uint8_t* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

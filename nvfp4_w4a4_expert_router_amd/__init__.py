@@ -1,0 +1,182 @@
+"""Routed NVFP4 W4A4 mixture-of-experts layer for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libnvfp4moe.so`` (the C ABI in include/moe_nvfp4.h).
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels; PyTorch supplies device memory and the stream.  There is no CPU
+fallback: importing this package without the built library raises.
+
+Steps (same names as the C ABI): ``moe_route`` -> ``moe_permute`` ->
+``moe_expert_ffn`` -> ``moe_combine``; ``moe_quantize_act`` exposes the A4
+activation encoding alone.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -3, -4
+MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s: %s (%d)" % (where, strerror(code), code))
+        self.code = code
+
+
+class Bank(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("gscale", ctypes.c_void_p)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("has_shared", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("w13", Bank), ("w2", Bank),
+                ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p), ("h", ctypes.c_void_p), ("hq", ctypes.c_void_p),
+                ("hs", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnvfp4moe.so is not built (run __graft_entry__.build() or "
+                          "python nvfp4_w4a4_expert_router_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    pl = ctypes.POINTER(LayerDesc)
+    L.moe_abi_version.restype = ci
+    L.moe_strerror.argtypes, L.moe_strerror.restype = [ci], ctypes.c_char_p
+    L.moe_workspace_bytes.argtypes, L.moe_workspace_bytes.restype = [pl, i64], sz
+    L.moe_route.argtypes = [pl, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.moe_permute.argtypes = [pl, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [pl, vp, i64, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz, vp]
+    L.moe_combine.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_quantize_act.argtypes = [vp, ci, i64, ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act"):
+        getattr(L, f).restype = ci
+    return L
+
+
+lib = _load()
+EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
+           "moe_combine", "moe_quantize_act")
+
+
+def strerror(code: int) -> str:
+    return lib.moe_strerror(code).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != MOE_OK:
+        raise MoEError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class MoELayer:
+    """Device-resident layer parameters plus the C descriptor that points at them.
+
+    router_w [E][H] float32; banks are dicts of uint8 codes / uint8 scales / float32
+    gscale tensors in the layouts of include/moe_nvfp4.h.  Tensors are kept alive here.
+    """
+
+    def __init__(self, H, I, E, k, router_w, w13, w2, sh13=None, sh2=None, a_gscale_in=1.0, a_gscale_mid=1.0):
+        self.H, self.I, self.E, self.k = H, I, E, k
+        self.has_shared = int(sh13 is not None)
+        self.router_w, self.w13, self.w2, self.sh13, self.sh2 = router_w, w13, w2, sh13, sh2
+
+        def bank(b):
+            return Bank() if b is None else Bank(_ptr(b["codes"]), _ptr(b["scales"]), _ptr(b["gscale"]))
+
+        self.desc = LayerDesc(H, I, E, k, self.has_shared, _ptr(router_w), bank(w13), bank(w2), bank(sh13), bank(sh2),
+                              a_gscale_in, a_gscale_mid)
+        self.a_gscale_in, self.a_gscale_mid = a_gscale_in, a_gscale_mid
+
+    def workspace_bytes(self, T_max: int) -> int:
+        return int(lib.moe_workspace_bytes(ctypes.byref(self.desc), T_max))
+
+    def workspace(self, T_max: int, device=None) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(T_max), dtype=torch.uint8, device=device or self.router_w.device)
+
+
+def moe_route(layer: MoELayer, x, topk_idx, topk_w, ws, logits_in=None, T=None, stream=None):
+    T = x.shape[0] if T is None else T
+    _check(lib.moe_route(ctypes.byref(layer.desc), _ptr(x), T, _ptr(logits_in), _ptr(topk_idx), _ptr(topk_w),
+                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "moe_route")
+
+
+def moe_permute(layer: MoELayer, topk_idx, expert_off, row2pair, pair2row, ws, T=None, stream=None):
+    T = topk_idx.shape[0] if T is None else T
+    _check(lib.moe_permute(ctypes.byref(layer.desc), _ptr(topk_idx), T, _ptr(expert_off), _ptr(row2pair),
+                           _ptr(pair2row), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "moe_permute")
+
+
+def moe_expert_ffn(layer: MoELayer, x, expert_off, row2pair, y_rows, y_shared, ws, debug=None, T=None,
+                   stream=None):
+    T = x.shape[0] if T is None else T
+    dbg = None
+    if debug is not None:
+        dbg = Debug(_ptr(debug.get("xq")), _ptr(debug.get("xs")), _ptr(debug.get("h")), _ptr(debug.get("hq")),
+                    _ptr(debug.get("hs")))
+    _check(lib.moe_expert_ffn(ctypes.byref(layer.desc), _ptr(x), T, _ptr(expert_off), _ptr(row2pair), _ptr(y_rows),
+                              _ptr(y_shared), None if dbg is None else ctypes.byref(dbg), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(layer: MoELayer, y_rows, y_shared, pair2row, topk_w, out, residual=None, T=None, stream=None):
+    T = out.shape[0] if T is None else T
+    _check(lib.moe_combine(ctypes.byref(layer.desc), T, _ptr(y_rows), _ptr(y_shared), _ptr(pair2row), _ptr(topk_w),
+                           _ptr(residual), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_quantize_act(x, codes, scales, gscale=1.0, stream=None):
+    dtype = {torch.bfloat16: MOE_DTYPE_BF16, torch.int16: MOE_DTYPE_BF16, torch.uint16: MOE_DTYPE_BF16,
+             torch.float32: MOE_DTYPE_F32}[x.dtype]
+    rows, cols = x.shape
+    _check(lib.moe_quantize_act(_ptr(x), dtype, rows, cols, gscale, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_act")
+
+
+class Buffers:
+    """Outputs and workspace of one layer call for up to T tokens (device tensors)."""
+
+    def __init__(self, layer: MoELayer, T: int, device):
+        k, H = layer.k, layer.H
+        self.T = T
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.expert_off = torch.empty(layer.E + 1, dtype=torch.int32, device=device)
+        self.row2pair = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.pair2row = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.y_rows = torch.empty((T * k, H), dtype=torch.float32, device=device)
+        self.y_shared = torch.empty((T, H), dtype=torch.float32, device=device) if layer.has_shared else None
+        self.out = torch.empty((T, H), dtype=torch.int16, device=device)
+        self.ws = layer.workspace(T, device)
+
+
+def moe_forward(layer: MoELayer, x, buf: Buffers, residual=None, debug=None, stream=None):
+    """route -> permute -> expert FFN -> combine on one stream; returns buf.out (BF16 bits as int16)."""
+    T = x.shape[0]
+    moe_route(layer, x, buf.topk_idx, buf.topk_w, buf.ws, T=T, stream=stream)
+    moe_permute(layer, buf.topk_idx, buf.expert_off, buf.row2pair, buf.pair2row, buf.ws, T=T, stream=stream)
+    moe_expert_ffn(layer, x, buf.expert_off, buf.row2pair, buf.y_rows, buf.y_shared, buf.ws, debug=debug, T=T,
+                   stream=stream)
+    moe_combine(layer, buf.y_rows, buf.y_shared, buf.pair2row, buf.topk_w, buf.out, residual=residual, T=T,
+                stream=stream)
+    return buf.out

@@ -1,0 +1,210 @@
+// C ABI of the NVFP4 W4A4 MoE layer: host-side validation, workspace layout
+// and kernel dispatch.  Declarations and the full contract are in
+// include/moe_nvfp4.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+inline bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+// the A4 comparisons are exact only for power-of-two global scales
+inline bool pow2_scale(float g) {
+  if (!(g > 0.0f) || g > 1e30f || g < 1e-30f) return false;
+  int e;
+  return frexpf(g, &e) == 0.5f;
+}
+
+int check_bank(const moe_nvfp4_bank& b) {
+  return (ptr_ok(b.codes) && ptr_ok(b.scales) && ptr_ok(b.gscale)) ? MOE_OK : MOE_EINVAL;
+}
+
+int check_shape(const moe_layer* L) {
+  if (!L) return MOE_EINVAL;
+  if (L->H <= 0 || L->I <= 0 || L->H % 32 || L->I % 32 || L->H > 16384 || L->I > 4096) return MOE_ESHAPE;
+  if (L->E < 1 || L->E > 1024) return MOE_ESHAPE;
+  if (L->k < 1 || L->k > 32 || L->k > L->E) return MOE_ESHAPE;
+  if (L->has_shared != 0 && L->has_shared != 1) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
+int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (need_router && !ptr_ok(L->router_w)) return MOE_EINVAL;
+  if (need_experts) {
+    if ((rc = check_bank(L->w13)) || (rc = check_bank(L->w2))) return rc;
+    if (L->has_shared && ((rc = check_bank(L->sh13)) || (rc = check_bank(L->sh2)))) return rc;
+    if (!pow2_scale(L->a_gscale_in) || !pow2_scale(L->a_gscale_mid)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+// workspace of each call, laid out from offset 0 (calls never overlap in time)
+size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E)); }
+
+size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
+
+struct FfnWs {
+  size_t xq, xs, xh, hh, end;
+};
+
+FfnWs ffn_ws(const moe_layer* L, int64_t T) {
+  FfnWs w;
+  const int64_t R = T * L->k + (L->has_shared ? T : 0);
+  size_t o = 0;
+  w.xq = o;
+  o = align_up(o + (size_t)T * (L->H / 2));
+  w.xs = o;
+  o = align_up(o + (size_t)T * (L->H / 16));
+  w.xh = o;
+  o = align_up(o + (size_t)T * L->H * sizeof(half_t));
+  w.hh = o;
+  o = align_up(o + (size_t)R * L->I * sizeof(half_t));
+  w.end = o;
+  return w;
+}
+
+inline int launch_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, bad dtype or scale)";
+    case MOE_ESHAPE: return "unsupported shape (H, I multiples of 32; 1 <= k <= min(E, 32); E <= 1024; T >= 0)";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
+  if (check_shape(L) != MOE_OK || T_max < 0) return 0;
+  size_t need = route_ws(L, T_max);
+  if (permute_ws(L, T_max) > need) need = permute_ws(L, T_max);
+  if (ffn_ws(L, T_max).end > need) need = ffn_ws(L, T_max).end;
+  return need < kAlign ? kAlign : need;
+}
+
+int moe_route(const moe_layer* L, const uint16_t* x, int64_t T, const float* logits_in, int32_t* topk_idx,
+              float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(topk_idx) || !ptr_ok(topk_w)) return MOE_EINVAL;
+  if (!logits_in) {
+    if ((rc = check_layer(L, true, false))) return rc;
+    if (!ptr_ok(x) || !ptr_ok(ws)) return MOE_EINVAL;
+    if (ws_bytes < route_ws(L, T)) return MOE_EWORKSPACE;
+  } else if (!aligned16(logits_in)) {
+    return MOE_EINVAL;
+  }
+  return launch_rc(launch_route(x, L->router_w, T, L->H, L->E, L->k, logits_in, topk_idx, topk_w, ws, stream));
+}
+
+int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t* expert_off, int32_t* row2pair,
+                int32_t* pair2row, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (!ptr_ok(expert_off)) return MOE_EINVAL;
+  if (T > 0 && (!ptr_ok(topk_idx) || !ptr_ok(row2pair) || !ptr_ok(pair2row) || !ptr_ok(ws))) return MOE_EINVAL;
+  if (T > 0 && ws_bytes < permute_ws(L, T)) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  return launch_rc(launch_permute(topk_idx, T, L->k, L->E, expert_off, row2pair, pair2row, ws, stream));
+}
+
+int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                   const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L, false, true);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(x) || !ptr_ok(expert_off) || !ptr_ok(row2pair) || !ptr_ok(y_rows) || !ptr_ok(ws)) return MOE_EINVAL;
+  if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
+  if (dbg && (!opt_ok(dbg->xq) || !opt_ok(dbg->xs) || !opt_ok(dbg->h) || !opt_ok(dbg->hq) || !opt_ok(dbg->hs)))
+    return MOE_EINVAL;
+  const FfnWs lay = ffn_ws(L, T);
+  if (ws_bytes < lay.end) return MOE_EWORKSPACE;
+  char* base = static_cast<char*>(ws);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + lay.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(base + lay.xs);
+  half_t* xh = reinterpret_cast<half_t*>(base + lay.xh);
+  if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs, xh, stream)))) return rc;
+  if (dbg && dbg->xq)
+    if (hipMemcpyAsync(dbg->xq, xq, (size_t)T * (L->H / 2), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return MOE_ELAUNCH;
+  if (dbg && dbg->xs)
+    if (hipMemcpyAsync(dbg->xs, xs, (size_t)T * (L->H / 16), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return MOE_ELAUNCH;
+  FfnParams p;
+  p.H = L->H;
+  p.I = L->I;
+  p.E = L->E;
+  p.k = L->k;
+  p.T = (int)T;
+  p.has_shared = L->has_shared;
+  const int64_t P = T * L->k;
+  p.n_routed_slots = (int)(P < L->E ? P : L->E);
+  p.off = expert_off;
+  p.row2pair = row2pair;
+  p.xh = xh;
+  p.w13 = L->w13;
+  p.w2 = L->w2;
+  p.sh13 = L->sh13;
+  p.sh2 = L->sh2;
+  p.g_in = L->a_gscale_in;
+  p.g_mid = L->a_gscale_mid;
+  p.hh = reinterpret_cast<half_t*>(base + lay.hh);
+  p.h_dbg = dbg ? dbg->h : nullptr;
+  p.hq_dbg = dbg ? dbg->hq : nullptr;
+  p.hs_dbg = dbg ? dbg->hs : nullptr;
+  p.y_rows = y_rows;
+  p.y_shared = L->has_shared ? y_shared : nullptr;
+  return launch_rc(launch_ffn_gemv(p, stream));
+}
+
+int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared, const int32_t* pair2row,
+                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(y_rows) || !ptr_ok(pair2row) || !ptr_ok(topk_w) || !ptr_ok(out) || !opt_ok(residual))
+    return MOE_EINVAL;
+  if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
+  return launch_rc(launch_combine(T, L->H, L->k, y_rows, L->has_shared ? y_shared : nullptr, pair2row, topk_w,
+                                  residual, out, stream));
+}
+
+int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
+                     uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 16) return MOE_ESHAPE;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_EINVAL;
+  if (!pow2_scale(gscale)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!ptr_ok(x) || !ptr_ok(codes) || !ptr_ok(scales)) return MOE_EINVAL;
+  return launch_rc(launch_quant_act(x, dtype, rows, cols, gscale, codes, scales, nullptr, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Router-weighted combine: out[t] = RNE_BF16(sum_j w[t][j] * y[pair2row[t*k+j]]
+// + y_shared[t] + residual[t]) in FP32, j ascending.  Every selected expert
+// contributes; none is dropped (capy-flash README v0.7.7, "Benchmarks");
+// partials stay in FP32 until the single final rounding (Richland article,
+// "Why it matters").  HBM-bound: (k+1) FP32 rows read and one BF16 row written
+// per token.  One thread per 4 output columns, 128-bit loads.
+#include "common.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const float* __restrict__ y_rows,
+                                                 const float* __restrict__ y_shared, const int32_t* __restrict__ p2r,
+                                                 const float* __restrict__ w, const uint16_t* __restrict__ residual,
+                                                 uint16_t* __restrict__ out) {
+  const int per_row = H / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= T * per_row) return;
+  const int64_t t = gid / per_row;
+  const int c4 = (int)(gid % per_row) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const int64_t r = p2r[t * k + j];
+    const float4 y = *reinterpret_cast<const float4*>(y_rows + r * H + c4);
+    acc.x += wj * y.x;
+    acc.y += wj * y.y;
+    acc.z += wj * y.z;
+    acc.w += wj * y.w;
+  }
+  if (y_shared) {
+    const float4 y = *reinterpret_cast<const float4*>(y_shared + t * H + c4);
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  if (residual) {
+    const uint2 rv = *reinterpret_cast<const uint2*>(residual + t * H + c4);
+    acc.x += __uint_as_float(rv.x << 16);
+    acc.y += __uint_as_float(rv.x & 0xFFFF0000u);
+    acc.z += __uint_as_float(rv.y << 16);
+    acc.w += __uint_as_float(rv.y & 0xFFFF0000u);
+  }
+  const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + t * H + c4) = make_uint2(lo, hi);
+}
+
+hipError_t launch_combine(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
+                          const float* w, const uint16_t* residual, uint16_t* out, hipStream_t s) {
+  const int64_t n = T * (H / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, H, k, y_rows, y_shared, p2r,
+                     w, residual, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

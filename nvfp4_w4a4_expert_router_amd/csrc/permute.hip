@@ -1,0 +1,112 @@
+// Token -> expert permutation: the T*k (token, slot) pairs grouped by expert id
+// (ascending), tokens ascending within an expert; pair id p = t*k + j.  Routed
+// experts are addressed by id (capy-flash README v0.5.4, "What it does").
+//
+// Integer work only; the result is unique.  Ranks inside an expert segment
+// come from per-wave bit masks: each lane (one token) sets its bit in the mask
+// of every expert it selected (atomic OR, order-free), then a token's rank
+// among the chunk's tokens of that expert is the popcount of the mask bits
+// below it.  Three kernels: per-chunk counts, a scan over (chunk, expert), and
+// the scatter.  A token selects k distinct experts, so one bit per token and
+// expert suffices.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kChunkTok = 256;  // tokens per workgroup (4 waves x 64)
+constexpr int kMaxE = 1024;
+
+// Fill this wave's masks for a chunk: masks[wave][e] bit lane = token (chunk base
+// + 64*wave + lane) selected e.
+__device__ __forceinline__ void build_masks(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                            unsigned long long (*masks)[kMaxE], int64_t t0) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  for (int e = lane; e < E; e += kWave) masks[wave][e] = 0ull;
+  __syncthreads();
+  const int64_t t = t0 + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicOr(&masks[wave][e], 1ull << lane);  // invalid ids are dropped
+    }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                    int32_t* __restrict__ cnt /*[nchunk][E]*/) {
+  __shared__ unsigned long long masks[4][kMaxE];
+  build_masks(idx, T, k, E, masks, (int64_t)blockIdx.x * kChunkTok);
+  for (int e = threadIdx.x; e < E; e += 256)
+    cnt[(int64_t)blockIdx.x * E + e] =
+        __popcll(masks[0][e]) + __popcll(masks[1][e]) + __popcll(masks[2][e]) + __popcll(masks[3][e]);
+}
+
+// One workgroup of 1024 threads: thread e walks the chunks in order (base of
+// expert e in chunk c = sum of earlier chunks' counts), then an exclusive scan
+// over experts gives expert_off; bases are shifted by it.
+__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ cnt /*in counts, out bases*/, int nchunk,
+                                                    int E, int32_t* __restrict__ off) {
+  __shared__ int32_t tot[kMaxE];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E)
+    for (int c = 0; c < nchunk; ++c) {
+      const int v = cnt[(int64_t)c * E + e];
+      cnt[(int64_t)c * E + e] = run;
+      run += v;
+    }
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1024 entries
+  for (int d = 1; d < kMaxE; d <<= 1) {
+    const int add = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += add;
+    __syncthreads();
+  }
+  const int excl = e > 0 ? tot[e - 1] : 0;
+  if (e < E) {
+    off[e] = excl;
+    for (int c = 0; c < nchunk; ++c) cnt[(int64_t)c * E + e] += excl;
+  }
+  if (e == E - 1) off[E] = tot[e];
+}
+
+__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                      const int32_t* __restrict__ base /*[nchunk][E]*/,
+                                                      int32_t* __restrict__ r2p, int32_t* __restrict__ p2r) {
+  __shared__ unsigned long long masks[4][kMaxE];
+  const int64_t t0 = (int64_t)blockIdx.x * kChunkTok;
+  build_masks(idx, T, k, E, masks, t0);
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t t = t0 + threadIdx.x;
+  if (t >= T) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= E) continue;
+    int r = base[(int64_t)blockIdx.x * E + e];
+    for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
+    r += __popcll(masks[wave][e] & below);
+    const int32_t p = (int32_t)(t * k + j);
+    r2p[r] = p;
+    p2r[p] = r;
+  }
+}
+
+size_t permute_ws_bytes(int64_t T, int E) {
+  const int64_t nchunk = (T + kChunkTok - 1) / kChunkTok;
+  return (size_t)(nchunk * E) * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* off, int32_t* r2p, int32_t* p2r,
+                          void* ws, hipStream_t s) {
+  const int nchunk = (int)((T + kChunkTok - 1) / kChunkTok);
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  if (nchunk > 0) hipLaunchKernelGGL(k_perm_count, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, cnt, nchunk, E, off);
+  if (nchunk > 0) hipLaunchKernelGGL(k_perm_scatter, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt, r2p, p2r);
+  return hipGetLastError();
+}
+
+}  // namespace moe

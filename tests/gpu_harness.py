@@ -1,0 +1,115 @@
+"""Helpers for the GPU parity tests: upload a generated layer, run the HIP path
+through the C ABI, and check every step against the oracle (teacher-forced
+where the checker accepts a near-tie or near-threshold difference)."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import checker
+import oracle
+import nvfp4_w4a4_expert_router_amd as moe
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bank_to_dev(b):
+    return {"codes": to_dev(b["codes"]), "scales": to_dev(b["scales"]), "gscale": to_dev(b["gscale"])}
+
+
+def device_layer(L, router_w=None) -> moe.MoELayer:
+    sh = L.shape
+    rw = L.router_w if router_w is None else router_w
+    return moe.MoELayer(sh.H, sh.I, sh.E, sh.k, to_dev(rw), bank_to_dev(L.w13), bank_to_dev(L.w2),
+                        bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid)
+
+
+def run_layer(DL: moe.MoELayer, x: np.ndarray, residual=None, dump=("xq", "xs", "hq", "hs"), logits_in=None):
+    """Run route -> permute -> ffn -> combine; returns numpy copies of every output and dump."""
+    T = x.shape[0]
+    H, I, k = DL.H, DL.I, DL.k
+    R = T * k + (T if DL.has_shared else 0)
+    xd = to_dev(x.view(np.int16))
+    buf = moe.Buffers(DL, T, DEV)
+    dbg = {}
+    if "xq" in dump:
+        dbg["xq"] = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+    if "xs" in dump:
+        dbg["xs"] = torch.empty((T, H // 16), dtype=torch.uint8, device=DEV)
+    if "h" in dump:
+        dbg["h"] = torch.empty((R, I), dtype=torch.float32, device=DEV)
+    if "hq" in dump:
+        dbg["hq"] = torch.empty((R, I // 2), dtype=torch.uint8, device=DEV)
+    if "hs" in dump:
+        dbg["hs"] = torch.empty((R, I // 16), dtype=torch.uint8, device=DEV)
+    res = None if residual is None else to_dev(residual.view(np.int16))
+    lg = None if logits_in is None else to_dev(logits_in.astype(np.float32))
+    moe.moe_route(DL, xd, buf.topk_idx, buf.topk_w, buf.ws, logits_in=lg, T=T)
+    moe.moe_permute(DL, buf.topk_idx, buf.expert_off, buf.row2pair, buf.pair2row, buf.ws, T=T)
+    moe.moe_expert_ffn(DL, xd, buf.expert_off, buf.row2pair, buf.y_rows, buf.y_shared, buf.ws, debug=dbg, T=T)
+    moe.moe_combine(DL, buf.y_rows, buf.y_shared, buf.pair2row, buf.topk_w, buf.out, residual=res, T=T)
+    torch.cuda.synchronize()
+    out = {"idx": buf.topk_idx.cpu().numpy(), "w": buf.topk_w.cpu().numpy(), "off": buf.expert_off.cpu().numpy(),
+           "r2p": buf.row2pair.cpu().numpy(), "p2r": buf.pair2row.cpu().numpy(),
+           "y_rows": buf.y_rows.cpu().numpy(), "out": buf.out.cpu().numpy().view(np.uint16)}
+    if buf.y_shared is not None:
+        out["y_shared"] = buf.y_shared.cpu().numpy()
+    for key, t in dbg.items():
+        out[key] = t.cpu().numpy()
+    return out
+
+
+def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
+    """Check GPU results g (from run_layer) against the oracle on `tokens` (default all)."""
+    rep = checker.Report() if rep is None else rep
+    sh = L.shape
+    T = x.shape[0]
+    t0 = time.time()
+    if logits64 is None:
+        logits64 = oracle.router_logits(x, L.router_w)
+    idx_ad, w_g = checker.check_topk(g["idx"], g["w"], logits64, sh.k, rep)
+    checker.check_permutation(idx_ad, sh.E, g["off"], g["r2p"], g["p2r"])
+    xq_o, xs_o = oracle.quantize(oracle.bf16_to_f64(x), L.a_gscale_in)
+    assert np.array_equal(g["xq"], xq_o), "A4(x) codes differ"
+    assert np.array_equal(g["xs"], xs_o), "A4(x) scales differ"
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, dtype=np.int32)
+    n = tok.shape[0]
+    a_row = np.repeat(tok, sh.k).astype(np.int32)
+    a_exp = idx_ad[tok].reshape(-1).astype(np.int32)
+    rows = g["p2r"][(tok[:, None] * sh.k + np.arange(sh.k)[None, :]).reshape(-1)]
+    srows = T * sh.k + tok
+    r_o = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
+    s_o = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
+                             L.a_gscale_mid)
+    checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid, rep, "h")
+    checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows], L.a_gscale_mid, rep,
+                          "hsh")
+    if "h" in g:
+        hr = g["h"][rows].astype(np.float64)
+        d = np.abs(hr - r_o["h"]) / (np.abs(r_o["h"]).max() + 1e-30)
+        rep["h_fp32_maxrel"] = float(d.max()) if d.size else 0.0
+    # teacher-forced down projection with the GPU's h codes
+    r_t = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid,
+                             hq_in=g["hq"][rows], hs_in=g["hs"][rows])
+    s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
+                             L.a_gscale_mid, hq_in=g["hq"][srows], hs_in=g["hs"][srows])
+    checker.check_fp32_rows(g["y_rows"][rows], r_t["y"], rep, "y_rows")
+    checker.check_fp32_rows(g["y_shared"][tok], s_t["y"], rep, "y_shared")
+    resid = None if residual is None else residual[tok]
+    o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_g[tok], s_t["y"], resid)
+    checker.check_output(g["out"][tok], o64, o16, rep)
+    rep["oracle_s"] = round(time.time() - t0, 2)
+    rep["checked_tokens"] = n
+    return rep

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every symbol include/moe_nvfp4.h declares, and
+turns bad arguments into the documented error codes on the host (CPU only: no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_w4a4_expert_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
+              "moe_workspace_bytes", "moe_strerror", "moe_abi_version"):
+        assert f in names, f
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), "missing export " + f
+
+
+def test_abi_version_and_strerror():
+    assert moe.lib.moe_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert moe.strerror(code) and moe.strerror(code) != "unknown error"
+    assert moe.strerror(-99) == "unknown error"
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fake_bank():
+    return moe.Bank(FAKE, FAKE, FAKE)
+
+
+def layer(H=2048, I=512, E=512, k=10, shared=1, **kw):
+    d = moe.LayerDesc(H, I, E, k, shared, FAKE, fake_bank(), fake_bank(), fake_bank(), fake_bank(), 1.0, 1.0)
+    for a, v in kw.items():
+        setattr(d, a, v)
+    return d
+
+
+def route(L, T=4, x=FAKE, idx=FAKE, w=FAKE, ws=FAKE, wsb=1 << 30):
+    return moe.lib.moe_route(ctypes.byref(L) if L is not None else None, x, T, None, idx, w, ws, wsb, None)
+
+
+@pytest.mark.parametrize("H,I,E,k", [(2000, 512, 512, 10), (2048, 500, 512, 10), (2048, 512, 0, 1),
+                                     (2048, 512, 2048, 10), (2048, 512, 8, 9), (2048, 512, 512, 0),
+                                     (2048, 512, 512, 33), (32768, 512, 512, 10), (2048, 8192, 512, 10)])
+def test_bad_shapes(H, I, E, k):
+    L = layer(H, I, E, k)
+    assert route(L) == moe.MOE_ESHAPE
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(L), 16) == 0
+
+
+def test_null_and_misaligned_pointers():
+    assert route(None) == moe.MOE_EINVAL
+    assert route(layer(), x=None) == moe.MOE_EINVAL
+    assert route(layer(), idx=FAKE + 4) == moe.MOE_EINVAL
+    assert route(layer(router_w=None)) == moe.MOE_EINVAL
+    L = layer()
+    L.w13.codes = FAKE + 8
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+
+
+def test_non_power_of_two_activation_scale():
+    L = layer(a_gscale_in=3.0)
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+    assert moe.lib.moe_quantize_act(FAKE, 0, 4, 64, 0.75, FAKE, FAKE, None) == moe.MOE_EINVAL
+
+
+def test_shared_output_required_when_shared():
+    L = layer()
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+
+
+def test_negative_T_and_zero_T():
+    L = layer()
+    assert route(L, T=-1) == moe.MOE_ESHAPE
+    assert route(L, T=0, x=None, idx=None, w=None, ws=None) == moe.MOE_OK
+    assert moe.lib.moe_permute(ctypes.byref(L), None, 0, FAKE, None, None, None, 0, None) == moe.MOE_OK
+    assert moe.lib.moe_expert_ffn(ctypes.byref(L), None, 0, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert moe.lib.moe_combine(ctypes.byref(L), 0, None, None, None, None, None, None, None) == moe.MOE_OK
+    assert moe.lib.moe_quantize_act(None, 0, 0, 64, 1.0, None, None, None) == moe.MOE_OK
+
+
+def test_workspace_too_small():
+    L = layer()
+    need = moe.lib.moe_workspace_bytes(ctypes.byref(L), 4)
+    assert need > 0
+    assert route(L, wsb=0) == moe.MOE_EWORKSPACE
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 256, None)
+    assert rc == moe.MOE_EWORKSPACE
+    rc = moe.lib.moe_permute(ctypes.byref(L), FAKE, 100000, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert rc == moe.MOE_EWORKSPACE
+
+
+def test_workspace_monotone_in_T():
+    L = layer()
+    sizes = [moe.lib.moe_workspace_bytes(ctypes.byref(L), T) for T in (1, 4, 4096, 15360)]
+    assert sizes == sorted(sizes) and all(s % 256 == 0 for s in sizes)
+
+
+def test_bad_dtype_and_cols():
+    assert moe.lib.moe_quantize_act(FAKE, 7, 4, 64, 1.0, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_quantize_act(FAKE, 0, 4, 60, 1.0, FAKE, FAKE, None) == moe.MOE_ESHAPE

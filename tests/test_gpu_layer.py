@@ -1,0 +1,244 @@
+"""GPU parity of the whole layer (route -> permute -> expert FFN -> combine) through
+the C ABI, against the FP64 oracle on the same seeded inputs.
+
+Sizes: the tiny layer in full; the decode layer at 1 and 4 tokens in full; a
+ragged token count that spans several permutation chunks; the 4,096- and
+15,360-token prefill chunks with Zipf-skewed routing on sampled tokens (every
+token's routing, permutation and A4(x) are still checked in full); the
+15,360-token tie-stress variant; degenerate inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import checker
+import gen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gpu_harness as gh
+    import nvfp4_w4a4_expert_router_amd as moe
+
+_layers = {}
+
+
+def layer_for(cfg):
+    if cfg not in _layers:
+        L = gen.make_layer(cfg)
+        _layers[cfg] = (L, gh.device_layer(L))
+    return _layers[cfg]
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s), dtype=np.int32)
+
+
+@pytest.mark.parametrize("cfg,T", [(0, 8), (1, 1), (1, 4), (1, 257)])
+def test_layer_full(cfg, T):
+    gh.log("case: config %d T=%d" % (cfg, T))
+    L, DL = layer_for(cfg)
+    x = gen.make_tokens(cfg, T, step=0 if T != 257 else 7)
+    g = gh.run_layer(DL, x, dump=("xq", "xs", "hq", "hs", "h"))
+    rep = gh.check_layer(L, x, g, tokens=None if T <= 64 else sample_tokens(T, 48, T))
+    gh.log("  ", rep.line())
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 4096), (3, 15360)])
+def test_layer_prefill_sampled(cfg, T):
+    gh.log("case: config %d T=%d (Zipf routing)" % (cfg, T))
+    L, DL = layer_for(cfg)
+    x = gen.make_tokens(cfg, T)
+    g = gh.run_layer(DL, x)
+    counts = np.diff(g["off"])
+    gh.log("   expert load: max %d min %d (head share %.3f)" % (counts.max(), counts.min(), counts.max() / T))
+    rep = gh.check_layer(L, x, g, tokens=sample_tokens(T, 40, cfg))
+    gh.log("  ", rep.line())
+
+
+def tie_stress_inputs(L, x, n_pairs=32, frac=0.01, seed=99):
+    """Twin router rows that agree except on the last 16 coordinates; chosen tokens get
+    x = 0 there, so the twins' logits are exactly equal and sit at ranks k and k+1."""
+    sh = L.shape
+    H, E, k = sh.H, sh.E, sh.k
+    rng = np.random.default_rng(seed)
+    wr = L.router_w.copy()
+    ids = rng.permutation(E)[:2 * n_pairs]
+    pairs = [(int(ids[2 * i]), int(ids[2 * i + 1])) for i in range(n_pairs)]
+    for a, b in pairs:
+        wr[b, :H - 16] = wr[a, :H - 16]
+    x0 = x.copy()
+    x0[:, H - 16:] = 0
+    lg = oracle.router_logits(x0, wr)
+    cand = []
+    for t in range(x.shape[0]):
+        for a, b in pairs:
+            v = lg[t, a]
+            assert v == lg[t, b]
+            if (lg[t] > v).sum() == k - 1:
+                cand.append((t, a, b))
+                break
+    rng.shuffle(cand)
+    chosen = cand[:int(round(frac * x.shape[0]))]
+    xt = x.copy()
+    for t, _, _ in chosen:
+        xt[t, H - 16:] = 0
+    return wr, xt, chosen
+
+
+def test_layer_tie_stress_long_prefill():
+    cfg, T = 3, 15360
+    gh.log("case: config 3 tie-stress T=%d" % T)
+    L, _ = layer_for(cfg)
+    x = gen.make_tokens(cfg, T, step=1)
+    wr, xt, chosen = tie_stress_inputs(L, x)
+    assert len(chosen) == 154, len(chosen)
+    DLt = gh.device_layer(L, router_w=wr)
+    g = gh.run_layer(DLt, xt)
+    for t, a, b in chosen:
+        assert min(a, b) in g["idx"][t] and max(a, b) not in g["idx"][t], (t, a, b, g["idx"][t])
+    import copy
+    Lt = copy.copy(L)
+    Lt.router_w = wr
+    tok = np.array(sorted({t for t, _, _ in chosen[:24]} | set(sample_tokens(T, 16, 5).tolist())), np.int32)
+    rep = gh.check_layer(Lt, xt, g, tokens=tok)
+    gh.log("  ", rep.line(), "tied tokens:", len(chosen))
+
+
+def test_route_injected_duplicate_logits():
+    """logits_in with exact duplicates at every rank 1..11: lower id first, bit-exact."""
+    L, DL = layer_for(1)
+    E, k = L.shape.E, L.shape.k
+    rng = np.random.default_rng(4)
+    T = 300
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    for t in range(T):
+        order = np.argsort(-lg[t], kind="stable")
+        r = t % 11
+        lg[t, order[r + 1]] = lg[t, order[r]]  # duplicate at rank r / r+1
+    lg[:20] = 0.5  # all equal
+    lg[20:25, :] = -1.0
+    lg[20:25, 100:110] = 2.0  # a block of equal winners
+    idx = torch.empty((T, k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=gh.DEV)
+    moe.moe_route(DL, None, idx, w, None, logits_in=gh.to_dev(lg), T=T)
+    torch.cuda.synchronize()
+    idx_o, w_o = oracle.topk_softmax(lg.astype(np.float64), k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    assert np.allclose(w.cpu().numpy(), w_o, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("kind", ["one_expert", "k_equals_E", "ragged_many_chunks"])
+def test_permute_adversarial(kind):
+    E = 32 if kind == "k_equals_E" else 512
+    k = E if kind == "k_equals_E" else (1 if kind == "one_expert" else 10)
+    DL = moe.MoELayer(256, 128, E, k, torch.empty(1, device=gh.DEV), None, None)
+    T = {"one_expert": 5000, "k_equals_E": 300, "ragged_many_chunks": 15361}[kind]
+    rng = np.random.default_rng(T)
+    if kind == "one_expert":
+        idx = np.full((T, 1), 137, np.int32)
+    elif kind == "k_equals_E":
+        idx = np.array([rng.permutation(E) for _ in range(T)], np.int32)
+    else:
+        idx = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], np.int32)
+    d_idx = gh.to_dev(idx)
+    off = torch.empty(E + 1, dtype=torch.int32, device=gh.DEV)
+    r2p = torch.empty(T * k, dtype=torch.int32, device=gh.DEV)
+    p2r = torch.empty(T * k, dtype=torch.int32, device=gh.DEV)
+    ws = DL.workspace(T, gh.DEV)
+    moe.moe_permute(DL, d_idx, off, r2p, p2r, ws, T=T)
+    torch.cuda.synchronize()
+    checker.check_permutation(idx, E, off.cpu().numpy(), r2p.cpu().numpy(), p2r.cpu().numpy())
+
+
+def test_zero_input_and_residual():
+    L, DL = layer_for(1)
+    T = 4
+    x = np.zeros((T, L.shape.H), np.uint16)
+    g = gh.run_layer(DL, x)
+    assert np.all((g["out"] & 0x7FFF) == 0)
+    res = gen.make_tokens(1, T, step=11)
+    g2 = gh.run_layer(DL, x, residual=res)
+    assert np.array_equal(g2["out"], res)
+
+
+def test_residual_path_parity():
+    L, DL = layer_for(0)
+    x = gen.make_tokens(0, 8, step=2)
+    res = gen.make_tokens(0, 8, step=3)
+    g = gh.run_layer(DL, x, residual=res)
+    rep = gh.check_layer(L, x, g, residual=res)
+    gh.log("  ", rep.line())
+
+
+def test_determinism_and_equivariance():
+    L, DL = layer_for(1)
+    T = 64
+    x = gen.make_tokens(1, T, step=5)
+    x[40] = x[3]  # a duplicated token
+    a = gh.run_layer(DL, x)
+    b = gh.run_layer(DL, x)
+    for key in ("idx", "w", "off", "r2p", "p2r", "y_rows", "out", "hq", "hs"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["out"][40], a["out"][3])
+    perm = np.random.default_rng(2).permutation(T)
+    c = gh.run_layer(DL, x[perm])
+    assert np.array_equal(c["out"], a["out"][perm])
+
+
+def test_quantize_act_exhaustive_bf16():
+    """Every finite BF16 value under every nonzero scale (blocks whose amax pins the
+    scale), GPU moe_quantize_act vs the oracle, bit-exact."""
+    b = np.arange(1 << 16, dtype=np.uint32)
+    f = (b << 16).view(np.float32)
+    vals = f[np.isfinite(f)]
+    blocks = []
+    for c in range(1, 127):
+        s = np.float32(oracle.ue4m3(c))
+        v = vals[np.abs(vals) <= 6 * s]
+        v = np.concatenate([v, np.zeros((-len(v)) % 15, np.float32)]).reshape(-1, 15)
+        blocks.append(np.concatenate([np.full((v.shape[0], 1), 6 * s, np.float32), v], axis=1))
+    blk = np.concatenate(blocks).astype(np.float32)
+    bits = (blk.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), blk)
+    rows = blk.shape[0]
+    codes = torch.empty((rows, 8), dtype=torch.uint8, device=gh.DEV)
+    scales = torch.empty((rows, 1), dtype=torch.uint8, device=gh.DEV)
+    moe.moe_quantize_act(gh.to_dev(bits.view(np.int16)), codes, scales)
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize(blk.astype(np.float64))
+    assert np.array_equal(scales.cpu().numpy(), so)
+    assert np.array_equal(codes.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("g", [1.0, 0.125, 16.0])
+def test_quantize_act_fp32_thresholds(g):
+    """FP32 inputs at and next to every scale and code threshold, plus random values."""
+    rng = np.random.default_rng(int(g * 8))
+    pts = []
+    for c in range(126):
+        m = np.float32(6 * g * 0.5 * (oracle.ue4m3(c) + oracle.ue4m3(c + 1)))
+        pts += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(np.inf))]
+    amax = np.array(pts, np.float32)
+    n = amax.shape[0]
+    blk = (rng.uniform(-1, 1, (n, 16)) * amax[:, None]).astype(np.float32)
+    blk[:, 3] = amax * np.where(rng.random(n) < 0.5, 1, -1).astype(np.float32)
+    s = np.array([oracle.ue4m3(oracle.scale_code(float(a), g)) * g for a in amax], np.float32)
+    t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    for j in range(7):  # element thresholds and neighbours in columns 4..15
+        blk[:, 4 + j] = t[j] * s
+        if j < 4:
+            blk[:, 11 + j] = np.nextafter(t[j] * s, np.float32(np.inf))
+    rnd = (rng.standard_normal((4000, 16)) * np.exp2(rng.uniform(-12, 8, (4000, 1)))).astype(np.float32)
+    blk = np.concatenate([blk, rnd])
+    rows = blk.shape[0]
+    codes = torch.empty((rows, 8), dtype=torch.uint8, device=gh.DEV)
+    scales = torch.empty((rows, 1), dtype=torch.uint8, device=gh.DEV)
+    moe.moe_quantize_act(gh.to_dev(blk), codes, scales, gscale=g)
+    torch.cuda.synchronize()
+    qo, so = oracle.quantize(blk.astype(np.float64), g)
+    assert np.array_equal(scales.cpu().numpy(), so)
+    assert np.array_equal(codes.cpu().numpy(), qo)
