@@ -88,13 +88,20 @@ typedef struct {
  *   h  [R][I] FP32            : h = silu(gate) * up before its A4 encoding
  *   hq [R][I/2], hs [R][I/16] : A4 encoding of h
  * R = T*k routed rows in permuted-row order, followed by T shared-expert rows
- * (token order) when has_shared.                                              */
+ * (token order) when has_shared.
+ *   events (host array, nullable): 2*MOE_FFN_KERNELS created HIP events;
+ *   events[2i] and events[2i+1] are recorded on the call's stream right before
+ *   and right after kernel i of moe_expert_ffn (0: A4(x), 1: gate/up + SwiGLU
+ *   + A4(h), 2: down projection).  The kernels are the same with or without
+ *   dumps and events.                                                         */
+#define MOE_FFN_KERNELS 3
 typedef struct {
   uint8_t* xq;
   uint8_t* xs;
   float* h;
   uint8_t* hq;
   uint8_t* hs;
+  hipEvent_t* events;
 } moe_debug;
 
 int moe_abi_version(void);
@@ -152,6 +159,24 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
  * computed); Richland article, "Why it matters" (FP32 partials).             */
 int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared, const int32_t* pair2row,
                 const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
+/* The whole layer in one call: route -> permute -> expert FFN -> combine, with
+ * every output of the four calls above written exactly as they write it
+ * (topk_idx, topk_w [T][k]; expert_off [E+1]; row2pair, pair2row [T*k];
+ * y_rows [T*k][H]; y_shared [T][H] (nullable iff !has_shared); out [T][H];
+ * residual nullable).  For decode batches (T <= 4, H <= 2048, E <= 512, no
+ * dumps requested; events allowed) it runs fused in four kernels: FP64 router
+ * logits (events 0/1 of moe_debug), gate/up (events 2/3),
+ * whose workgroups select the top k, form the softmax weights and derive the
+ * permutation themselves; down projection (events 4/5); combine.  Otherwise it runs the four
+ * calls in order.  Results are identical either way.  ws must hold
+ * moe_workspace_bytes(L, T_max) bytes with T <= T_max.
+ * Pages: capy-flash README v0.5.4, "What it does" (a routed layer computed
+ * per expert id with the W4A4 quantization).                                */
+int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const uint16_t* residual,
+                      int32_t* topk_idx, float* topk_w, int32_t* expert_off, int32_t* row2pair, int32_t* pair2row,
+                      float* y_rows, float* y_shared, uint16_t* out, const moe_debug* dbg, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 /* A4 encoding of a row-major [rows][cols] matrix (cols % 16 == 0):
  *   dtype MOE_DTYPE_BF16 (x is uint16 BF16 patterns) or MOE_DTYPE_F32

@@ -39,9 +39,12 @@ class LayerDesc(ctypes.Structure):
                 ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float)]
 
 
+FFN_KERNELS = 3  # A4(x), gate/up + SwiGLU + A4(h), down
+
+
 class Debug(ctypes.Structure):
     _fields_ = [("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p), ("h", ctypes.c_void_p), ("hq", ctypes.c_void_p),
-                ("hs", ctypes.c_void_p)]
+                ("hs", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p))]
 
 
 def _load():
@@ -59,14 +62,16 @@ def _load():
     L.moe_expert_ffn.argtypes = [pl, vp, i64, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz, vp]
     L.moe_combine.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp, vp]
     L.moe_quantize_act.argtypes = [vp, ci, i64, ctypes.c_int32, ctypes.c_float, vp, vp, vp]
-    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act"):
+    L.moe_layer_forward.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz,
+                                    vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward"):
         getattr(L, f).restype = ci
     return L
 
 
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_quantize_act")
+           "moe_combine", "moe_quantize_act", "moe_layer_forward")
 
 
 def strerror(code: int) -> str:
@@ -127,13 +132,25 @@ def moe_permute(layer: MoELayer, topk_idx, expert_off, row2pair, pair2row, ws, T
            "moe_permute")
 
 
+def _debug(debug):
+    """moe_debug from a dict of optional device tensors and/or 2 * FFN_KERNELS recorded events."""
+    if debug is None:
+        return None
+    evs = debug.get("events")  # sequence of 2 * FFN_KERNELS recorded torch.cuda.Event
+    ev_arr = None
+    if evs is not None:
+        assert len(evs) == 2 * FFN_KERNELS
+        ev_arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    dbg = Debug(_ptr(debug.get("xq")), _ptr(debug.get("xs")), _ptr(debug.get("h")), _ptr(debug.get("hq")),
+                _ptr(debug.get("hs")), ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if evs else None)
+    dbg._keep = ev_arr
+    return dbg
+
+
 def moe_expert_ffn(layer: MoELayer, x, expert_off, row2pair, y_rows, y_shared, ws, debug=None, T=None,
                    stream=None):
     T = x.shape[0] if T is None else T
-    dbg = None
-    if debug is not None:
-        dbg = Debug(_ptr(debug.get("xq")), _ptr(debug.get("xs")), _ptr(debug.get("h")), _ptr(debug.get("hq")),
-                    _ptr(debug.get("hs")))
+    dbg = _debug(debug)
     _check(lib.moe_expert_ffn(ctypes.byref(layer.desc), _ptr(x), T, _ptr(expert_off), _ptr(row2pair), _ptr(y_rows),
                               _ptr(y_shared), None if dbg is None else ctypes.byref(dbg), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(stream)), "moe_expert_ffn")
@@ -168,6 +185,21 @@ class Buffers:
         self.y_shared = torch.empty((T, H), dtype=torch.float32, device=device) if layer.has_shared else None
         self.out = torch.empty((T, H), dtype=torch.int16, device=device)
         self.ws = layer.workspace(T, device)
+
+
+def moe_layer_forward(layer: MoELayer, x, buf: Buffers, residual=None, T=None, debug=None, topk=None,
+                      stream=None):
+    """The whole layer in one library call (fused kernels for decode batches); returns buf.out.
+
+    topk: optional (topk_idx, topk_w) tensors to write the routing into instead of buf's."""
+    T = x.shape[0] if T is None else T
+    idx, w = (buf.topk_idx, buf.topk_w) if topk is None else topk
+    dbg = _debug(debug)
+    _check(lib.moe_layer_forward(ctypes.byref(layer.desc), _ptr(x), T, _ptr(residual), _ptr(idx), _ptr(w),
+                                 _ptr(buf.expert_off), _ptr(buf.row2pair), _ptr(buf.pair2row), _ptr(buf.y_rows),
+                                 _ptr(buf.y_shared), _ptr(buf.out), None if dbg is None else ctypes.byref(dbg),
+                                 _ptr(buf.ws), buf.ws.numel(), _stream(stream)), "moe_layer_forward")
+    return buf.out
 
 
 def moe_forward(layer: MoELayer, x, buf: Buffers, residual=None, debug=None, stream=None):

@@ -96,11 +96,18 @@ const char* moe_strerror(int code) {
   }
 }
 
+// FP64 logits of the fused decode path sit before the expert-FFN workspace
+size_t fused_logits_ws(const moe_layer* L, int64_t T) {
+  const int64_t t = T < 4 ? T : 4;
+  return align_up((size_t)t * L->E * sizeof(double));
+}
+
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
   if (check_shape(L) != MOE_OK || T_max < 0) return 0;
   size_t need = route_ws(L, T_max);
   if (permute_ws(L, T_max) > need) need = permute_ws(L, T_max);
   if (ffn_ws(L, T_max).end > need) need = ffn_ws(L, T_max).end;
+  need += fused_logits_ws(L, T_max);
   return need < kAlign ? kAlign : need;
 }
 
@@ -150,14 +157,24 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + lay.xq);
   uint8_t* xs = reinterpret_cast<uint8_t*>(base + lay.xs);
   half_t* xh = reinterpret_cast<half_t*>(base + lay.xh);
-  if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs, xh, stream)))) return rc;
+  hipEvent_t* ev = dbg ? dbg->events : nullptr;
+  const bool stream_path = ffn_stream_supported(L->H, L->I);
+  const bool want_xdump = dbg && (dbg->xq || dbg->xs);
+  // kernel 0: A4(x) into the workspace (the streaming kernels encode x themselves
+  // and need it only for the dumps)
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
+  if (!stream_path || want_xdump)
+    if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
+                                         stream_path ? nullptr : xh, stream))))
+      return rc;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
   if (dbg && dbg->xq)
     if (hipMemcpyAsync(dbg->xq, xq, (size_t)T * (L->H / 2), hipMemcpyDeviceToDevice, stream) != hipSuccess)
       return MOE_ELAUNCH;
   if (dbg && dbg->xs)
     if (hipMemcpyAsync(dbg->xs, xs, (size_t)T * (L->H / 16), hipMemcpyDeviceToDevice, stream) != hipSuccess)
       return MOE_ELAUNCH;
-  FfnParams p;
+  FfnParams p = {};
   p.H = L->H;
   p.I = L->I;
   p.E = L->E;
@@ -168,6 +185,7 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.n_routed_slots = (int)(P < L->E ? P : L->E);
   p.off = expert_off;
   p.row2pair = row2pair;
+  p.x = x;
   p.xh = xh;
   p.w13 = L->w13;
   p.w2 = L->w2;
@@ -181,7 +199,17 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.hs_dbg = dbg ? dbg->hs : nullptr;
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
-  return launch_rc(launch_ffn_gemv(p, stream));
+  if (ffn_decode_supported(L->H, L->I, T)) {
+    p.shared_split = 1;
+    if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
+    return launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
+  }
+  if (stream_path) {
+    if ((rc = launch_rc(launch_gateup_stream(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
+    return launch_rc(launch_down_stream(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
+  }
+  if ((rc = launch_rc(launch_ffn_gateup(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
+  return launch_rc(launch_ffn_down(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
 }
 
 int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared, const int32_t* pair2row,
@@ -195,6 +223,70 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
   return launch_rc(launch_combine(T, L->H, L->k, y_rows, L->has_shared ? y_shared : nullptr, pair2row, topk_w,
                                   residual, out, stream));
+}
+
+int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const uint16_t* residual,
+                      int32_t* topk_idx, float* topk_w, int32_t* expert_off, int32_t* row2pair, int32_t* pair2row,
+                      float* y_rows, float* y_shared, uint16_t* out, const moe_debug* dbg, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L, true, true);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(x) || !ptr_ok(topk_idx) || !ptr_ok(topk_w) || !ptr_ok(expert_off) || !ptr_ok(row2pair) ||
+      !ptr_ok(pair2row) || !ptr_ok(y_rows) || !ptr_ok(out) || !ptr_ok(ws) || !opt_ok(residual))
+    return MOE_EINVAL;
+  if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
+  const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
+  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps) {
+    if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
+    if ((rc = moe_permute(L, topk_idx, T, expert_off, row2pair, pair2row, ws, ws_bytes, stream))) return rc;
+    if ((rc = moe_expert_ffn(L, x, T, expert_off, row2pair, y_rows, y_shared, dbg, ws, ws_bytes, stream))) return rc;
+    return moe_combine(L, T, y_rows, y_shared, pair2row, topk_w, residual, out, stream);
+  }
+  const size_t lg_bytes = fused_logits_ws(L, T);
+  const FfnWs lay = ffn_ws(L, T);
+  if (ws_bytes < lg_bytes + lay.end) return MOE_EWORKSPACE;
+  char* base = static_cast<char*>(ws);
+  double* logits = reinterpret_cast<double*>(base);
+  char* fbase = base + lg_bytes;
+  hipEvent_t* ev = dbg ? dbg->events : nullptr;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
+  if ((rc = launch_rc(launch_router_logits64(x, L->router_w, T, L->H, L->E, logits, stream)))) return rc;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
+  FfnParams p = {};
+  p.H = L->H;
+  p.I = L->I;
+  p.E = L->E;
+  p.k = L->k;
+  p.T = (int)T;
+  p.has_shared = L->has_shared;
+  const int64_t P = T * L->k;
+  p.n_routed_slots = (int)(P < L->E ? P : L->E);
+  p.off = expert_off;
+  p.row2pair = row2pair;
+  p.x = x;
+  p.w13 = L->w13;
+  p.w2 = L->w2;
+  p.sh13 = L->sh13;
+  p.sh2 = L->sh2;
+  p.g_in = L->a_gscale_in;
+  p.g_mid = L->a_gscale_mid;
+  p.hh = reinterpret_cast<half_t*>(fbase + lay.hh);
+  p.y_rows = y_rows;
+  p.y_shared = L->has_shared ? y_shared : nullptr;
+  p.shared_split = 1;
+  p.logits64 = logits;
+  p.out_idx = topk_idx;
+  p.out_w = topk_w;
+  p.out_off = expert_off;
+  p.out_r2p = row2pair;
+  p.out_p2r = pair2row;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ELAUNCH;
+  if ((rc = launch_rc(launch_gateup_fused(p, stream)))) return rc;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ELAUNCH;
+  if ((rc = launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr)))) return rc;
+  return launch_rc(launch_combine(T, L->H, L->k, y_rows, p.y_shared, pair2row, topk_w, residual, out, stream));
 }
 
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,

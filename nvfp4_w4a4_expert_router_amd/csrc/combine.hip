@@ -17,15 +17,31 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
   if (gid >= T * per_row) return;
   const int64_t t = gid / per_row;
   const int c4 = (int)(gid % per_row) * 4;
+  // all row indices and weights first, then every row load, then the sums in
+  // slot order (loads in flight together instead of one round trip per slot)
+  constexpr int kMaxK = 32;
+  int64_t r[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      r[j] = p2r[t * k + j];
+      wj[j] = w[t * k + j];
+    }
+  }
+  float4 y[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) y[j] = *reinterpret_cast<const float4*>(y_rows + r[j] * H + c4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const int64_t r = p2r[t * k + j];
-    const float4 y = *reinterpret_cast<const float4*>(y_rows + r * H + c4);
-    acc.x += wj * y.x;
-    acc.y += wj * y.y;
-    acc.z += wj * y.z;
-    acc.w += wj * y.w;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      acc.x += wj[j] * y[j].x;
+      acc.y += wj[j] * y[j].y;
+      acc.z += wj[j] * y[j].z;
+      acc.w += wj[j] * y[j].w;
+    }
   }
   if (y_shared) {
     const float4 y = *reinterpret_cast<const float4*>(y_shared + t * H + c4);

@@ -86,8 +86,179 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes): 32-bit per-lane offsets, a
+// wave-uniform scalar offset, and reads past the end return zero.  Word 3 is
+// the gfx9-family raw-buffer configuration (32-bit data format).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Wave-wide max / min through DPP moves (no LDS round trips).  The sequence
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror,
+// row_bcast:15 (rows 1, 3), row_bcast:31 (rows 2, 3) leaves the wave result in
+// lane 63, which is then broadcast.  Exact (no arithmetic).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, kCtrl, kRowMask, 0xF, false);
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = dpp_mov<kCtrl, kRowMask>((int)(u & 0xFFFFFFFFull));
+  const int hi = dpp_mov<kCtrl, kRowMask>((int)(u >> 32));
+  return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_mov_f64<0xB1, 0xF>(v));
+  v = fmax(v, dpp_mov_f64<0x4E, 0xF>(v));
+  v = fmax(v, dpp_mov_f64<0x141, 0xF>(v));
+  v = fmax(v, dpp_mov_f64<0x140, 0xF>(v));
+  v = fmax(v, dpp_mov_f64<0x142, 0xA>(v));
+  v = fmax(v, dpp_mov_f64<0x143, 0xC>(v));
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), 63);
+  const unsigned hi = __builtin_amdgcn_readlane((int)(u >> 32), 63);
+  return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_mov<0xB1, 0xF>(v));
+  v = min(v, dpp_mov<0x4E, 0xF>(v));
+  v = min(v, dpp_mov<0x141, 0xF>(v));
+  v = min(v, dpp_mov<0x140, 0xF>(v));
+  v = min(v, dpp_mov<0x142, 0xA>(v));
+  v = min(v, dpp_mov<0x143, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top k (k <= 32) of up to 512 values held 8 per lane (value v[j], id[j];
+// unused entries -inf / 0x7FFFFFFF), ordered by (value descending, id
+// ascending).  Each lane sorts its 8 entries (Batcher's network, 19 compare-
+// exchanges); tau = the k-th best of the 64 lane heads.  The k best heads are
+// all at least tau, so every entry of the true top k is at least tau: only the
+// entries >= tau (a prefix of each sorted lane, ~k in total) are ranked against
+// each other.  Lane r < k receives the r-th entry.  scratch_v / scratch_i: LDS of
+// kTopkScratch entries for this wave (512 candidates + 32 results).
+constexpr int kTopkScratch = 512 + 32;
+
+__device__ __forceinline__ bool ahead(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void cas_desc(double& va, int& ia, double& vb, int& ib) {
+  const bool sw = ahead(vb, ib, va, ia);
+  const double tv = sw ? vb : va;
+  const int ti = sw ? ib : ia;
+  vb = sw ? va : vb;
+  ib = sw ? ia : ib;
+  va = tv;
+  ia = ti;
+}
+
+__device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k, double* scratch_v, int* scratch_i,
+                                             double* out_v, int* out_id) {
+  const int lane = (int)(threadIdx.x & 63);
+#define MOE_CAS(a, b) cas_desc(v[a], id[a], v[b], id[b])
+  MOE_CAS(0, 1); MOE_CAS(2, 3); MOE_CAS(4, 5); MOE_CAS(6, 7);
+  MOE_CAS(0, 2); MOE_CAS(1, 3); MOE_CAS(4, 6); MOE_CAS(5, 7);
+  MOE_CAS(1, 2); MOE_CAS(5, 6);
+  MOE_CAS(0, 4); MOE_CAS(1, 5); MOE_CAS(2, 6); MOE_CAS(3, 7);
+  MOE_CAS(2, 4); MOE_CAS(3, 5);
+  MOE_CAS(1, 2); MOE_CAS(3, 4); MOE_CAS(5, 6);
+#undef MOE_CAS
+  // rank of this lane's head among the 64 heads
+  scratch_v[lane] = v[0];
+  scratch_i[lane] = id[0];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int hr = 0;
+#pragma unroll 8
+  for (int q = 0; q < kWave; ++q) hr += ahead(scratch_v[q], scratch_i[q], v[0], id[0]);
+  const uint64_t at = __ballot(hr == k - 1);
+  const int L = __ffsll((long long)at) - 1;
+  const unsigned long long hu = __double_as_longlong(v[0]);
+  const double tau = __longlong_as_double(
+      ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(hu >> 32), L) << 32) |
+      (unsigned)__builtin_amdgcn_readlane((int)(hu & 0xFFFFFFFFull), L));
+  const int tau_id = __builtin_amdgcn_readlane(id[0], L);
+  // candidates: the prefix of each sorted lane that is not behind tau
+  int m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m += !ahead(tau, tau_id, v[j], id[j]);
+  int incl = m;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  const int nc = __builtin_amdgcn_readlane(incl, 63);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < m) {
+      scratch_v[incl - m + j] = v[j];
+      scratch_i[incl - m + j] = id[j];
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // rank every candidate among the candidates; rank r < k goes to lane r
+  for (int c0 = 0; c0 < nc; c0 += kWave) {
+    const int c = c0 + lane;
+    double cv = -INFINITY;
+    int ci = 0x7FFFFFFF, r = 0;
+    if (c < nc) {
+      cv = scratch_v[c];
+      ci = scratch_i[c];
+      for (int q = 0; q < nc; ++q) r += ahead(scratch_v[q], scratch_i[q], cv, ci);
+    }
+    if (c < nc && r < k) {  // results after the 512 candidate slots
+      scratch_v[512 + r] = cv;
+      scratch_i[512 + r] = ci;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < k) {
+    *out_v = scratch_v[512 + lane];
+    *out_id = scratch_i[512 + lane];
+  }
+}
+
+// Softmax weights of the k selected logits in rank order (lane r holds the
+// r-th logit): exp(l_r - l_0) / sum_j exp(l_j - l_0), the sum taken j = 0..k-1.
+__device__ __forceinline__ float topk_softmax_weight(double my_v, int k) {
+  const int lane = (int)(threadIdx.x & 63);
+  const unsigned long long u = __double_as_longlong(my_v);
+  const double top = __longlong_as_double(
+      ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(u >> 32), 0) << 32) |
+      (unsigned)__builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), 0));
+  const double ex = lane < k ? exp(my_v - top) : 0.0;
+  double total = 0.0;
+  for (int j = 0; j < k; ++j) total += __shfl(ex, j);
+  return (float)(ex / total);
+}
 
 // The s-th expert (0-based, ascending id) with a nonzero count in off[0..E].
 // Called by a whole wave; every lane gets the same answer.  Returns -1 if
@@ -121,7 +292,8 @@ struct FfnParams {
   int n_routed_slots;  // grid slots for routed experts (min(E, T*k))
   const int32_t* off;
   const int32_t* row2pair;
-  const half_t* xh;  // [T][H] dequantized A4(x) without a_gscale_in
+  const uint16_t* x;  // [T][H] BF16 hidden states
+  const half_t* xh;   // [T][H] dequantized A4(x) without a_gscale_in (generic kernels)
   moe_nvfp4_bank w13, w2, sh13, sh2;
   float g_in, g_mid;
   half_t* hh;  // [R][I] dequantized A4(h) without a_gscale_mid; R = T*k (+ T)
@@ -130,6 +302,16 @@ struct FfnParams {
   uint8_t* hs_dbg;
   float* y_rows;
   float* y_shared;
+  // decode kernels only: the shared expert takes one slot per token
+  int shared_split;
+  // fused decode path (moe_layer_forward): routing computed inside the gate/up
+  // kernel from FP64 logits; workgroup 0 publishes it
+  const double* logits64;  // [T][E]
+  int32_t* out_idx;
+  float* out_w;
+  int32_t* out_off;
+  int32_t* out_r2p;
+  int32_t* out_p2r;
 };
 
 // launchers (one translation unit each)
@@ -141,7 +323,21 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
 size_t permute_ws_bytes(int64_t T, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* off, int32_t* r2p, int32_t* p2r,
                           void* ws, hipStream_t s);
-hipError_t launch_ffn_gemv(const FfnParams& p, hipStream_t s);
+// ev_before / ev_after (nullable) are recorded around the kernel on stream s
+hipError_t launch_ffn_gateup(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+hipError_t launch_ffn_down(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+// decode kernels (T <= 8, H <= 2048, I / 32 a power of two <= 64)
+bool ffn_decode_supported(int H, int I, int64_t T);
+hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+bool fused_decode_supported(int H, int I, int E, int k, int64_t T);
+hipError_t launch_gateup_fused(const FfnParams& p, hipStream_t s);
+hipError_t launch_router_logits64(const uint16_t* x, const float* W, int64_t T, int H, int E, double* logits,
+                                  hipStream_t s);
+hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+// weight-streaming kernels (H % 256 == 0, I / 32 a power of two <= 64)
+bool ffn_stream_supported(int H, int I);
+hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+hipError_t launch_down_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_combine(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
                           const float* w, const uint16_t* residual, uint16_t* out, hipStream_t s);
 

@@ -1,0 +1,542 @@
+// Expert FFN for decode batches (T <= 8 tokens), weight streaming with every
+// load of a workgroup issued in one burst.
+//
+// At decode each selected expert's weights are used by about one token, so
+// the kernels are bound by streaming packed NVFP4 bytes from HBM, and with
+// only ~40 experts per call the time is mostly memory latency.  Two choices
+// follow from that:
+//   * each thread holds 16 x 16 B of weight codes plus their scales in
+//     registers, so one round of resident workgroups covers the whole call;
+//   * loads are issued in dependency order with nothing else in between:
+//     HIP's vmcnt waits are in order, so a load issued after the weight burst
+//     could not be consumed before the whole burst had arrived.
+// Arithmetic is the one of the streaming kernels: FP4->FP16 conversion (exact
+// E2M1 values), v_dot2_f32_f16 over a 16-element block (exact), times the
+// weight's UE4M3 scale (exact), FP32 accumulation (Richland article, "What
+// shipped" and "Why it matters").  Dot products are finished by recursive
+// halving across lanes (fixed pairing: deterministic).
+#include "common.hpp"
+
+namespace moe {
+
+bool ffn_stream_supported(int H, int I);
+
+namespace {
+
+template <int kByte>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
+}
+
+__device__ __forceinline__ float dot8(uint32_t w, half8_t a, float c) {
+  c = __builtin_amdgcn_fdot2(fp4x2<0>(w), half2_t{a[0], a[1]}, c, false);
+  c = __builtin_amdgcn_fdot2(fp4x2<1>(w), half2_t{a[2], a[3]}, c, false);
+  c = __builtin_amdgcn_fdot2(fp4x2<2>(w), half2_t{a[4], a[5]}, c, false);
+  c = __builtin_amdgcn_fdot2(fp4x2<3>(w), half2_t{a[6], a[7]}, c, false);
+  return c;
+}
+
+// 32 elements: codes (two blocks), scales of the two blocks in sc2 (low byte
+// first), FP16 activations a[0..3]
+__device__ __forceinline__ float chunk32(uint4 q, uint32_t sc2, const half8_t* a) {
+  float b0 = dot8(q.x, a[0], 0.0f);
+  b0 = dot8(q.y, a[1], b0);
+  float b1 = dot8(q.z, a[2], 0.0f);
+  b1 = dot8(q.w, a[3], b1);
+  return b0 * ue4m3_value(sc2 & 0xFFu) + b1 * ue4m3_value((sc2 >> 8) & 0xFFu);
+}
+
+// Opaque copy: keeps the compiler from hoisting the FP4 decode of loop-
+// invariant weights out of the activation-row loop (which would hold 256
+// decoded registers per thread and cut occupancy).
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+  return v;
+}
+
+// Sum v[0..15] over aligned groups of kG lanes by recursive halving (all steps
+// resolved at compile time).  Afterwards lane l holds the group total of
+// indices base + i for i < max(1, 16 / kG), where base adds `half` for every
+// halving step whose mask bit the lane has.
+template <int kG, int kN>
+struct ReduceScatter {
+  __device__ __forceinline__ static void run(float (&v)[16], int lane) {
+    if constexpr (kG > 1) {
+      constexpr int m = kG / 2;
+      const bool upper = (lane & m) != 0;
+      if constexpr (kN > 1) {
+        constexpr int half = kN / 2;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          const float send = upper ? v[i] : v[half + i];
+          const float keep = upper ? v[half + i] : v[i];
+          v[i] = keep + __shfl_xor(send, m);
+        }
+        ReduceScatter<m, half>::run(v, lane);
+      } else {
+        v[0] += __shfl_xor(v[0], m);
+        ReduceScatter<m, 1>::run(v, lane);
+      }
+    }
+  }
+  __device__ __forceinline__ static int base(int lane) {
+    if constexpr (kG > 1 && kN > 1) {
+      constexpr int m = kG / 2, half = kN / 2;
+      return ((lane & m) ? half : 0) + ReduceScatter<m, half>::base(lane);
+    } else {
+      return 0;
+    }
+  }
+};
+
+template <int kG>
+__device__ __forceinline__ void reduce_scatter16(float (&v)[16], int lane) {
+  ReduceScatter<kG, 16>::run(v, lane);
+}
+
+template <int kG>
+__device__ __forceinline__ int scatter_base(int lane) {
+  return ReduceScatter<kG, 16>::base(lane);
+}
+
+// Slot -> expert (the s-th expert with a nonzero count), one round trip.
+__device__ __forceinline__ int active_expert(const int32_t* __restrict__ off, int E, int s, int* row0, int* cnt) {
+  const int lane = lane_id();
+  const int G = (E + kWave - 1) / kWave;  // <= 16
+  int o[17];
+#pragma unroll
+  for (int i = 0; i < 17; ++i) {
+    const int e = lane * G + i;
+    o[i] = (i <= G && e <= E) ? off[e] : 0;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane * G + i;
+    if (i < G && e < E && o[i + 1] > o[i]) m |= 1u << i;
+  }
+  const int n = __popc(m);
+  int incl = n;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - n;
+  const bool mine = s >= excl && s < incl;
+  const uint64_t who = __ballot(mine);
+  if (who == 0) return -1;
+  const int L = __ffsll((long long)who) - 1;
+  int e = -1, r0 = 0, c = 0;
+  if (mine) {
+    int want = s - excl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((m >> i) & 1u) {
+        if (want == 0 && e < 0) {
+          e = lane * G + i;
+          r0 = o[i];
+          c = o[i + 1] - o[i];
+        }
+        --want;
+      }
+    }
+  }
+  // the same in every lane: make it wave-uniform (scalar) for the compiler
+  *row0 = __builtin_amdgcn_readfirstlane(__shfl(r0, L));
+  *cnt = __builtin_amdgcn_readfirstlane(__shfl(c, L));
+  return __builtin_amdgcn_readfirstlane(__shfl(e, L));
+}
+
+}  // namespace
+
+constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use the streaming kernels
+
+// ---------------------------------------------------------------- gate/up
+// Slots: [0, n_routed_slots) routed experts in ascending id order; then the
+// shared expert, one slot per token (so no workgroup carries T activation rows).
+//
+// Routing prologue (fused decode path only): waves 0..T-1 each take one token's
+// FP64 logits, select the top k (sorted lanes + DPP tournament: value
+// descending, id ascending) and form the softmax weights; wave 0 then derives
+// the permutation of the T*k pairs (expert ascending, token ascending) and
+// every workgroup finds its own expert and rows from it.  Workgroup 0 writes
+// topk_idx, topk_w, expert_off, row2pair, pair2row for the later kernels.
+constexpr int kMaxPairs = kDecMaxT * 32;
+constexpr int kMaxRouteE = 512;
+
+struct Routing {
+  double sv[kDecMaxT][kTopkScratch];  // top-k scratch, one per token wave
+  int si[kDecMaxT][kTopkScratch];
+  int e[kMaxPairs];                   // expert of pair p = t*k + j
+  float w[kMaxPairs];
+  int cnt[kMaxRouteE];                // pairs per expert
+  int off[kMaxRouteE + 1];            // exclusive prefix sum of cnt
+  int nzr[kMaxRouteE];                // active experts with a smaller id
+};
+
+// Routing of the (few) tokens inside a workgroup.  Top k per token wave and
+// softmax exactly as moe_route; then a histogram of the T*k pairs over the
+// experts and one wave scan give expert_off and the distinct-expert ranks
+// (the slot order).  Workgroup 0 publishes topk_idx, topk_w, expert_off,
+// row2pair and pair2row.
+__device__ __forceinline__ void route_in_workgroup(const FfnParams& p, Routing& R) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int T = p.T, E = p.E, k = p.k, P = T * k;
+  for (int e = tid; e < E; e += 256) R.cnt[e] = 0;
+  if (wave < T) {
+    double v[8];
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + kWave * j;
+      v[j] = e < E ? p.logits64[(int64_t)wave * E + e] : -INFINITY;
+      id[j] = e < E ? e : 0x7FFFFFFF;
+    }
+    double my_v = 0.0;
+    int my_e = 0;
+    wave_topk512(v, id, k, R.sv[wave], R.si[wave], &my_v, &my_e);
+    const float wk = topk_softmax_weight(my_v, k);
+    if (lane < k) {
+      R.e[wave * k + lane] = my_e;
+      R.w[wave * k + lane] = wk;
+    }
+  }
+  __syncthreads();
+  for (int pi = tid; pi < P; pi += 256) atomicAdd(&R.cnt[R.e[pi]], 1);
+  __syncthreads();
+  if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
+    int c[8], nz[8], sc = 0, snz = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane * 8 + j;
+      c[j] = e < E ? R.cnt[e] : 0;
+      nz[j] = c[j] > 0;
+      sc += c[j];
+      snz += nz[j];
+    }
+    int ic = sc, inz = snz;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int a = __shfl_up(ic, d), b = __shfl_up(inz, d);
+      if (lane >= d) {
+        ic += a;
+        inz += b;
+      }
+    }
+    int rc = ic - sc, rnz = inz - snz;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane * 8 + j;
+      if (e < E) {
+        R.off[e] = rc;
+        R.nzr[e] = rnz;
+      }
+      rc += c[j];
+      rnz += nz[j];
+    }
+    if (lane == 63) R.off[E] = ic;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {  // publish the routing
+    for (int e = tid; e <= E; e += 256) p.out_off[e] = R.off[e];
+    for (int pi = tid; pi < P; pi += 256) {
+      const int t = pi / k, ep = R.e[pi];
+      int before = 0;  // earlier tokens that chose the same expert
+      for (int t2 = 0; t2 < t; ++t2)
+        for (int j2 = 0; j2 < k; ++j2) before += R.e[t2 * k + j2] == ep;
+      const int row = R.off[ep] + before;
+      p.out_idx[pi] = ep;
+      p.out_w[pi] = R.w[pi];
+      p.out_p2r[pi] = row;
+      p.out_r2p[row] = pi;
+    }
+  }
+}
+
+template <bool kFused>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
+  __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized, [T][H]
+  __shared__ float gu[kDecMaxT][64];
+  __shared__ int toks[kDecMaxT];
+  __shared__ int slot_info[3];
+  __shared__ Routing R;
+  const int H = p.H, I = p.I, T = p.T;
+  const int n_cg = I / 32;
+  const int cg = blockIdx.x % n_cg, slot = blockIdx.x / n_cg;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
+  const int nblk = H / 16;
+
+  // 1. x blocks of every token (no dependency on the routing)
+  uint4 xa[2], xb[2];  // up to 2 blocks per thread (T * H / 16 <= 512)
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int task = tid + 256 * q;
+    if (task < T * nblk) {
+      const uint4* src = reinterpret_cast<const uint4*>(p.x + (int64_t)task * 16);
+      xa[q] = src[0];
+      xb[q] = src[1];
+    }
+  }
+  // 2. this slot's expert and activation rows
+  const int sh_slot = slot - p.n_routed_slots;
+  const bool shared = p.has_shared && sh_slot >= 0;
+  int e, row0, nrows;
+  if (shared) {
+    e = 0;
+    row0 = p.shared_split ? sh_slot : 0;
+    nrows = p.shared_split ? 1 : T;
+  } else if (kFused) {
+    route_in_workgroup(p, R);
+    if (tid == 0) slot_info[0] = -1;
+    __syncthreads();
+    for (int ee = tid; ee < p.E; ee += 256)
+      if (R.cnt[ee] > 0 && R.nzr[ee] == slot) slot_info[0] = ee;
+    __syncthreads();
+    e = __builtin_amdgcn_readfirstlane(slot_info[0]);
+    if (e < 0) return;
+    row0 = __builtin_amdgcn_readfirstlane(R.off[e]);
+    nrows = __builtin_amdgcn_readfirstlane(R.cnt[e]);
+  } else {
+    e = active_expert(p.off, p.E, slot, &row0, &nrows);
+    if (e < 0) return;
+  }
+  // tokens of the rows, then the weight burst (buffer loads: one instruction
+  // per 16 B, the row stride in the scalar offset)
+  int tok = 0;
+  if (!kFused && !shared && tid < nrows) tok = p.row2pair[row0 + tid] / p.k;
+  const uint8_t* bcodes = shared ? p.sh13.codes : p.w13.codes;
+  const uint8_t* bscales = shared ? p.sh13.scales : p.w13.scales;
+  const float* bg = shared ? p.sh13.gscale : p.w13.gscale;
+  const int nch = H / 32;
+  const uint32_t qrow = (uint32_t)H / 2, srow = (uint32_t)H / 16;
+  const auto rq = buffer_rsrc(bcodes + (int64_t)e * 2 * I * qrow, 2u * I * qrow);
+  const auto rs = buffer_rsrc(bscales + (int64_t)e * 2 * I * srow, 2u * I * srow);
+  // lanes past the row's chunks read past the buffer: zeros
+  const uint32_t vq = l < nch ? (uint32_t)(cg * 32 + w) * qrow + l * 16u : 0x80000000u;
+  const uint32_t vs = l < nch ? (uint32_t)(cg * 32 + w) * srow + l * 2u : 0x80000000u;
+  uint4 q[16];
+  uint32_t sc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // rows w + 4j: j < 8 gate column cg*32 + w + 4j, j >= 8 up column (same + I)
+    const uint32_t rowoff = j < 8 ? (uint32_t)(4 * j) : (uint32_t)I + 4u * (j - 8);
+    q[j] = buffer_load16(rq, vq, rowoff * qrow);
+    sc[j] = buffer_load2(rs, vs, rowoff * srow);
+  }
+  const float G = bg[e] * p.g_in;
+  // 3. A4(x) into LDS while the weights are in flight
+  const float g6 = 6.0f * p.g_in;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int task = tid + 256 * qi;
+    if (task < T * nblk) {
+      const uint32_t wv[8] = {xa[qi].x, xa[qi].y, xa[qi].z, xa[qi].w, xb[qi].x, xb[qi].y, xb[qi].z, xb[qi].w};
+      float v[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(wv[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+      }
+      const uint32_t scode = scale_code(amax, g6);
+      const float sv = ue4m3_value(scode);
+      const float s = sv * p.g_in;
+      half8_t h0, h1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        h0[i] = (half_t)(e2m1_value(elem_code(v[i], s)) * sv);
+        h1[i] = (half_t)(e2m1_value(elem_code(v[8 + i], s)) * sv);
+      }
+      half8_t* dst = reinterpret_cast<half8_t*>(xs + (size_t)task * 16);
+      dst[0] = h0;
+      dst[1] = h1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (shared) {
+    if (tid < nrows) toks[tid] = row0 + tid;
+  } else if (kFused) {
+    if (tid == 0) {  // tokens choosing e, ascending (at most one pair per token)
+      int r = 0;
+      for (int t = 0; t < T; ++t)
+        for (int j = 0; j < p.k; ++j)
+          if (R.e[t * p.k + j] == e) toks[r++] = t;
+    }
+  } else if (tid < nrows) {
+    toks[tid] = tok;
+  }
+  __syncthreads();
+  // 4. dot products, one activation row at a time
+  for (int rr = 0; rr < nrows; ++rr) {
+    half8_t a[4];
+    const half8_t* src = reinterpret_cast<const half8_t*>(xs + (size_t)toks[rr] * H + l * 32);
+    if (l < nch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = src[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = half8_t{};
+    }
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc[j] = chunk32(opaque(q[j]), sc[j], a);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: bounded live registers
+    }
+    reduce_scatter16<64>(acc, l);
+    if ((l & 3) == 0) gu[rr][w + 4 * scatter_base<64>(l)] = acc[0];
+  }
+  __syncthreads();
+  // 5. SwiGLU + A4(h): 32 lanes per activation row (two 16-blocks)
+  for (int task = tid; task < nrows * 32; task += 256) {
+    const int rr = task / 32, i = task % 32;
+    const float g = G * gu[rr][i], u = G * gu[rr][32 + i];
+    const float h = silu(g) * u;
+    float amax = fabsf(h);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
+    const float sv = ue4m3_value(scode);
+    const uint32_t c = elem_code(h, sv * p.g_mid);
+    const uint32_t c_hi = __shfl_down(c, 1, 16);
+    const int64_t orow = shared ? (int64_t)T * p.k + row0 + rr : (int64_t)row0 + rr;
+    const int64_t col = (int64_t)cg * 32 + i;
+    p.hh[orow * I + col] = (half_t)(e2m1_value(c) * sv);
+    if (p.h_dbg) p.h_dbg[orow * I + col] = h;
+    if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
+    if (p.hs_dbg && (i & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
+  }
+}
+
+// ---------------------------------------------------------------- down
+// W2 rows n, I/32 chunks per row = kLPR lanes per row, 64/kLPR rows per wave
+// instruction.  Thread (w, l): chunk l % kLPR of rows
+// n0 + (64/kLPR) * (w + 4 j) + l / kLPR, j < 16.
+template <int kLPR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_decode(FfnParams p) {
+  constexpr int kRPI = 64 / kLPR;       // rows per wave instruction
+  constexpr int kRowsWG = 64 * kRPI;    // 4 waves x 16 x kRPI
+  const int H = p.H, I = p.I, T = p.T;
+  const int n_nb = (H + kRowsWG - 1) / kRowsWG;
+  const int nb = blockIdx.x % n_nb, slot = blockIdx.x / n_nb;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
+  int e, row0, nrows;
+  const int sh_slot = slot - p.n_routed_slots;
+  const bool shared = p.has_shared && sh_slot >= 0;
+  if (shared) {
+    e = 0;
+    row0 = p.shared_split ? sh_slot : 0;
+    nrows = p.shared_split ? 1 : T;
+  } else {
+    e = active_expert(p.off, p.E, slot, &row0, &nrows);
+    if (e < 0) return;
+  }
+  const uint8_t* bcodes = shared ? p.sh2.codes : p.w2.codes;
+  const uint8_t* bscales = shared ? p.sh2.scales : p.w2.scales;
+  const float* bg = shared ? p.sh2.gscale : p.w2.gscale;
+  const int ch = l % kLPR;
+  const int base_n = nb * kRowsWG + l / kLPR;
+  // activation chunk of the first row, then the weight burst
+  const int64_t hrow0 = shared ? (int64_t)T * p.k + row0 : (int64_t)row0;
+  half8_t a[4];
+  {
+    const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + hrow0 * I + ch * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = src[i];
+  }
+  const uint32_t qrow = (uint32_t)I / 2, srow = (uint32_t)I / 16;
+  const auto rq = buffer_rsrc(bcodes + (int64_t)e * H * qrow, (uint32_t)H * qrow);
+  const auto rs = buffer_rsrc(bscales + (int64_t)e * H * srow, (uint32_t)H * srow);
+  const uint32_t n_lane = (uint32_t)(base_n + kRPI * w);
+  const uint32_t vq = n_lane * qrow + ch * 16u, vs = n_lane * srow + ch * 2u;
+  uint4 q[16];
+  uint32_t sc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {  // rows past H read past the buffer: zeros
+    q[j] = buffer_load16(rq, vq, (uint32_t)(4 * kRPI * j) * qrow);
+    sc[j] = buffer_load2(rs, vs, (uint32_t)(4 * kRPI * j) * srow);
+  }
+  const float G = bg[e] * p.g_mid;
+  float* dst0 = shared ? p.y_shared + (int64_t)row0 * H : p.y_rows + (int64_t)row0 * H;
+  for (int rr = 0; rr < nrows; ++rr) {
+    if (rr > 0) {
+      const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + (hrow0 + rr) * I + ch * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = src[i];
+    }
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc[j] = chunk32(opaque(q[j]), sc[j], a);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    reduce_scatter16<kLPR>(acc, l);
+    constexpr int kKeep = 16 / kLPR > 1 ? 16 / kLPR : 1;
+    const bool writer = kLPR <= 16 || (l & (kLPR / 16 - 1)) == 0;
+    if (writer) {
+      const int jb = scatter_base<kLPR>(l);
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i) {
+        const int n = base_n + kRPI * (w + 4 * (jb + i));
+        if (n < H) dst0[(int64_t)rr * H + n] = G * acc[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+bool ffn_decode_supported(int H, int I, int64_t T) {
+  const int lpr = I / 32;
+  return T <= kDecMaxT && H <= 2048 && H % 32 == 0 && I % 32 == 0 && lpr >= 1 && lpr <= 64 &&
+         (lpr & (lpr - 1)) == 0;
+}
+
+static int decode_slots(const FfnParams& p) {
+  return p.n_routed_slots + (p.has_shared ? (p.shared_split ? p.T : 1) : 0);
+}
+
+hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+  const int slots = decode_slots(p);
+  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
+  if (slots > 0)
+    hipLaunchKernelGGL(k_gateup_decode<false>, dim3((unsigned)(slots * (p.I / 32))), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
+  return e;
+}
+
+bool fused_decode_supported(int H, int I, int E, int k, int64_t T) {
+  return ffn_decode_supported(H, I, T) && E <= 8 * kWave && k <= 32 && T >= 1;
+}
+
+hipError_t launch_gateup_fused(const FfnParams& p, hipStream_t s) {
+  const int slots = decode_slots(p);
+  hipLaunchKernelGGL(k_gateup_decode<true>, dim3((unsigned)(slots * (p.I / 32))), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+  const int slots = decode_slots(p);
+  const int lpr = p.I / 32;
+  const int rows_wg = 64 * (64 / lpr);
+  const unsigned grid = (unsigned)(slots * ((p.H + rows_wg - 1) / rows_wg));
+  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
+  if (slots > 0) {
+    switch (lpr) {
+      case 1: hipLaunchKernelGGL(k_down_decode<1>, dim3(grid), dim3(256), 0, s, p); break;
+      case 2: hipLaunchKernelGGL(k_down_decode<2>, dim3(grid), dim3(256), 0, s, p); break;
+      case 4: hipLaunchKernelGGL(k_down_decode<4>, dim3(grid), dim3(256), 0, s, p); break;
+      case 8: hipLaunchKernelGGL(k_down_decode<8>, dim3(grid), dim3(256), 0, s, p); break;
+      case 16: hipLaunchKernelGGL(k_down_decode<16>, dim3(grid), dim3(256), 0, s, p); break;
+      case 32: hipLaunchKernelGGL(k_down_decode<32>, dim3(grid), dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL(k_down_decode<64>, dim3(grid), dim3(256), 0, s, p); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
+  return e;
+}
+
+}  // namespace moe

@@ -191,12 +191,22 @@ __global__ __launch_bounds__(256) void k_ffn_down(FfnParams p) {
   }
 }
 
-hipError_t launch_ffn_gemv(const FfnParams& p, hipStream_t s) {
+hipError_t launch_ffn_gateup(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = p.n_routed_slots + (p.has_shared ? 1 : 0);
-  if (slots == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_ffn_gateup, dim3((unsigned)(slots * (p.I / 16))), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_ffn_down, dim3((unsigned)(slots * (p.H / kWRows))), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
+  if (slots > 0) hipLaunchKernelGGL(k_ffn_gateup, dim3((unsigned)(slots * (p.I / 16))), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
+  return e;
+}
+
+hipError_t launch_ffn_down(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+  const int slots = p.n_routed_slots + (p.has_shared ? 1 : 0);
+  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
+  if (slots > 0) hipLaunchKernelGGL(k_ffn_down, dim3((unsigned)(slots * (p.H / kWRows))), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
+  return e;
 }
 
 }  // namespace moe

@@ -94,6 +94,59 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   }
 }
 
+// Up to 256 tokens: one workgroup does count, scan and scatter (one launch).
+__global__ __launch_bounds__(256) void k_perm_single(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                     int32_t* __restrict__ off, int32_t* __restrict__ r2p,
+                                                     int32_t* __restrict__ p2r) {
+  __shared__ unsigned long long masks[4][kMaxE];
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t part[256];
+  build_masks(idx, T, k, E, masks, 0);
+  // per-thread run of up to 4 experts, then a scan over the 256 runs
+  const int tid = threadIdx.x;
+  const int per = (E + 255) / 256;
+  int run = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      base[e] = run;
+      run += __popcll(masks[0][e]) + __popcll(masks[1][e]) + __popcll(masks[2][e]) + __popcll(masks[3][e]);
+    }
+  }
+  part[tid] = run;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int add = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const int excl = tid > 0 ? part[tid - 1] : 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      base[e] += excl;
+      off[e] = base[e];
+    }
+  }
+  if (tid == 255) off[E] = part[255];
+  __syncthreads();
+  const int wave = tid >> 6, lane = lane_id();
+  const int64_t t = tid;
+  if (t >= T) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= E) continue;
+    int r = base[e];
+    for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
+    r += __popcll(masks[wave][e] & below);
+    const int32_t pr = (int32_t)(t * k + j);
+    r2p[r] = pr;
+    p2r[pr] = r;
+  }
+}
+
 size_t permute_ws_bytes(int64_t T, int E) {
   const int64_t nchunk = (T + kChunkTok - 1) / kChunkTok;
   return (size_t)(nchunk * E) * sizeof(int32_t);
@@ -102,6 +155,10 @@ size_t permute_ws_bytes(int64_t T, int E) {
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* off, int32_t* r2p, int32_t* p2r,
                           void* ws, hipStream_t s) {
   const int nchunk = (int)((T + kChunkTok - 1) / kChunkTok);
+  if (nchunk == 1) {
+    hipLaunchKernelGGL(k_perm_single, dim3(1), dim3(256), 0, s, idx, T, k, E, off, r2p, p2r);
+    return hipGetLastError();
+  }
   int32_t* cnt = static_cast<int32_t*>(ws);
   if (nchunk > 0) hipLaunchKernelGGL(k_perm_count, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, cnt, nchunk, E, off);

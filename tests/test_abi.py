@@ -105,7 +105,10 @@ def test_workspace_too_small():
     need = moe.lib.moe_workspace_bytes(ctypes.byref(L), 4)
     assert need > 0
     assert route(L, wsb=0) == moe.MOE_EWORKSPACE
-    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 256, None)
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, None)
+    assert rc == moe.MOE_EWORKSPACE
+    rc = moe.lib.moe_layer_forward(ctypes.byref(L), FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, FAKE, 1024, None)
     assert rc == moe.MOE_EWORKSPACE
     rc = moe.lib.moe_permute(ctypes.byref(L), FAKE, 100000, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert rc == moe.MOE_EWORKSPACE

@@ -242,3 +242,27 @@ def test_quantize_act_fp32_thresholds(g):
     qo, so = oracle.quantize(blk.astype(np.float64), g)
     assert np.array_equal(scales.cpu().numpy(), so)
     assert np.array_equal(codes.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("cfg,T", [(1, 1), (1, 2), (1, 4), (0, 4), (0, 8), (1, 7)])
+def test_layer_forward_matches_separate_calls(cfg, T):
+    """moe_layer_forward (fused decode kernels for T <= 4) writes exactly what the four
+    separate calls write; the separate calls are checked against the oracle above."""
+    gh.log("case: moe_layer_forward config %d T=%d" % (cfg, T))
+    L, DL = layer_for(cfg)
+    x = gen.make_tokens(cfg, T, step=13)
+    res = gen.make_tokens(cfg, T, step=14)
+    ref = gh.run_layer(DL, x, residual=res, dump=())
+    buf = moe.Buffers(DL, T, gh.DEV)
+    moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf, residual=gh.to_dev(res.view(np.int16)))
+    torch.cuda.synchronize()
+    got = {"idx": buf.topk_idx, "w": buf.topk_w, "off": buf.expert_off, "r2p": buf.row2pair, "p2r": buf.pair2row,
+           "y_rows": buf.y_rows, "y_shared": buf.y_shared, "out": buf.out}
+    for key, t in got.items():
+        a = t.cpu().numpy()
+        b = ref[key]
+        if key == "out":
+            a = a.view(np.uint16)
+        assert np.array_equal(a, b), key
+    rep = gh.check_layer(L, x, dict(ref, **gh.run_layer(DL, x, residual=res)), residual=res)
+    gh.log("  ", rep.line())
