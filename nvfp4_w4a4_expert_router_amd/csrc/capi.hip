@@ -58,7 +58,7 @@ size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(
 size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
 
 struct FfnWs {
-  size_t xq, xs, xh, hh, end;
+  size_t xq, xs, xh, hh, tiles, end;
 };
 
 FfnWs ffn_ws(const moe_layer* L, int64_t T) {
@@ -73,6 +73,8 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   o = align_up(o + (size_t)T * L->H * sizeof(half_t));
   w.hh = o;
   o = align_up(o + (size_t)R * L->I * sizeof(half_t));
+  w.tiles = o;
+  o = align_up(o + ffn_mfma_ws_bytes(L->E));
   w.end = o;
   return w;
 }
@@ -158,14 +160,19 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   uint8_t* xs = reinterpret_cast<uint8_t*>(base + lay.xs);
   half_t* xh = reinterpret_cast<half_t*>(base + lay.xh);
   hipEvent_t* ev = dbg ? dbg->events : nullptr;
-  const bool stream_path = ffn_stream_supported(L->H, L->I);
+  // path by batch size: decode kernels (T <= 4), matrix cores (T >= 32), weight
+  // streaming in between; generic kernels for shapes the others do not cover
+  const bool decode_path = ffn_decode_supported(L->H, L->I, T);
+  const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E);
+  const bool stream_path = !decode_path && !mfma_path && ffn_stream_supported(L->H, L->I);
+  const bool self_encoding = decode_path || stream_path;  // these kernels encode x themselves
   const bool want_xdump = dbg && (dbg->xq || dbg->xs);
-  // kernel 0: A4(x) into the workspace (the streaming kernels encode x themselves
-  // and need it only for the dumps)
+  // kernel 0: A4(x) into the workspace (dequantized FP16 copy for the matrix cores
+  // and the generic kernels; codes for the dumps)
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
-  if (!stream_path || want_xdump)
+  if (!self_encoding || want_xdump)
     if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
-                                         stream_path ? nullptr : xh, stream))))
+                                         self_encoding ? nullptr : xh, stream))))
       return rc;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
   if (dbg && dbg->xq)
@@ -199,7 +206,9 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.hs_dbg = dbg ? dbg->hs : nullptr;
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
-  if (ffn_decode_supported(L->H, L->I, T)) {
+  if (mfma_path)
+    return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), stream, ev));
+  if (decode_path) {
     p.shared_split = 1;
     if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
     return launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));

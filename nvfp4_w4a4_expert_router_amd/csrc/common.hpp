@@ -334,6 +334,10 @@ hipError_t launch_gateup_fused(const FfnParams& p, hipStream_t s);
 hipError_t launch_router_logits64(const uint16_t* x, const float* W, int64_t T, int H, int E, double* logits,
                                   hipStream_t s);
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+// matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
+bool ffn_mfma_supported(int H, int I, int E);
+size_t ffn_mfma_ws_bytes(int E);
+hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev);
 // weight-streaming kernels (H % 256 == 0, I / 32 a power of two <= 64)
 bool ffn_stream_supported(int H, int I);
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
