@@ -58,7 +58,7 @@ size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(
 size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
 
 struct FfnWs {
-  size_t xq, xs, xh, hh, tiles, end;
+  size_t xq, xs, xh, hh, hq, hs, tiles, end;
 };
 
 FfnWs ffn_ws(const moe_layer* L, int64_t T) {
@@ -73,6 +73,10 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   o = align_up(o + (size_t)T * L->H * sizeof(half_t));
   w.hh = o;
   o = align_up(o + (size_t)R * L->I * sizeof(half_t));
+  w.hq = o;
+  o = align_up(o + (size_t)R * (L->I / 2));
+  w.hs = o;
+  o = align_up(o + (size_t)R * (L->I / 16));
   w.tiles = o;
   o = align_up(o + ffn_mfma_ws_bytes(L->E));
   w.end = o;
@@ -172,7 +176,7 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
   if (!self_encoding || want_xdump)
     if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
-                                         self_encoding ? nullptr : xh, stream))))
+                                         self_encoding || mfma_path ? nullptr : xh, stream))))
       return rc;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
   if (dbg && dbg->xq)
@@ -207,7 +211,9 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
   if (mfma_path)
-    return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), stream, ev));
+    return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), xq, xs,
+                                     reinterpret_cast<uint8_t*>(base + lay.hq),
+                                     reinterpret_cast<uint8_t*>(base + lay.hs), stream, ev));
   if (decode_path) {
     p.shared_split = 1;
     if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;

@@ -337,7 +337,8 @@ hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_b
 // matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
 bool ffn_mfma_supported(int H, int I, int E);
 size_t ffn_mfma_ws_bytes(int E);
-hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, const uint8_t* xq, const uint8_t* xs,
+                           uint8_t* hq, uint8_t* hs, hipStream_t s, hipEvent_t* ev);
 // weight-streaming kernels (H % 256 == 0, I / 32 a power of two <= 64)
 bool ffn_stream_supported(int H, int I);
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);

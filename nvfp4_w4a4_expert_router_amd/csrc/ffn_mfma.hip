@@ -84,8 +84,68 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
   if (tid <= E + 1) tile_start[tid] = tid > 0 ? part[tid - 1] : 0;
 }
 
+// One K step of 64: each thread carries 16 B of codes and the two UE4M3 scales
+// of one A row and of one B row (32 elements each).
+struct Stage {
+  uint4 aq, bq;
+  uint32_t as, bs;
+};
+
+// A (activation rows, A4 codes) x B (weight rows, NVFP4 codes), both decoded to
+// FP16 in LDS; 4 waves, wave (wm, wn) owns a 64 x 64 quadrant as 2 x 2 MFMA tiles.
+// kGateUp: B rows 0..63 are gate columns, 64..127 the matching up columns, and
+// wave w covers h columns 32*(w%2).. of both.
+template <bool kGateUp>
+__device__ __forceinline__ void tile_mma(const uint8_t* __restrict__ arow_q, const uint8_t* __restrict__ arow_s,
+                                         const uint8_t* __restrict__ brow_q, const uint8_t* __restrict__ brow_s,
+                                         int K, half_t* As, half_t* Bs, floatx16 (&acc)[2][2]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int r = tid >> 1, hf = tid & 1;  // loader row and 32-element half of the K step
+  const int wm = (wave >> 1) * 64;
+  const int wn = kGateUp ? (wave & 1) * 32 : (wave & 1) * 64;
+  auto fetch = [&](int k0, Stage& st) {
+    st.aq = *reinterpret_cast<const uint4*>(arow_q + k0 / 2 + hf * 16);
+    st.as = *reinterpret_cast<const uint16_t*>(arow_s + k0 / 16 + hf * 2);
+    st.bq = *reinterpret_cast<const uint4*>(brow_q + k0 / 2 + hf * 16);
+    st.bs = *reinterpret_cast<const uint16_t*>(brow_s + k0 / 16 + hf * 2);
+  };
+  Stage st;
+  fetch(0, st);
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    __syncthreads();  // the previous step's fragments are read
+    decode32_to_lds(st.aq, st.as, &As[r * kLdsStride + hf * 32]);
+    decode32_to_lds(st.bq, st.bs, &Bs[r * kLdsStride + hf * 32]);
+    __syncthreads();
+    if (k0 + kBK < K) fetch(k0 + kBK, st);  // next step in flight during the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 16) {
+      const int ko = kk + 8 * (lane >> 5);
+      half8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const half8_t*>(&As[(wm + 32 * i + (lane & 31)) * kLdsStride + ko]);
+      if (kGateUp) {
+        b[0] = *reinterpret_cast<const half8_t*>(&Bs[(wn + (lane & 31)) * kLdsStride + ko]);
+        b[1] = *reinterpret_cast<const half8_t*>(&Bs[(64 + wn + (lane & 31)) * kLdsStride + ko]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[j] = *reinterpret_cast<const half8_t*>(&Bs[(wn + 32 * j + (lane & 31)) * kLdsStride + ko]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- G1
-__global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+// h codes + scales of every row go to hq / hs (permuted rows, then shared rows);
+// the down GEMM reads them back as its A operand.
+__global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   __shared__ __align__(16) half_t As[kBM * kLdsStride];
   __shared__ __align__(16) half_t Bs[kBN * kLdsStride];
   const int H = p.H, I = p.I, T = p.T, E = p.E;
@@ -97,61 +157,30 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t*
   const bool shared = seg == E;
   const int seg_row0 = shared ? 0 : p.off[seg];
   const int seg_rows = shared ? T : p.off[seg + 1] - p.off[seg];
-  const int m0 = (mt - tile_start[seg]) * kBM;  // first row of the tile within the segment
+  const int m0 = (mt - tile_start[seg]) * kBM;
   const uint8_t* codes = shared ? p.sh13.codes : p.w13.codes + (int64_t)seg * 2 * I * (H / 2);
   const uint8_t* scales = shared ? p.sh13.scales : p.w13.scales + (int64_t)seg * 2 * I * (H / 16);
   const float G = (shared ? p.sh13.gscale[0] : p.w13.gscale[seg]) * p.g_in;
-
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  // A rows: token of each tile row (rows past the segment reuse token 0; results dropped)
-  const int ar = tid >> 1, ah = tid & 1;  // A loader: row ar, halfs [32 ah, 32 ah + 32) of the K step
+  const int r = tid >> 1;
+  // A row r: the token of tile row r (rows past the segment reuse token 0; dropped)
   int atok = 0;
-  if (m0 + ar < seg_rows) atok = shared ? m0 + ar : p.row2pair[seg_row0 + m0 + ar] / p.k;
-  const half_t* arow = p.xh + (int64_t)atok * H + ah * 32;
-  // B rows: local row br (0..63 gate columns nt*64.., 64..127 up columns)
-  const int br = tid >> 1, bh = tid & 1;
-  const int64_t wrow = br < 64 ? (int64_t)nt * 64 + br : (int64_t)I + nt * 64 + (br - 64);
-  const uint8_t* brow = codes + wrow * (H / 2) + bh * 16;
-  const uint8_t* bsrow = scales + wrow * (H / 16) + bh * 2;
-
-  floatx16 acc[2][2] = {};  // [m sub-tile][0 gate, 1 up]
+  if (m0 + r < seg_rows) atok = shared ? m0 + r : p.row2pair[seg_row0 + m0 + r] / p.k;
+  // B row r: 0..63 gate columns nt*64.., 64..127 the up columns
+  const int64_t wrow = r < 64 ? (int64_t)nt * 64 + r : (int64_t)I + nt * 64 + (r - 64);
+  floatx16 acc[2][2] = {};
+  tile_mma<true>(xq + (int64_t)atok * (H / 2), xs + (int64_t)atok * (H / 16), codes + wrow * (H / 2),
+                 scales + wrow * (H / 16), H, As, Bs, acc);
+  // epilogue: lane holds h column wn + (lane & 31) of rows 8*(q/4) + 4*(lane/32) + q%4
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 32;
-  for (int k0 = 0; k0 < H; k0 += kBK) {
-    // global -> registers
-    uint4 av[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + k0 + 8 * i);
-    const uint4 bq = *reinterpret_cast<const uint4*>(brow + k0 / 2);
-    const uint32_t bs = *reinterpret_cast<const uint16_t*>(bsrow + k0 / 16);
-    __syncthreads();  // previous step's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[ar * kLdsStride + ah * 32 + 8 * i]) = av[i];
-    decode32_to_lds(bq, bs, &Bs[br * kLdsStride + bh * 32]);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      const int ko = kk + 8 * (lane >> 5);
-      half8_t a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const half8_t*>(&As[(wm + 32 * i + (lane & 31)) * kLdsStride + ko]);
-      b[0] = *reinterpret_cast<const half8_t*>(&Bs[(wn + (lane & 31)) * kLdsStride + ko]);
-      b[1] = *reinterpret_cast<const half8_t*>(&Bs[(64 + wn + (lane & 31)) * kLdsStride + ko]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  // epilogue: lane holds column wn + (lane & 31) of rows 8*(r/4) + 4*(lane/32) + r%4
-  const int col = nt * 64 + wn + (lane & 31);  // h column
+  const int col = nt * 64 + wn + (lane & 31);
   const float g6 = 6.0f * p.g_mid;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row within the tile
-      const float g = G * acc[i][0][r], u = G * acc[i][1][r];
+    for (int q = 0; q < 16; ++q) {
+      const int m = wm + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      const float g = G * acc[i][0][q], u = G * acc[i][1][q];
       const float h = silu(g) * u;
       float amax = fabsf(h);
       amax = fmaxf(amax, __shfl_xor(amax, 1));
@@ -164,9 +193,11 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t*
       const uint32_t c_hi = __shfl_xor(c, 1);
       if (m0 + m < seg_rows) {
         const int64_t orow = shared ? (int64_t)T * p.k + m0 + m : (int64_t)seg_row0 + m0 + m;
-        p.hh[orow * I + col] = (half_t)(e2m1_value(c) * sv);
+        const uint8_t byte = (uint8_t)(c | (c_hi << 4));
+        if ((col & 1) == 0) hq[orow * (I / 2) + col / 2] = byte;
+        if ((col & 15) == 0) hs[orow * (I / 16) + col / 16] = (uint8_t)scode;
         if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-        if (p.hq_dbg && (col & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
+        if (p.hq_dbg && (col & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = byte;
         if (p.hs_dbg && (col & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
       }
     }
@@ -174,7 +205,8 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t*
 }
 
 // ---------------------------------------------------------------- G2
-__global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+__global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                   const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs) {
   __shared__ __align__(16) half_t As[kBM * kLdsStride];
   __shared__ __align__(16) half_t Bs[kBN * kLdsStride];
   const int H = p.H, I = p.I, T = p.T, E = p.E;
@@ -190,56 +222,26 @@ __global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* _
   const uint8_t* codes = shared ? p.sh2.codes : p.w2.codes + (int64_t)seg * H * (I / 2);
   const uint8_t* scales = shared ? p.sh2.scales : p.w2.scales + (int64_t)seg * H * (I / 16);
   const float G = (shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
-
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int ar = tid >> 1, ah = tid & 1;
-  const int arow_i = m0 + ar < seg_rows ? m0 + ar : 0;
+  const int r = tid >> 1;
+  const int arow_i = m0 + r < seg_rows ? m0 + r : 0;
   const int64_t hrow = shared ? (int64_t)T * p.k + arow_i : (int64_t)seg_row0 + arow_i;
-  const half_t* arow = p.hh + hrow * I + ah * 32;
-  const int br = tid >> 1, bh = tid & 1;
-  const int64_t wrow = (int64_t)nt * kBN + br;
-  const uint8_t* brow = codes + wrow * (I / 2) + bh * 16;
-  const uint8_t* bsrow = scales + wrow * (I / 16) + bh * 2;
-
+  const int64_t wrow = (int64_t)nt * kBN + r;
   floatx16 acc[2][2] = {};
+  tile_mma<false>(hq + hrow * (I / 2), hs + hrow * (I / 16), codes + wrow * (I / 2), scales + wrow * (I / 16), I,
+                  As, Bs, acc);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  for (int k0 = 0; k0 < I; k0 += kBK) {
-    uint4 av[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + k0 + 8 * i);
-    const uint4 bq = *reinterpret_cast<const uint4*>(brow + k0 / 2);
-    const uint32_t bs = *reinterpret_cast<const uint16_t*>(bsrow + k0 / 16);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[ar * kLdsStride + ah * 32 + 8 * i]) = av[i];
-    decode32_to_lds(bq, bs, &Bs[br * kLdsStride + bh * 32]);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      const int ko = kk + 8 * (lane >> 5);
-      half8_t a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const half8_t*>(&As[(wm + 32 * i + (lane & 31)) * kLdsStride + ko]);
-        b[i] = *reinterpret_cast<const half8_t*>(&Bs[(wn + 32 * i + (lane & 31)) * kLdsStride + ko]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = nt * kBN + wn + 32 * j + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int q = 0; q < 16; ++q) {
+        const int m = wm + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         if (m0 + m < seg_rows) {
           float* dst = shared ? p.y_shared + (int64_t)(m0 + m) * H : p.y_rows + (int64_t)(seg_row0 + m0 + m) * H;
-          dst[n] = G * acc[i][j][r];
+          dst[n] = G * acc[i][j][q];
         }
       }
     }
@@ -252,15 +254,17 @@ bool ffn_mfma_supported(int H, int I, int E) {
 
 size_t ffn_mfma_ws_bytes(int E) { return (size_t)(E + 2) * sizeof(int32_t); }
 
-hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev) {
+hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, const uint8_t* xq, const uint8_t* xs,
+                           uint8_t* hq, uint8_t* hs, hipStream_t s, hipEvent_t* ev) {
   const int64_t P = (int64_t)p.T * p.k;
   const int64_t max_tiles = (P + kBM - 1) / kBM + (P < p.E ? P : p.E) + (p.has_shared ? (p.T + kBM - 1) / kBM : 0);
   hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, p.off, p.E, p.T, p.has_shared, tile_start);
   if (ev && hipEventRecord(ev[2], s) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 64))), dim3(256), 0, s, p, tile_start);
+  hipLaunchKernelGGL(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 64))), dim3(256), 0, s, p, tile_start, xq, xs,
+                     hq, hs);
   if (ev && hipEventRecord(ev[3], s) != hipSuccess) return hipErrorInvalidValue;
   if (ev && hipEventRecord(ev[4], s) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, p, tile_start);
+  hipLaunchKernelGGL(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, p, tile_start, hq, hs);
   if (ev && hipEventRecord(ev[5], s) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
