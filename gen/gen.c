@@ -54,6 +54,15 @@ double gen_normal_at(uint64_t key, uint64_t j) {
   return (j & 1) ? r * sin(a) : r * cos(a);
 }
 
+/* normals 2p and 2p+1 of the stream at once (the same values as gen_normal_at) */
+static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+  double u1 = u01(key, 2 * p), u2 = u01(key, 2 * p + 1);
+  double r = sqrt(-2.0 * log(u1));
+  double a = 6.283185307179586476925286766559 * u2;
+  *z0 = r * cos(a);
+  *z1 = r * sin(a);
+}
+
 /* IEEE round-to-nearest-even FP32 -> BF16 (finite inputs) */
 static inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u;
@@ -95,15 +104,20 @@ static void build_grids(void) {
   grids_ready = 1;
 }
 
-/* nearest grid point, ties to the even code; v >= 0; grid ascending */
+/* nearest grid point, ties to the even code; v >= 0; grid strictly ascending.
+ * The distance to the grid is unimodal, so the nearest point is one of the two
+ * neighbours of v, found by bisection. */
 static int nearest_code(const double* grid, int n, double v) {
-  int best = 0;
-  double bd = fabs(v - grid[0]);
-  for (int c = 1; c < n; ++c) {
-    double d = fabs(v - grid[c]);
-    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) { best = c; bd = d; }
+  if (v >= grid[n - 1]) return n - 1;
+  int lo = 0, hi = n - 1; /* grid[lo] <= v < grid[hi] */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (grid[mid] <= v) lo = mid; else hi = mid;
   }
-  return best;
+  double dl = v - grid[lo], dh = grid[hi] - v;
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (lo & 1) ? hi : lo;
 }
 
 /*
@@ -118,39 +132,47 @@ int gen_nvfp4_bank(uint64_t key, double sigma, int64_t n_exp, int64_t N, int64_t
   if (K % 16 != 0) return -1;
   build_grids();
   int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t e = 0; e < n_exp; ++e) {
-    const int64_t base = e * N * K;
+#pragma omp parallel
+  {
+    /* one staging buffer per thread, reused across experts */
     double* w = (double*)malloc(sizeof(double) * (size_t)(N * K));
     if (!w) {
 #pragma omp atomic write
       bad = 1;
-      continue;
     }
-    double amax = 0.0;
-    for (int64_t i = 0; i < N * K; ++i) {
-      w[i] = sigma * gen_normal_at(key, (uint64_t)(base + i));
-      if (fabs(w[i]) > amax) amax = fabs(w[i]);
-    }
-    float G = (float)(amax / (6.0 * 448.0));
-    gscale[e] = G;
-    for (int64_t n = 0; n < N; ++n) {
-      for (int64_t b = 0; b < K / 16; ++b) {
-        const double* wb = w + n * K + b * 16;
-        double bmax = 0.0;
-        for (int j = 0; j < 16; ++j)
-          if (fabs(wb[j]) > bmax) bmax = fabs(wb[j]);
-        int sc = G > 0.0f ? nearest_code(ue4m3_val, 127, bmax / (6.0 * (double)G)) : 0;
-        scales[(e * N + n) * (K / 16) + b] = (uint8_t)sc;
-        double s = ue4m3_val[sc] * (double)G;
-        for (int j = 0; j < 16; j += 2) {
-          uint8_t nib[2];
-          for (int h = 0; h < 2; ++h) {
-            double v = wb[j + h];
-            int mag = s > 0.0 ? nearest_code(e2m1_mag, 8, fabs(v) / s) : 0;
-            nib[h] = (uint8_t)(mag | (signbit(v) ? 8 : 0));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t e = 0; e < n_exp; ++e) {
+      if (!w) continue;
+      const int64_t base = e * N * K;
+      double amax = 0.0;
+      for (int64_t i = 0; i < N * K; i += 2) { /* base and N*K are even */
+        double z0, z1;
+        normal_pair(key, (uint64_t)(base + i) >> 1, &z0, &z1);
+        w[i] = sigma * z0;
+        w[i + 1] = sigma * z1;
+        if (fabs(w[i]) > amax) amax = fabs(w[i]);
+        if (fabs(w[i + 1]) > amax) amax = fabs(w[i + 1]);
+      }
+      float G = (float)(amax / (6.0 * 448.0));
+      gscale[e] = G;
+      for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / 16; ++b) {
+          const double* wb = w + n * K + b * 16;
+          double bmax = 0.0;
+          for (int j = 0; j < 16; ++j)
+            if (fabs(wb[j]) > bmax) bmax = fabs(wb[j]);
+          int sc = G > 0.0f ? nearest_code(ue4m3_val, 127, bmax / (6.0 * (double)G)) : 0;
+          scales[(e * N + n) * (K / 16) + b] = (uint8_t)sc;
+          double s = ue4m3_val[sc] * (double)G;
+          for (int j = 0; j < 16; j += 2) {
+            uint8_t nib[2];
+            for (int h = 0; h < 2; ++h) {
+              double v = wb[j + h];
+              int mag = s > 0.0 ? nearest_code(e2m1_mag, 8, fabs(v) / s) : 0;
+              nib[h] = (uint8_t)(mag | (signbit(v) ? 8 : 0));
+            }
+            codes[(e * N + n) * (K / 2) + (b * 16 + j) / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
           }
-          codes[(e * N + n) * (K / 2) + (b * 16 + j) / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
         }
       }
     }

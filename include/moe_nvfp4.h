@@ -89,11 +89,13 @@ typedef struct {
  *   hq [R][I/2], hs [R][I/16] : A4 encoding of h
  * R = T*k routed rows in permuted-row order, followed by T shared-expert rows
  * (token order) when has_shared.
- *   events (host array, nullable): 2*MOE_FFN_KERNELS created HIP events;
- *   events[2i] and events[2i+1] are recorded on the call's stream right before
- *   and right after kernel i of moe_expert_ffn (0: A4(x), 1: gate/up + SwiGLU
- *   + A4(h), 2: down projection).  The kernels are the same with or without
- *   dumps and events.                                                         */
+ *   events (host array, nullable): 2*MOE_FFN_KERNELS created HIP events (a null
+ *   entry is MOE_EINVAL); events[2i] and events[2i+1] take the start and end
+ *   timestamps of kernel i of moe_expert_ffn itself (0: A4(x), 1: gate/up +
+ *   SwiGLU + A4(h), 2: down projection), so hipEventElapsedTime gives that
+ *   kernel's execution time; a kernel that a path does not run has both events
+ *   recorded at the same point.  The kernels are the same with or without dumps
+ *   and events.                                                              */
 #define MOE_FFN_KERNELS 3
 typedef struct {
   uint8_t* xq;
@@ -107,12 +109,14 @@ typedef struct {
 int moe_abi_version(void);
 const char* moe_strerror(int code);
 
-/* Bytes of workspace that moe_route, moe_permute and moe_expert_ffn need for
- * up to T_max tokens of layer L (one workspace may serve all three calls, not
- * concurrently).  Returns 0 if L or T_max is invalid.  Host call.             */
+/* Bytes of workspace that moe_route, moe_permute, moe_expert_ffn and
+ * moe_layer_forward need for up to T_max tokens of layer L (one workspace may
+ * serve all of them, not concurrently).  Returns 0 if L or T_max is invalid.
+ * Host call.  The workspace is scratch: nothing is kept between calls.       */
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max);
 
-/* Router: logits l[t][e] = sum_h x[t][h] * router_w[e][h] (FP32 accumulation),
+/* Router: logits l[t][e] = sum_h x[t][h] * router_w[e][h] (selection on FP64
+ * sums of the exact products, see route.hip),
  * the k largest per token in descending order (equal logits: lower expert id
  * first), and w[t][j] = softmax over the k selected logits.
  *   x        [T][H] BF16 hidden states (bit patterns)
@@ -165,12 +169,13 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
  * (topk_idx, topk_w [T][k]; expert_off [E+1]; row2pair, pair2row [T*k];
  * y_rows [T*k][H]; y_shared [T][H] (nullable iff !has_shared); out [T][H];
  * residual nullable).  For decode batches (T <= 4, H <= 2048, E <= 512, no
- * dumps requested; events allowed) it runs fused in four kernels: FP64 router
- * logits (events 0/1 of moe_debug), gate/up (events 2/3),
- * whose workgroups select the top k, form the softmax weights and derive the
- * permutation themselves; down projection (events 4/5); combine.  Otherwise it runs the four
- * calls in order.  Results are identical either way.  ws must hold
- * moe_workspace_bytes(L, T_max) bytes with T <= T_max.
+ * dumps requested; events allowed) it runs fused in five kernels: router
+ * (FP64 logits and the A4 codes of x), routing (one workgroup: top k, softmax
+ * weights, permutation and a table of the experts to run; events 0/1 of
+ * moe_debug span these two), gate/up (events 2/3), down projection (events
+ * 4/5), combine.  Otherwise it runs the four calls in order.  Results are
+ * identical either way.  ws must hold moe_workspace_bytes(L, T_max) bytes with
+ * T <= T_max.
  * Pages: capy-flash README v0.5.4, "What it does" (a routed layer computed
  * per expert id with the W4A4 quantization).                                */
 int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const uint16_t* residual,

@@ -139,8 +139,13 @@ def _debug(debug):
     evs = debug.get("events")  # sequence of 2 * FFN_KERNELS recorded torch.cuda.Event
     ev_arr = None
     if evs is not None:
-        assert len(evs) == 2 * FFN_KERNELS
-        ev_arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+        if len(evs) != 2 * FFN_KERNELS:
+            raise ValueError("debug['events'] takes %d events" % (2 * FFN_KERNELS))
+        handles = [e.cuda_event for e in evs]
+        if not all(handles):
+            raise ValueError("record every event once (event.record()) before passing it: "
+                             "torch creates the HIP event on first use")
+        ev_arr = (ctypes.c_void_p * len(evs))(*handles)
     dbg = Debug(_ptr(debug.get("xq")), _ptr(debug.get("xs")), _ptr(debug.get("h")), _ptr(debug.get("hq")),
                 _ptr(debug.get("hs")), ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if evs else None)
     dbg._keep = ev_arr

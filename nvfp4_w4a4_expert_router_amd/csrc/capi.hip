@@ -53,6 +53,7 @@ int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
 }
 
 // workspace of each call, laid out from offset 0 (calls never overlap in time)
+
 size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E)); }
 
 size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
@@ -102,10 +103,11 @@ const char* moe_strerror(int code) {
   }
 }
 
-// FP64 logits of the fused decode path sit before the expert-FFN workspace
+// FP64 logits and the slot table of the fused decode path sit before the
+// expert-FFN workspace
 size_t fused_logits_ws(const moe_layer* L, int64_t T) {
   const int64_t t = T < 4 ? T : 4;
-  return align_up((size_t)t * L->E * sizeof(double));
+  return align_up((size_t)t * L->E * sizeof(double)) + align_up((size_t)t * L->k * sizeof(int4));
 }
 
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
@@ -131,7 +133,8 @@ int moe_route(const moe_layer* L, const uint16_t* x, int64_t T, const float* log
   } else if (!aligned16(logits_in)) {
     return MOE_EINVAL;
   }
-  return launch_rc(launch_route(x, L->router_w, T, L->H, L->E, L->k, logits_in, topk_idx, topk_w, ws, stream));
+  return launch_rc(launch_route(x, L->router_w, T, L->H, L->E, L->k, logits_in, topk_idx, topk_w,
+                                logits_in ? nullptr : ws, stream));
 }
 
 int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t* expert_off, int32_t* row2pair,
@@ -146,6 +149,16 @@ int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t*
   return launch_rc(launch_permute(topk_idx, T, L->k, L->E, expert_off, row2pair, pair2row, ws, stream));
 }
 
+// dumps aligned or null; when an event array is given, every entry is a created event
+static bool debug_ok(const moe_debug* d) {
+  if (!d) return true;
+  if (!opt_ok(d->xq) || !opt_ok(d->xs) || !opt_ok(d->h) || !opt_ok(d->hq) || !opt_ok(d->hs)) return false;
+  if (d->events)
+    for (int i = 0; i < 2 * MOE_FFN_KERNELS; ++i)
+      if (!d->events[i]) return false;
+  return true;
+}
+
 int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
                    const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
                    size_t ws_bytes, hipStream_t stream) {
@@ -155,8 +168,7 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   if (T == 0) return MOE_OK;
   if (!ptr_ok(x) || !ptr_ok(expert_off) || !ptr_ok(row2pair) || !ptr_ok(y_rows) || !ptr_ok(ws)) return MOE_EINVAL;
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
-  if (dbg && (!opt_ok(dbg->xq) || !opt_ok(dbg->xs) || !opt_ok(dbg->h) || !opt_ok(dbg->hq) || !opt_ok(dbg->hs)))
-    return MOE_EINVAL;
+  if (!debug_ok(dbg)) return MOE_EINVAL;
   const FfnWs lay = ffn_ws(L, T);
   if (ws_bytes < lay.end) return MOE_EWORKSPACE;
   char* base = static_cast<char*>(ws);
@@ -169,16 +181,19 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   const bool decode_path = ffn_decode_supported(L->H, L->I, T);
   const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E);
   const bool stream_path = !decode_path && !mfma_path && ffn_stream_supported(L->H, L->I);
-  const bool self_encoding = decode_path || stream_path;  // these kernels encode x themselves
+  const bool self_encoding = stream_path;  // these kernels encode x themselves
   const bool want_xdump = dbg && (dbg->xq || dbg->xs);
-  // kernel 0: A4(x) into the workspace (dequantized FP16 copy for the matrix cores
-  // and the generic kernels; codes for the dumps)
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
-  if (!self_encoding || want_xdump)
+  // kernel 0: A4(x) codes into the workspace (plus a dequantized FP16 copy for
+  // the generic kernels)
+  if (!self_encoding || want_xdump) {
     if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
-                                         self_encoding || mfma_path ? nullptr : xh, stream))))
+                                         self_encoding || mfma_path || decode_path ? nullptr : xh, stream,
+                                         ev ? ev[0] : nullptr,
+                                         ev ? ev[1] : nullptr))))
       return rc;
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
+  } else if (ev && record_idle(stream, ev[0], ev[1]) != hipSuccess) {
+    return MOE_ELAUNCH;
+  }
   if (dbg && dbg->xq)
     if (hipMemcpyAsync(dbg->xq, xq, (size_t)T * (L->H / 2), hipMemcpyDeviceToDevice, stream) != hipSuccess)
       return MOE_ELAUNCH;
@@ -198,6 +213,8 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.row2pair = row2pair;
   p.x = x;
   p.xh = xh;
+  p.xq = xq;
+  p.xs = xs;
   p.w13 = L->w13;
   p.w2 = L->w2;
   p.sh13 = L->sh13;
@@ -252,6 +269,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
       !ptr_ok(pair2row) || !ptr_ok(y_rows) || !ptr_ok(out) || !ptr_ok(ws) || !opt_ok(residual))
     return MOE_EINVAL;
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
+  if (!debug_ok(dbg)) return MOE_EINVAL;
   const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
   if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps) {
     if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
@@ -263,12 +281,28 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   const FfnWs lay = ffn_ws(L, T);
   if (ws_bytes < lg_bytes + lay.end) return MOE_EWORKSPACE;
   char* base = static_cast<char*>(ws);
-  double* logits = reinterpret_cast<double*>(base);
   char* fbase = base + lg_bytes;
   hipEvent_t* ev = dbg ? dbg->events : nullptr;
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ELAUNCH;
-  if ((rc = launch_rc(launch_router_logits64(x, L->router_w, T, L->H, L->E, logits, stream)))) return rc;
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ELAUNCH;
+  // kernel 1: FP64 logits + A4(x), then one workgroup: the routing and slot table
+  RouteDecodeParams q = {};
+  q.x = x;
+  q.W = L->router_w;
+  q.T = (int)T;
+  q.H = L->H;
+  q.E = L->E;
+  q.k = L->k;
+  q.g_in = L->a_gscale_in;
+  q.logits = reinterpret_cast<double*>(base);
+  q.slot_tab = reinterpret_cast<int4*>(base + align_up((size_t)T * L->E * sizeof(double)));
+  q.xq = reinterpret_cast<uint8_t*>(fbase + lay.xq);
+  q.xs = reinterpret_cast<uint8_t*>(fbase + lay.xs);
+  q.idx = topk_idx;
+  q.w = topk_w;
+  q.off = expert_off;
+  q.r2p = row2pair;
+  q.p2r = pair2row;
+  if ((rc = launch_rc(launch_route_decode(q, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)))) return rc;
+  // kernels 2, 3: gate/up and down over the slot table; kernel 4: combine
   FfnParams p = {};
   p.H = L->H;
   p.I = L->I;
@@ -281,6 +315,9 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.off = expert_off;
   p.row2pair = row2pair;
   p.x = x;
+  p.xq = q.xq;
+  p.xs = q.xs;
+  p.slot_tab = q.slot_tab;
   p.w13 = L->w13;
   p.w2 = L->w2;
   p.sh13 = L->sh13;
@@ -291,15 +328,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
   p.shared_split = 1;
-  p.logits64 = logits;
-  p.out_idx = topk_idx;
-  p.out_w = topk_w;
-  p.out_off = expert_off;
-  p.out_r2p = row2pair;
-  p.out_p2r = pair2row;
-  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ELAUNCH;
-  if ((rc = launch_rc(launch_gateup_fused(p, stream)))) return rc;
-  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ELAUNCH;
+  if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
   if ((rc = launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr)))) return rc;
   return launch_rc(launch_combine(T, L->H, L->k, y_rows, p.y_shared, pair2row, topk_w, residual, out, stream));
 }

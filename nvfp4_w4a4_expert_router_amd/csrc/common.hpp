@@ -6,6 +6,7 @@
 // scales, FP32 per-expert scale.  A4 (capy-flash README v0.5.4, "What it
 // does" / "Serve"): activations encoded the same way before every expert.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,9 +25,11 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- formats
 // UE4M3 code (0..126) -> value: exponent field bits 6..3 (bias 7), mantissa
 // bits 2..0; exponent 0 is subnormal m * 2^-9.
+// Written without a branch as 2^(max(e,1) - 10) * (8 [e > 0] + m), exact.
 __device__ __forceinline__ float ue4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t eb = e > 1u ? e : 1u;
+  return __uint_as_float((eb + 117u) << 23) * (float)((e > 0u ? 8u : 0u) + m);
 }
 
 // E2M1 magnitude code (0..7) -> value {0, .5, 1, 1.5, 2, 3, 4, 6}.
@@ -72,6 +75,50 @@ __device__ __forceinline__ uint32_t elem_code(float v, float s) {
           (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
           (uint32_t)(a > 5.0f * s);
   return mag | (__float_as_uint(v) >> 31 << 3);
+}
+
+// A4 encoding of one 16-element block (global scale g, g6 = 6g): returns the
+// UE4M3 scale code; the 16 E2M1 codes go to *packed, element i in bits
+// 4(i % 8).. of word i / 8 (the low nibble of each byte first).
+__device__ __forceinline__ uint32_t encode_a4_block16(const float (&v)[16], float g, float g6, uint2* packed) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = scale_code(amax, g6);
+  const float s = ue4m3_value(sc) * g;
+  uint32_t p0 = 0u, p1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p0 |= elem_code(v[i], s) << (4 * i);
+    p1 |= elem_code(v[8 + i], s) << (4 * i);
+  }
+  *packed = make_uint2(p0, p1);
+  return sc;
+}
+
+// Two E2M1 codes (byte kByte of w, low nibble first) -> two exact FP16 values
+template <int kByte>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
+}
+
+// 32 codes (16 B: two 16-element blocks) times their UE4M3 scales (sc2: low
+// byte = first block) -> 32 FP16 values at dst (16-byte aligned).  Each
+// product has at most 6 significant bits and lies in [2^-10, 2688]: exact.
+__device__ __forceinline__ void decode32_fp16(uint4 q, uint32_t sc2, half_t* dst) {
+  const half_t s0 = (half_t)ue4m3_value(sc2 & 0xFFu), s1 = (half_t)ue4m3_value((sc2 >> 8) & 0xFFu);
+  const half2_t S0 = half2_t{s0, s0}, S1 = half2_t{s1, s1};
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  half8_t out[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const half2_t S = d < 2 ? S0 : S1;
+    const half2_t a = fp4x2<0>(w[d]) * S, b = fp4x2<1>(w[d]) * S, c = fp4x2<2>(w[d]) * S, e = fp4x2<3>(w[d]) * S;
+    out[d] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+  }
+  half8_t* o = reinterpret_cast<half8_t*>(dst);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = out[d];
 }
 
 // BF16 bits -> FP32 (exact)
@@ -304,35 +351,71 @@ struct FfnParams {
   float* y_shared;
   // decode kernels only: the shared expert takes one slot per token
   int shared_split;
-  // fused decode path (moe_layer_forward): routing computed inside the gate/up
-  // kernel from FP64 logits; workgroup 0 publishes it
-  const double* logits64;  // [T][E]
-  int32_t* out_idx;
-  float* out_w;
-  int32_t* out_off;
-  int32_t* out_r2p;
-  int32_t* out_p2r;
+  // decode kernels: A4(x) codes [T][H/2] and scales [T][H/16]
+  const uint8_t* xq;
+  const uint8_t* xs;
+  // decode kernels, fused path: routed slot s -> {expert (or -1), first row,
+  // rows, tokens of the rows (one byte each)}; null: slots from expert_off
+  const int4* slot_tab;
 };
 
-// launchers (one translation unit each)
+// Fused decode routing (moe_layer_forward, T <= 4): FP64 logits and A4(x),
+// then in one workgroup top k, softmax weights, permutation and slot table.
+struct RouteDecodeParams {
+  const uint16_t* x;   // [T][H] BF16
+  const float* W;      // [E][H]
+  int T, H, E, k;
+  float g_in;
+  double* logits;      // [T][E]
+  uint8_t* xq;         // [T][H/2]
+  uint8_t* xs;         // [T][H/16]
+  int32_t* idx;
+  float* w;
+  int32_t* off;
+  int32_t* r2p;
+  int32_t* p2r;
+  int4* slot_tab;      // [T*k]
+};
+
+// Launch with optional events that take the kernel's own start (e0) and end
+// (e1) timestamps (the dispatch's, not the host's view of the stream); with
+// neither it is a plain launch.
+template <typename F, typename... Args>
+inline hipError_t launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1, Args... args) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+
+// the event pair of a kernel that has nothing to do: both taken at this point
+inline hipError_t record_idle(hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 && hipEventRecord(e0, s) != hipSuccess) return hipErrorInvalidValue;
+  if (e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+// launchers (one translation unit each); the event pairs (nullable) time the
+// kernel named by each, as launch_timed does
 hipError_t launch_quant_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
-                            uint8_t* scales, half_t* deq, hipStream_t s);
+                            uint8_t* scales, half_t* deq, hipStream_t s, hipEvent_t e0 = nullptr,
+                            hipEvent_t e1 = nullptr);
 size_t route_ws_bytes(int64_t T, int E);
 hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int E, int k, const float* logits_in,
                         int32_t* idx, float* w, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int64_t T, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* off, int32_t* r2p, int32_t* p2r,
                           void* ws, hipStream_t s);
-// ev_before / ev_after (nullable) are recorded around the kernel on stream s
 hipError_t launch_ffn_gateup(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 // decode kernels (T <= 8, H <= 2048, I / 32 a power of two <= 64)
 bool ffn_decode_supported(int H, int I, int64_t T);
 hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 bool fused_decode_supported(int H, int I, int E, int k, int64_t T);
-hipError_t launch_gateup_fused(const FfnParams& p, hipStream_t s);
-hipError_t launch_router_logits64(const uint16_t* x, const float* W, int64_t T, int H, int E, double* logits,
-                                  hipStream_t s);
+bool route_decode_supported(int H, int E, int k, int64_t T);
+hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 // matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
 bool ffn_mfma_supported(int H, int I, int E);

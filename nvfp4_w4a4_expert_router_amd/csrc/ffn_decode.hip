@@ -23,11 +23,6 @@ bool ffn_stream_supported(int H, int I);
 
 namespace {
 
-template <int kByte>
-__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
-}
-
 __device__ __forceinline__ float dot8(uint32_t w, half8_t a, float c) {
   c = __builtin_amdgcn_fdot2(fp4x2<0>(w), half2_t{a[0], a[1]}, c, false);
   c = __builtin_amdgcn_fdot2(fp4x2<1>(w), half2_t{a[2], a[3]}, c, false);
@@ -155,159 +150,55 @@ constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use th
 // ---------------------------------------------------------------- gate/up
 // Slots: [0, n_routed_slots) routed experts in ascending id order; then the
 // shared expert, one slot per token (so no workgroup carries T activation rows).
-//
-// Routing prologue (fused decode path only): waves 0..T-1 each take one token's
-// FP64 logits, select the top k (sorted lanes + DPP tournament: value
-// descending, id ascending) and form the softmax weights; wave 0 then derives
-// the permutation of the T*k pairs (expert ascending, token ascending) and
-// every workgroup finds its own expert and rows from it.  Workgroup 0 writes
-// topk_idx, topk_w, expert_off, row2pair, pair2row for the later kernels.
-constexpr int kMaxPairs = kDecMaxT * 32;
-constexpr int kMaxRouteE = 512;
-
-struct Routing {
-  double sv[kDecMaxT][kTopkScratch];  // top-k scratch, one per token wave
-  int si[kDecMaxT][kTopkScratch];
-  int e[kMaxPairs];                   // expert of pair p = t*k + j
-  float w[kMaxPairs];
-  int cnt[kMaxRouteE];                // pairs per expert
-  int off[kMaxRouteE + 1];            // exclusive prefix sum of cnt
-  int nzr[kMaxRouteE];                // active experts with a smaller id
-};
-
-// Routing of the (few) tokens inside a workgroup.  Top k per token wave and
-// softmax exactly as moe_route; then a histogram of the T*k pairs over the
-// experts and one wave scan give expert_off and the distinct-expert ranks
-// (the slot order).  Workgroup 0 publishes topk_idx, topk_w, expert_off,
-// row2pair and pair2row.
-__device__ __forceinline__ void route_in_workgroup(const FfnParams& p, Routing& R) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int T = p.T, E = p.E, k = p.k, P = T * k;
-  for (int e = tid; e < E; e += 256) R.cnt[e] = 0;
-  if (wave < T) {
-    double v[8];
-    int id[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane + kWave * j;
-      v[j] = e < E ? p.logits64[(int64_t)wave * E + e] : -INFINITY;
-      id[j] = e < E ? e : 0x7FFFFFFF;
-    }
-    double my_v = 0.0;
-    int my_e = 0;
-    wave_topk512(v, id, k, R.sv[wave], R.si[wave], &my_v, &my_e);
-    const float wk = topk_softmax_weight(my_v, k);
-    if (lane < k) {
-      R.e[wave * k + lane] = my_e;
-      R.w[wave * k + lane] = wk;
-    }
-  }
-  __syncthreads();
-  for (int pi = tid; pi < P; pi += 256) atomicAdd(&R.cnt[R.e[pi]], 1);
-  __syncthreads();
-  if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
-    int c[8], nz[8], sc = 0, snz = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane * 8 + j;
-      c[j] = e < E ? R.cnt[e] : 0;
-      nz[j] = c[j] > 0;
-      sc += c[j];
-      snz += nz[j];
-    }
-    int ic = sc, inz = snz;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int a = __shfl_up(ic, d), b = __shfl_up(inz, d);
-      if (lane >= d) {
-        ic += a;
-        inz += b;
-      }
-    }
-    int rc = ic - sc, rnz = inz - snz;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane * 8 + j;
-      if (e < E) {
-        R.off[e] = rc;
-        R.nzr[e] = rnz;
-      }
-      rc += c[j];
-      rnz += nz[j];
-    }
-    if (lane == 63) R.off[E] = ic;
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) {  // publish the routing
-    for (int e = tid; e <= E; e += 256) p.out_off[e] = R.off[e];
-    for (int pi = tid; pi < P; pi += 256) {
-      const int t = pi / k, ep = R.e[pi];
-      int before = 0;  // earlier tokens that chose the same expert
-      for (int t2 = 0; t2 < t; ++t2)
-        for (int j2 = 0; j2 < k; ++j2) before += R.e[t2 * k + j2] == ep;
-      const int row = R.off[ep] + before;
-      p.out_idx[pi] = ep;
-      p.out_w[pi] = R.w[pi];
-      p.out_p2r[pi] = row;
-      p.out_r2p[row] = pi;
-    }
-  }
-}
-
-template <bool kFused>
+// A routed slot's expert comes from the slot table of the fused path (one
+// load) or from expert_off (one round trip and a wave scan).  The A4 codes of
+// x are read from the workspace and decoded to FP16 in LDS while the weight
+// burst is in flight.
+template <bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
-  __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized, [T][H]
+  __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
   __shared__ float gu[kDecMaxT][64];
   __shared__ int toks[kDecMaxT];
-  __shared__ int slot_info[3];
-  __shared__ Routing R;
   const int H = p.H, I = p.I, T = p.T;
   const int n_cg = I / 32;
   const int cg = blockIdx.x % n_cg, slot = blockIdx.x / n_cg;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
-  const int nblk = H / 16;
-
-  // 1. x blocks of every token (no dependency on the routing)
-  uint4 xa[2], xb[2];  // up to 2 blocks per thread (T * H / 16 <= 512)
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int task = tid + 256 * q;
-    if (task < T * nblk) {
-      const uint4* src = reinterpret_cast<const uint4*>(p.x + (int64_t)task * 16);
-      xa[q] = src[0];
-      xb[q] = src[1];
-    }
-  }
-  // 2. this slot's expert and activation rows
   const int sh_slot = slot - p.n_routed_slots;
   const bool shared = p.has_shared && sh_slot >= 0;
+  // 1. the slot's table entry, then the A4(x) codes (32 elements per thread)
+  int4 ent = make_int4(0, 0, 0, 0);
+  if (kTable && !shared) ent = p.slot_tab[slot];
+  const int xchunks = H / 32;
+  const int xt = tid / xchunks, xc = tid % xchunks;
+  const bool xmine = xt < T;  // T * H / 32 <= 256
+  uint4 xq4 = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t xs2 = 0u;
+  if (xmine) {
+    xq4 = *reinterpret_cast<const uint4*>(p.xq + (size_t)xt * (H / 2) + xc * 16);
+    xs2 = *reinterpret_cast<const uint16_t*>(p.xs + (size_t)xt * (H / 16) + xc * 2);
+  }
+  // 2. this slot's expert and activation rows
   int e, row0, nrows;
   if (shared) {
     e = 0;
     row0 = p.shared_split ? sh_slot : 0;
     nrows = p.shared_split ? 1 : T;
-  } else if (kFused) {
-    route_in_workgroup(p, R);
-    if (tid == 0) slot_info[0] = -1;
-    __syncthreads();
-    for (int ee = tid; ee < p.E; ee += 256)
-      if (R.cnt[ee] > 0 && R.nzr[ee] == slot) slot_info[0] = ee;
-    __syncthreads();
-    e = __builtin_amdgcn_readfirstlane(slot_info[0]);
+  } else if (kTable) {
+    e = __builtin_amdgcn_readfirstlane(ent.x);
+    row0 = __builtin_amdgcn_readfirstlane(ent.y);
+    nrows = __builtin_amdgcn_readfirstlane(ent.z);
     if (e < 0) return;
-    row0 = __builtin_amdgcn_readfirstlane(R.off[e]);
-    nrows = __builtin_amdgcn_readfirstlane(R.cnt[e]);
   } else {
     e = active_expert(p.off, p.E, slot, &row0, &nrows);
     if (e < 0) return;
   }
-  // tokens of the rows, then the weight burst (buffer loads: one instruction
-  // per 16 B, the row stride in the scalar offset)
+  // tokens of the rows and the per-expert scale, then the weight burst (buffer
+  // loads: one instruction per 16 B, the row stride in the scalar offset)
   int tok = 0;
-  if (!kFused && !shared && tid < nrows) tok = p.row2pair[row0 + tid] / p.k;
+  if (!kTable && !shared && tid < nrows) tok = p.row2pair[row0 + tid] / p.k;
   const uint8_t* bcodes = shared ? p.sh13.codes : p.w13.codes;
   const uint8_t* bscales = shared ? p.sh13.scales : p.w13.scales;
-  const float* bg = shared ? p.sh13.gscale : p.w13.gscale;
+  const float gsc = (shared ? p.sh13.gscale : p.w13.gscale)[e];
   const int nch = H / 32;
   const uint32_t qrow = (uint32_t)H / 2, srow = (uint32_t)H / 16;
   const auto rq = buffer_rsrc(bcodes + (int64_t)e * 2 * I * qrow, 2u * I * qrow);
@@ -324,49 +215,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     q[j] = buffer_load16(rq, vq, rowoff * qrow);
     sc[j] = buffer_load2(rs, vs, rowoff * srow);
   }
-  const float G = bg[e] * p.g_in;
-  // 3. A4(x) into LDS while the weights are in flight
-  const float g6 = 6.0f * p.g_in;
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const int task = tid + 256 * qi;
-    if (task < T * nblk) {
-      const uint32_t wv[8] = {xa[qi].x, xa[qi].y, xa[qi].z, xa[qi].w, xb[qi].x, xb[qi].y, xb[qi].z, xb[qi].w};
-      float v[16];
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = __uint_as_float(wv[i] << 16);
-        v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
-        amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
-      }
-      const uint32_t scode = scale_code(amax, g6);
-      const float sv = ue4m3_value(scode);
-      const float s = sv * p.g_in;
-      half8_t h0, h1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        h0[i] = (half_t)(e2m1_value(elem_code(v[i], s)) * sv);
-        h1[i] = (half_t)(e2m1_value(elem_code(v[8 + i], s)) * sv);
-      }
-      half8_t* dst = reinterpret_cast<half8_t*>(xs + (size_t)task * 16);
-      dst[0] = h0;
-      dst[1] = h1;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (shared) {
-    if (tid < nrows) toks[tid] = row0 + tid;
-  } else if (kFused) {
-    if (tid == 0) {  // tokens choosing e, ascending (at most one pair per token)
-      int r = 0;
-      for (int t = 0; t < T; ++t)
-        for (int j = 0; j < p.k; ++j)
-          if (R.e[t * p.k + j] == e) toks[r++] = t;
-    }
-  } else if (tid < nrows) {
-    toks[tid] = tok;
-  }
+  const float G = gsc * p.g_in;
+  // 3. A4(x) to FP16 in LDS while the weights are in flight
+  if (xmine) decode32_fp16(xq4, xs2, xs + (size_t)xt * H + xc * 32);
+  if (tid < nrows) toks[tid] = shared ? row0 + tid : kTable ? (int)(((unsigned)ent.w >> (8 * tid)) & 0xFFu) : tok;
   __syncthreads();
   // 4. dot products, one activation row at a time
   for (int rr = 0; rr < nrows; ++rr) {
@@ -414,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // W2 rows n, I/32 chunks per row = kLPR lanes per row, 64/kLPR rows per wave
 // instruction.  Thread (w, l): chunk l % kLPR of rows
 // n0 + (64/kLPR) * (w + 4 j) + l / kLPR, j < 16.
-template <int kLPR>
+template <int kLPR, bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_decode(FfnParams p) {
   constexpr int kRPI = 64 / kLPR;       // rows per wave instruction
   constexpr int kRowsWG = 64 * kRPI;    // 4 waves x 16 x kRPI
@@ -429,13 +281,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     e = 0;
     row0 = p.shared_split ? sh_slot : 0;
     nrows = p.shared_split ? 1 : T;
+  } else if (kTable) {
+    const int4 ent = p.slot_tab[slot];
+    e = __builtin_amdgcn_readfirstlane(ent.x);
+    row0 = __builtin_amdgcn_readfirstlane(ent.y);
+    nrows = __builtin_amdgcn_readfirstlane(ent.z);
+    if (e < 0) return;
   } else {
     e = active_expert(p.off, p.E, slot, &row0, &nrows);
     if (e < 0) return;
   }
   const uint8_t* bcodes = shared ? p.sh2.codes : p.w2.codes;
   const uint8_t* bscales = shared ? p.sh2.scales : p.w2.scales;
-  const float* bg = shared ? p.sh2.gscale : p.w2.gscale;
+  const float gsc = (shared ? p.sh2.gscale : p.w2.gscale)[e];
   const int ch = l % kLPR;
   const int base_n = nb * kRowsWG + l / kLPR;
   // activation chunk of the first row, then the weight burst
@@ -458,7 +316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     q[j] = buffer_load16(rq, vq, (uint32_t)(4 * kRPI * j) * qrow);
     sc[j] = buffer_load2(rs, vs, (uint32_t)(4 * kRPI * j) * srow);
   }
-  const float G = bg[e] * p.g_mid;
+  const float G = gsc * p.g_mid;
   float* dst0 = shared ? p.y_shared + (int64_t)row0 * H : p.y_rows + (int64_t)row0 * H;
   for (int rr = 0; rr < nrows; ++rr) {
     if (rr > 0) {
@@ -499,44 +357,38 @@ static int decode_slots(const FfnParams& p) {
 
 hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = decode_slots(p);
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0)
-    hipLaunchKernelGGL(k_gateup_decode<false>, dim3((unsigned)(slots * (p.I / 32))), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  const dim3 grid((unsigned)(slots * (p.I / 32)));
+  if (p.slot_tab) return launch_timed(k_gateup_decode<true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  return launch_timed(k_gateup_decode<false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
 }
 
 bool fused_decode_supported(int H, int I, int E, int k, int64_t T) {
-  return ffn_decode_supported(H, I, T) && E <= 8 * kWave && k <= 32 && T >= 1;
+  return ffn_decode_supported(H, I, T) && route_decode_supported(H, E, k, T);
 }
 
-hipError_t launch_gateup_fused(const FfnParams& p, hipStream_t s) {
-  const int slots = decode_slots(p);
-  hipLaunchKernelGGL(k_gateup_decode<true>, dim3((unsigned)(slots * (p.I / 32))), dim3(256), 0, s, p);
-  return hipGetLastError();
+template <bool kTable>
+static hipError_t launch_down_lpr(const FfnParams& p, int lpr, dim3 grid, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  switch (lpr) {
+    case 1: return launch_timed(k_down_decode<1, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    case 2: return launch_timed(k_down_decode<2, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    case 4: return launch_timed(k_down_decode<4, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    case 8: return launch_timed(k_down_decode<8, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    case 16: return launch_timed(k_down_decode<16, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    case 32: return launch_timed(k_down_decode<32, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+    default: return launch_timed(k_down_decode<64, kTable>, grid, dim3(256), 0, s, e0, e1, p);
+  }
 }
 
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = decode_slots(p);
   const int lpr = p.I / 32;
   const int rows_wg = 64 * (64 / lpr);
-  const unsigned grid = (unsigned)(slots * ((p.H + rows_wg - 1) / rows_wg));
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0) {
-    switch (lpr) {
-      case 1: hipLaunchKernelGGL(k_down_decode<1>, dim3(grid), dim3(256), 0, s, p); break;
-      case 2: hipLaunchKernelGGL(k_down_decode<2>, dim3(grid), dim3(256), 0, s, p); break;
-      case 4: hipLaunchKernelGGL(k_down_decode<4>, dim3(grid), dim3(256), 0, s, p); break;
-      case 8: hipLaunchKernelGGL(k_down_decode<8>, dim3(grid), dim3(256), 0, s, p); break;
-      case 16: hipLaunchKernelGGL(k_down_decode<16>, dim3(grid), dim3(256), 0, s, p); break;
-      case 32: hipLaunchKernelGGL(k_down_decode<32>, dim3(grid), dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL(k_down_decode<64>, dim3(grid), dim3(256), 0, s, p); break;
-    }
-  }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  const dim3 grid((unsigned)(slots * ((p.H + rows_wg - 1) / rows_wg)));
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  if (p.slot_tab) return launch_down_lpr<true>(p, lpr, grid, s, ev_before, ev_after);
+  return launch_down_lpr<false>(p, lpr, grid, s, ev_before, ev_after);
 }
 
 }  // namespace moe

@@ -193,20 +193,15 @@ __global__ __launch_bounds__(256) void k_ffn_down(FfnParams p) {
 
 hipError_t launch_ffn_gateup(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = p.n_routed_slots + (p.has_shared ? 1 : 0);
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0) hipLaunchKernelGGL(k_ffn_gateup, dim3((unsigned)(slots * (p.I / 16))), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  return launch_timed(k_ffn_gateup, dim3((unsigned)(slots * (p.I / 16))), dim3(256), 0, s, ev_before, ev_after, p);
 }
 
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = p.n_routed_slots + (p.has_shared ? 1 : 0);
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0) hipLaunchKernelGGL(k_ffn_down, dim3((unsigned)(slots * (p.H / kWRows))), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  return launch_timed(k_ffn_down, dim3((unsigned)(slots * (p.H / kWRows))), dim3(256), 0, s, ev_before, ev_after,
+                      p);
 }
 
 }  // namespace moe

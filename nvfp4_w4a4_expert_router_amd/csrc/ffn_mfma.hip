@@ -32,27 +32,6 @@ constexpr int kLdsStride = kBK + 8;  // halfs per LDS row (+16 B against bank co
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-template <int kByte>
-__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
-}
-
-// 32 codes (16 B, two blocks) times their UE4M3 scales -> 32 FP16 into LDS
-__device__ __forceinline__ void decode32_to_lds(uint4 q, uint32_t sc2, half_t* dst) {
-  const half_t s0 = (half_t)ue4m3_value(sc2 & 0xFFu), s1 = (half_t)ue4m3_value((sc2 >> 8) & 0xFFu);
-  const half2_t S0 = half2_t{s0, s0}, S1 = half2_t{s1, s1};
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  half8_t out[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const half2_t S = d < 2 ? S0 : S1;
-    const half2_t a = fp4x2<0>(w[d]) * S, b = fp4x2<1>(w[d]) * S, c = fp4x2<2>(w[d]) * S, e = fp4x2<3>(w[d]) * S;
-    out[d] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
-  }
-  half8_t* o = reinterpret_cast<half8_t*>(dst);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) o[d] = out[d];
-}
 
 // row tile -> (expert slot, first row in the segment); slot E = shared expert
 __device__ __forceinline__ int find_tile(const int32_t* __restrict__ tile_start, int nseg, int mt) {
@@ -113,8 +92,8 @@ __device__ __forceinline__ void tile_mma(const uint8_t* __restrict__ arow_q, con
   fetch(0, st);
   for (int k0 = 0; k0 < K; k0 += kBK) {
     __syncthreads();  // the previous step's fragments are read
-    decode32_to_lds(st.aq, st.as, &As[r * kLdsStride + hf * 32]);
-    decode32_to_lds(st.bq, st.bs, &Bs[r * kLdsStride + hf * 32]);
+    decode32_fp16(st.aq, st.as, &As[r * kLdsStride + hf * 32]);
+    decode32_fp16(st.bq, st.bs, &Bs[r * kLdsStride + hf * 32]);
     __syncthreads();
     if (k0 + kBK < K) fetch(k0 + kBK, st);  // next step in flight during the MFMAs
 #pragma unroll
@@ -259,14 +238,13 @@ hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, const uint8_
   const int64_t P = (int64_t)p.T * p.k;
   const int64_t max_tiles = (P + kBM - 1) / kBM + (P < p.E ? P : p.E) + (p.has_shared ? (p.T + kBM - 1) / kBM : 0);
   hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, p.off, p.E, p.T, p.has_shared, tile_start);
-  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 64))), dim3(256), 0, s, p, tile_start, xq, xs,
-                     hq, hs);
-  if (ev && hipEventRecord(ev[3], s) != hipSuccess) return hipErrorInvalidValue;
-  if (ev && hipEventRecord(ev[4], s) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, p, tile_start, hq, hs);
-  if (ev && hipEventRecord(ev[5], s) != hipSuccess) return hipErrorInvalidValue;
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_timed(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 64))), dim3(256), 0, s, ev ? ev[2] : nullptr,
+                   ev ? ev[3] : nullptr, p, (const int32_t*)tile_start, xq, xs, hq, hs);
+  if (e != hipSuccess) return e;
+  return launch_timed(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, ev ? ev[4] : nullptr,
+                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start, (const uint8_t*)hq, (const uint8_t*)hs);
 }
 
 }  // namespace moe

@@ -89,12 +89,6 @@ __device__ __forceinline__ bool slot_expert(const FfnParams& p, int slot, Slot* 
   return si->e >= 0;
 }
 
-// E2M1 byte pair -> two FP16 values (exact; the FP32 scale operand is 1.0)
-template <int kByte>
-__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
-}
-
 // 8 weight nibbles (one dword) against 8 FP16 activations, accumulated into c
 __device__ __forceinline__ float dot8(uint32_t w, half8_t a, float c) {
   c = __builtin_amdgcn_fdot2(fp4x2<0>(w), half2_t{a[0], a[1]}, c, false);
@@ -309,11 +303,9 @@ bool ffn_stream_supported(int H, int I) {
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = p.n_routed_slots + (p.has_shared ? 1 : 0);
   const size_t lds = (size_t)kGRB * p.H * sizeof(half_t) + kGRB * kGRows * sizeof(float) + kGRB * sizeof(int);
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0) hipLaunchKernelGGL(k_gateup_stream, dim3((unsigned)(slots * (p.I / 16))), dim3(256), lds, s, p);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  return launch_timed(k_gateup_stream, dim3((unsigned)(slots * (p.I / 16))), dim3(256), (uint32_t)lds, s, ev_before,
+                      ev_after, p);
 }
 
 hipError_t launch_down_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
@@ -322,11 +314,8 @@ hipError_t launch_down_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_b
   while ((1 << lg) < p.I / 32) ++lg;
   const int rows_wg = (256 >> lg) * kDRows;
   const int n_nb = (p.H + rows_wg - 1) / rows_wg;
-  if (ev_before && hipEventRecord(ev_before, s) != hipSuccess) return hipErrorInvalidValue;
-  if (slots > 0) hipLaunchKernelGGL(k_down_stream, dim3((unsigned)(slots * n_nb)), dim3(256), 0, s, p, lg);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_after) e = hipEventRecord(ev_after, s);
-  return e;
+  if (slots == 0) return record_idle(s, ev_before, ev_after);
+  return launch_timed(k_down_stream, dim3((unsigned)(slots * n_nb)), dim3(256), 0, s, ev_before, ev_after, p, lg);
 }
 
 }  // namespace moe

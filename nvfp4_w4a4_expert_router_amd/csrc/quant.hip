@@ -65,16 +65,14 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
 }
 
 hipError_t launch_quant_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
-                            uint8_t* scales, half_t* deq, hipStream_t s) {
+                            uint8_t* scales, half_t* deq, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t nblocks = rows * (int64_t)(cols / 16);
-  if (nblocks == 0) return hipSuccess;
+  if (nblocks == 0) return record_idle(s, e0, e1);
   const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
   const float g6 = 6.0f * gscale;
   if (dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(k_quant_act<true>, grid, block, 0, s, x, nblocks, gscale, g6, codes, scales, deq);
-  else
-    hipLaunchKernelGGL(k_quant_act<false>, grid, block, 0, s, x, nblocks, gscale, g6, codes, scales, deq);
-  return hipGetLastError();
+    return launch_timed(k_quant_act<true>, grid, block, 0, s, e0, e1, x, nblocks, gscale, g6, codes, scales, deq);
+  return launch_timed(k_quant_act<false>, grid, block, 0, s, e0, e1, x, nblocks, gscale, g6, codes, scales, deq);
 }
 
 }  // namespace moe

@@ -96,55 +96,198 @@ __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ 
   if (lane == 0) wnorm[e] = sqrtf(s);
 }
 
-// ---------------------------------------------------------------- decode: FP64 GEMV
+// ---------------------------------------------------------------- decode: FP64 logits
 // For a few tokens the router weights (E x H x 4 bytes) are streamed once and
-// every logit is summed in FP64 from exact products, so no refinement pass is
-// needed.  One wave per expert row; lane l owns elements [l*H/64, (l+1)*H/64)
-// (loaded with 128-bit loads, all issued before the arithmetic), then a
-// butterfly over the wave.
+// every logit is summed in FP64 from exact products (BF16 x FP32 fits in 53
+// bits), so the selection needs no refinement pass.  A workgroup takes two
+// experts, two waves each: lane L = 64 (wave & 1) + lane of an expert's pair
+// owns elements 2048 j + 16 L .. + 16 (two FP64 partial sums per token, all
+// loads issued before the arithmetic), then a butterfly over each wave and the
+// sum of the two waves' totals.
+//
+// Fused variant (moe_layer_forward at T <= 4): the workgroups also write the
+// A4 codes of x; then one workgroup (k_route_tokens) selects the top k of every
+// token, forms the softmax weights and the permutation, and writes the slot
+// table of the expert kernels: the routing is computed once per call, not once
+// per expert tile.  (A last-workgroup-done election inside the logits kernel
+// needs a device-scope release per workgroup, which measured slower than the
+// kernel boundary.)
 constexpr int kGemvMaxT = 8;
-constexpr int kGemvPer = 32;  // elements per lane per pass (H = 2048 is one pass)
+constexpr int kRdMaxT = 4;  // fused variant: one wave per token in the last workgroup
+constexpr int kRdMaxE = 512;
+constexpr int kRdMaxPairs = kRdMaxT * 32;
 
-__global__ __launch_bounds__(256) void k_router_gemv64(const uint16_t* __restrict__ x, const float* __restrict__ W,
-                                                      int T, int H, int E, double* __restrict__ logits) {
-  const int lane = lane_id();
-  const int waves = (int)(gridDim.x * (blockDim.x / kWave));
-  for (int e = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6); e < E; e += waves) {
-    double acc[kGemvMaxT] = {};
-    for (int h0 = lane * kGemvPer; h0 < H; h0 += kWave * kGemvPer) {
-      float4 w[kGemvPer / 4];
+struct RoutingLds {
+  double sv[kRdMaxT][kTopkScratch];  // top-k scratch, one per token wave
+  int si[kRdMaxT][kTopkScratch];
+  int e[kRdMaxPairs];  // expert of pair p = t*k + j
+  int cnt[kRdMaxE];    // pairs per expert
+  int off[kRdMaxE + 1];
+  int nzr[kRdMaxE];    // experts with pairs and a smaller id (slot of the expert)
+  unsigned int tok[kRdMaxPairs];  // slot -> tokens of its rows, one byte each
+  int slot_e[kRdMaxPairs];
+  int n_slots;
+};
+
+// The routing of all T tokens in one workgroup (wave t takes token t).
+__device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, RoutingLds& R) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int T = q.T, E = q.E, k = q.k, P = T * k;
+  for (int e = tid; e < E; e += 256) R.cnt[e] = 0;
+  for (int s = tid; s < P; s += 256) R.tok[s] = 0u;
+  if (wave < T) {
+    double v[8];
+    int id[8];
 #pragma unroll
-      for (int i = 0; i < kGemvPer / 4; ++i) w[i] = *reinterpret_cast<const float4*>(W + (int64_t)e * H + h0 + 4 * i);
-#pragma unroll
-      for (int t = 0; t < kGemvMaxT; ++t) {
-        if (t >= T) break;
-        uint4 xv[kGemvPer / 8];
-#pragma unroll
-        for (int i = 0; i < kGemvPer / 8; ++i) xv[i] = *reinterpret_cast<const uint4*>(x + (int64_t)t * H + h0 + 8 * i);
-        double a = acc[t];
-#pragma unroll
-        for (int i = 0; i < kGemvPer / 8; ++i) {
-          const uint32_t q[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-          const float4 w0 = w[2 * i], w1 = w[2 * i + 1];
-          const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a = fma((double)__uint_as_float(q[j] << 16), (double)wf[2 * j], a);
-            a = fma((double)__uint_as_float(q[j] & 0xFFFF0000u), (double)wf[2 * j + 1], a);
-          }
-        }
-        acc[t] = a;
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + kWave * j;
+      v[j] = e < E ? q.logits[(int64_t)wave * E + e] : -INFINITY;
+      id[j] = e < E ? e : 0x7FFFFFFF;
     }
-#pragma unroll
-    for (int t = 0; t < kGemvMaxT; ++t) {
-      if (t >= T) break;
-      double a = acc[t];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m);
-      if (lane == 0) logits[(int64_t)t * E + e] = a;
+    double my_v = 0.0;
+    int my_e = 0;
+    wave_topk512(v, id, k, R.sv[wave], R.si[wave], &my_v, &my_e);
+    const float wk = topk_softmax_weight(my_v, k);
+    if (lane < k) {
+      R.e[wave * k + lane] = my_e;
+      q.idx[wave * k + lane] = my_e;
+      q.w[wave * k + lane] = wk;
     }
   }
+  __syncthreads();
+  for (int pi = tid; pi < P; pi += 256) atomicAdd(&R.cnt[R.e[pi]], 1);
+  __syncthreads();
+  if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
+    int c[8], nz[8], sc = 0, snz = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane * 8 + j;
+      c[j] = e < E ? R.cnt[e] : 0;
+      nz[j] = c[j] > 0;
+      sc += c[j];
+      snz += nz[j];
+    }
+    int ic = sc, inz = snz;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int a = __shfl_up(ic, d), b = __shfl_up(inz, d);
+      if (lane >= d) {
+        ic += a;
+        inz += b;
+      }
+    }
+    int rc = ic - sc, rnz = inz - snz;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane * 8 + j;
+      if (e < E) {
+        R.off[e] = rc;
+        R.nzr[e] = rnz;
+      }
+      rc += c[j];
+      rnz += nz[j];
+    }
+    if (lane == 63) {
+      R.off[E] = ic;
+      R.n_slots = inz;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 256) q.off[e] = R.off[e];
+  for (int pi = tid; pi < P; pi += 256) {
+    const int t = pi / k, ep = R.e[pi];
+    int before = 0;  // earlier tokens that chose the same expert (rows in token order)
+    for (int p2 = 0; p2 < t * k; ++p2) before += R.e[p2] == ep;
+    const int row = R.off[ep] + before;
+    q.p2r[pi] = row;
+    q.r2p[row] = pi;
+    const int s = R.nzr[ep];
+    atomicOr(&R.tok[s], (unsigned)t << (8 * before));
+    if (before == 0) R.slot_e[s] = ep;
+  }
+  __syncthreads();
+  for (int s = tid; s < P; s += 256) {
+    int4 ent = make_int4(-1, 0, 0, 0);
+    if (s < R.n_slots) {
+      const int ep = R.slot_e[s];
+      ent = make_int4(ep, R.off[ep], R.cnt[ep], (int)R.tok[s]);
+    }
+    q.slot_tab[s] = ent;
+  }
+}
+
+template <bool kFused>
+__global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
+  __shared__ double part[2][kGemvMaxT][2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int T = q.T, H = q.H, E = q.E;
+  // 1. A4 codes of x (fused): the T*H/16 blocks over the grid's threads
+  if (kFused) {
+    const int64_t nb = (int64_t)T * (H / 16);
+    for (int64_t b = (int64_t)blockIdx.x * 256 + tid; b < nb; b += (int64_t)gridDim.x * 256) {
+      const uint4* src = reinterpret_cast<const uint4*>(q.x + b * 16);
+      const uint4 a0 = src[0], a1 = src[1];
+      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(wv[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+      uint2 pk;
+      const uint32_t sc = encode_a4_block16(v, q.g_in, 6.0f * q.g_in, &pk);
+      reinterpret_cast<uint2*>(q.xq)[b] = pk;
+      q.xs[b] = (uint8_t)sc;
+    }
+  }
+  // 2. logits of expert e
+  const int e = 2 * blockIdx.x + (wave >> 1);
+  const int L = kWave * (wave & 1) + lane;
+  double acc[kGemvMaxT][2] = {};
+  if (e < E) {
+    for (int h0 = 16 * L; h0 < H; h0 += 2048) {
+      float4 wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const float4*>(q.W + (int64_t)e * H + h0 + 4 * i);
+      uint4 xv[kGemvMaxT][2];
+#pragma unroll
+      for (int t = 0; t < kGemvMaxT; ++t)
+        if (t < T)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) xv[t][i] = *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + h0 + 8 * i);
+      const float wf[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                            wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
+#pragma unroll
+      for (int t = 0; t < kGemvMaxT; ++t) {
+        if (t < T) {
+          const uint32_t xw[8] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
+                                  xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            acc[t][0] = fma((double)__uint_as_float(xw[i] << 16), (double)wf[2 * i], acc[t][0]);
+            acc[t][1] = fma((double)__uint_as_float(xw[i] & 0xFFFF0000u), (double)wf[2 * i + 1], acc[t][1]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kGemvMaxT; ++t) {
+    if (t < T) {
+      double a = acc[t][0] + acc[t][1];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m);
+      if (lane == 0) part[wave >> 1][t][wave & 1] = a;
+    }
+  }
+  __syncthreads();
+  if ((wave & 1) == 0 && lane < T && e < E)
+    q.logits[(int64_t)lane * E + e] = part[wave >> 1][lane][0] + part[wave >> 1][lane][1];
+}
+
+__global__ __launch_bounds__(256) void k_route_tokens(RouteDecodeParams q) {
+  __shared__ RoutingLds R;
+  route_tokens(q, R);
 }
 
 // ---------------------------------------------------------------- pass B: selection
@@ -367,10 +510,16 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_router_logits64(const uint16_t* x, const float* W, int64_t T, int H, int E, double* logits,
-                                  hipStream_t s) {
-  hipLaunchKernelGGL(k_router_gemv64, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, s, x, W, (int)T, H, E, logits);
-  return hipGetLastError();
+bool route_decode_supported(int H, int E, int k, int64_t T) {
+  return T >= 1 && T <= kRdMaxT && E <= kRdMaxE && k <= 32 && H % 32 == 0;
+}
+
+// two kernels: the event pair spans the start of the first and the end of the second
+hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+  const hipError_t e =
+      launch_timed(k_route_decode<true>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before, nullptr, q);
+  if (e != hipSuccess) return e;
+  return launch_timed(k_route_tokens, dim3(1), dim3(256), 0, s, nullptr, ev_after, q);
 }
 
 static float gamma_for_depth(int d) {
@@ -400,10 +549,16 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
     p.l32 = logits_in;
     p.mode = kSelF32;
   } else if (T <= kGemvMaxT) {
-    double* lg = static_cast<double*>(ws);
-    const int blocks = (E + 3) / 4;
-    hipLaunchKernelGGL(k_router_gemv64, dim3(blocks), dim3(256), 0, s, x, W, (int)T, H, E, lg);
-    p.l64 = lg;
+    RouteDecodeParams q = {};
+    q.x = x;
+    q.W = W;
+    q.T = (int)T;
+    q.H = H;
+    q.E = E;
+    q.k = k;
+    q.logits = static_cast<double*>(ws);
+    hipLaunchKernelGGL(k_route_decode<false>, dim3((unsigned)((E + 1) / 2)), dim3(256), 0, s, q);
+    p.l64 = q.logits;
     p.mode = kSelF64;
   } else {
     float* lg = static_cast<float*>(ws);

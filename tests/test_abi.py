@@ -123,3 +123,15 @@ def test_workspace_monotone_in_T():
 def test_bad_dtype_and_cols():
     assert moe.lib.moe_quantize_act(FAKE, 7, 4, 64, 1.0, FAKE, FAKE, None) == moe.MOE_EINVAL
     assert moe.lib.moe_quantize_act(FAKE, 0, 4, 60, 1.0, FAKE, FAKE, None) == moe.MOE_ESHAPE
+
+
+def test_null_event_entry_is_rejected():
+    L = layer()
+    arr = (ctypes.c_void_p * (2 * moe.FFN_KERNELS))(*([FAKE] * (2 * moe.FFN_KERNELS - 1) + [None]))
+    dbg = moe.Debug(None, None, None, None, None, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, ctypes.byref(dbg), FAKE, 1 << 30,
+                                None)
+    assert rc == moe.MOE_EINVAL
+    rc = moe.lib.moe_layer_forward(ctypes.byref(L), FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   ctypes.byref(dbg), FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL

@@ -266,3 +266,19 @@ def test_layer_forward_matches_separate_calls(cfg, T):
         assert np.array_equal(a, b), key
     rep = gh.check_layer(L, x, dict(ref, **gh.run_layer(DL, x, residual=res)), residual=res)
     gh.log("  ", rep.line())
+
+
+@pytest.mark.parametrize("cfg,T", [(1, 4), (0, 3)])
+def test_fused_path_repeated_calls(cfg, T):
+    """Several fused calls on one workspace and one set of outputs: every call
+    routes its own batch and matches the four separate calls on that batch."""
+    gh.log("case: fused workspace reuse config %d T=%d" % (cfg, T))
+    L, DL = layer_for(cfg)
+    buf = moe.Buffers(DL, T, gh.DEV)
+    for step in (21, 22, 23):
+        x = gen.make_tokens(cfg, T, step=step)
+        ref = gh.run_layer(DL, x, dump=())
+        moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.topk_idx.cpu().numpy(), ref["idx"])
+        assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), ref["out"])
