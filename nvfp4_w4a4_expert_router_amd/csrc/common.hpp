@@ -155,130 +155,136 @@ __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint3
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-// Wave-wide max / min through DPP moves (no LDS round trips).  The sequence
-// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror,
-// row_bcast:15 (rows 1, 3), row_bcast:31 (rows 2, 3) leaves the wave result in
-// lane 63, which is then broadcast.  Exact (no arithmetic).
-template <int kCtrl, int kRowMask>
+// Wave-wide reductions and scans through DPP moves (no LDS round trips).
+// Sum: quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror
+// give 16-lane row sums in every lane; row_bcast:15 into rows 1 and 3, then
+// row_bcast:31 into rows 2 and 3, leave the wave total in lane 63 (disabled
+// rows add 0).  The order of the additions is fixed: deterministic.
+template <int kCtrl, int kRowMask, bool kZeroOld>
 __device__ __forceinline__ int dpp_mov(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, kCtrl, kRowMask, 0xF, false);
+  return __builtin_amdgcn_update_dpp(kZeroOld ? 0 : v, v, kCtrl, kRowMask, 0xF, true);
 }
 
-template <int kCtrl, int kRowMask>
+template <int kCtrl, int kRowMask, bool kZeroOld>
 __device__ __forceinline__ double dpp_mov_f64(double v) {
   const unsigned long long u = __double_as_longlong(v);
-  const int lo = dpp_mov<kCtrl, kRowMask>((int)(u & 0xFFFFFFFFull));
-  const int hi = dpp_mov<kCtrl, kRowMask>((int)(u >> 32));
+  const int lo = dpp_mov<kCtrl, kRowMask, kZeroOld>((int)(u & 0xFFFFFFFFull));
+  const int hi = dpp_mov<kCtrl, kRowMask, kZeroOld>((int)(u >> 32));
   return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-__device__ __forceinline__ double wave_max_f64(double v) {
-  v = fmax(v, dpp_mov_f64<0xB1, 0xF>(v));
-  v = fmax(v, dpp_mov_f64<0x4E, 0xF>(v));
-  v = fmax(v, dpp_mov_f64<0x141, 0xF>(v));
-  v = fmax(v, dpp_mov_f64<0x140, 0xF>(v));
-  v = fmax(v, dpp_mov_f64<0x142, 0xA>(v));
-  v = fmax(v, dpp_mov_f64<0x143, 0xC>(v));
+// FP64 sum over the wave, returned in every lane
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_mov_f64<0xB1, 0xF, false>(v);
+  v += dpp_mov_f64<0x4E, 0xF, false>(v);
+  v += dpp_mov_f64<0x141, 0xF, false>(v);
+  v += dpp_mov_f64<0x140, 0xF, false>(v);
+  v += dpp_mov_f64<0x142, 0xA, true>(v);
+  v += dpp_mov_f64<0x143, 0xC, true>(v);
   const unsigned long long u = __double_as_longlong(v);
   const unsigned lo = __builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), 63);
   const unsigned hi = __builtin_amdgcn_readlane((int)(u >> 32), 63);
   return __longlong_as_double(((unsigned long long)hi << 32) | lo);
 }
 
-__device__ __forceinline__ int wave_min_i32(int v) {
-  v = min(v, dpp_mov<0xB1, 0xF>(v));
-  v = min(v, dpp_mov<0x4E, 0xF>(v));
-  v = min(v, dpp_mov<0x141, 0xF>(v));
-  v = min(v, dpp_mov<0x140, 0xF>(v));
-  v = min(v, dpp_mov<0x142, 0xA>(v));
-  v = min(v, dpp_mov<0x143, 0xC>(v));
-  return __builtin_amdgcn_readlane(v, 63);
+// Inclusive prefix sum over the wave: row_shr:1, 2, 4, 8 within 16-lane rows
+// (lanes without a source add 0), then the row totals through row_bcast:15 and
+// row_bcast:31.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += dpp_mov<0x111, 0xF, true>(v);
+  v += dpp_mov<0x112, 0xF, true>(v);
+  v += dpp_mov<0x114, 0xF, true>(v);
+  v += dpp_mov<0x118, 0xF, true>(v);
+  v += dpp_mov<0x142, 0xA, true>(v);
+  v += dpp_mov<0x143, 0xC, true>(v);
+  return v;
 }
 
 // Top k (k <= 32) of up to 512 values held 8 per lane (value v[j], id[j];
 // unused entries -inf / 0x7FFFFFFF), ordered by (value descending, id
-// ascending).  Each lane sorts its 8 entries (Batcher's network, 19 compare-
-// exchanges); tau = the k-th best of the 64 lane heads.  The k best heads are
-// all at least tau, so every entry of the true top k is at least tau: only the
-// entries >= tau (a prefix of each sorted lane, ~k in total) are ranked against
-// each other.  Lane r < k receives the r-th entry.  scratch_v / scratch_i: LDS of
-// kTopkScratch entries for this wave (512 candidates + 32 results).
+// ascending).  tau = the k-th best of the 64 lane heads (the best entry of each
+// lane).  The k best heads are all at least tau, so every entry of the true
+// top k is at least tau: only the entries >= tau (~k in total) are ranked
+// against each other.  Lane r < k receives the r-th entry.  The heads and the
+// candidates go through LDS and every lane compares against all of them with
+// broadcast reads, 16 in flight (a single wave has no other wave to hide
+// latency behind).  scratch_v / scratch_i: LDS of kTopkScratch entries for
+// this wave.
 constexpr int kTopkScratch = 512 + 32;
 
+// (va, ia) ranks before (vb, ib); evaluated without short circuit (no branch)
 __device__ __forceinline__ bool ahead(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
-__device__ __forceinline__ void cas_desc(double& va, int& ia, double& vb, int& ib) {
-  const bool sw = ahead(vb, ib, va, ia);
-  const double tv = sw ? vb : va;
-  const int ti = sw ? ib : ia;
-  vb = sw ? va : vb;
-  ib = sw ? ia : ib;
-  va = tv;
-  ia = ti;
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), l);
+  const unsigned hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+  return __longlong_as_double(((unsigned long long)hi << 32) | lo);
 }
 
 __device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k, double* scratch_v, int* scratch_i,
                                              double* out_v, int* out_id) {
   const int lane = (int)(threadIdx.x & 63);
-#define MOE_CAS(a, b) cas_desc(v[a], id[a], v[b], id[b])
-  MOE_CAS(0, 1); MOE_CAS(2, 3); MOE_CAS(4, 5); MOE_CAS(6, 7);
-  MOE_CAS(0, 2); MOE_CAS(1, 3); MOE_CAS(4, 6); MOE_CAS(5, 7);
-  MOE_CAS(1, 2); MOE_CAS(5, 6);
-  MOE_CAS(0, 4); MOE_CAS(1, 5); MOE_CAS(2, 6); MOE_CAS(3, 7);
-  MOE_CAS(2, 4); MOE_CAS(3, 5);
-  MOE_CAS(1, 2); MOE_CAS(3, 4); MOE_CAS(5, 6);
-#undef MOE_CAS
+  // this lane's head
+  double hv = v[0];
+  int hi = id[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    const bool b = ahead(v[j], id[j], hv, hi);
+    hv = b ? v[j] : hv;
+    hi = b ? id[j] : hi;
+  }
   // rank of this lane's head among the 64 heads
-  scratch_v[lane] = v[0];
-  scratch_i[lane] = id[0];
+  scratch_v[lane] = hv;
+  scratch_i[lane] = hi;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int hr = 0;
-#pragma unroll 8
-  for (int q = 0; q < kWave; ++q) hr += ahead(scratch_v[q], scratch_i[q], v[0], id[0]);
+#pragma unroll 16
+  for (int q = 0; q < 64; ++q) hr += ahead(scratch_v[q], scratch_i[q], hv, hi);
   const uint64_t at = __ballot(hr == k - 1);
   const int L = __ffsll((long long)at) - 1;
-  const unsigned long long hu = __double_as_longlong(v[0]);
-  const double tau = __longlong_as_double(
-      ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(hu >> 32), L) << 32) |
-      (unsigned)__builtin_amdgcn_readlane((int)(hu & 0xFFFFFFFFull), L));
-  const int tau_id = __builtin_amdgcn_readlane(id[0], L);
-  // candidates: the prefix of each sorted lane that is not behind tau
+  const double tau = readlane_f64(hv, L);
+  const int tau_id = __builtin_amdgcn_readlane(hi, L);
+  // candidates: the entries not behind tau, compacted in lane order
+  bool cand[8];
   int m = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m += !ahead(tau, tau_id, v[j], id[j]);
-  int incl = m;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(incl, d);
-    if (lane >= d) incl += t;
+  for (int j = 0; j < 8; ++j) {
+    cand[j] = !ahead(tau, tau_id, v[j], id[j]);
+    m += cand[j];
   }
+  const int incl = wave_incl_scan_i32(m);
   const int nc = __builtin_amdgcn_readlane(incl, 63);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  int pos = incl - m;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the heads are read
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (j < m) {
-      scratch_v[incl - m + j] = v[j];
-      scratch_i[incl - m + j] = id[j];
+    if (cand[j]) {
+      scratch_v[pos] = v[j];
+      scratch_i[pos] = id[j];
+      ++pos;
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // rank every candidate among the candidates; rank r < k goes to lane r
+  // rank every candidate among the candidates (blocks of 64 held in lanes);
+  // rank r < k goes to result slot r
   for (int c0 = 0; c0 < nc; c0 += kWave) {
     const int c = c0 + lane;
-    double cv = -INFINITY;
-    int ci = 0x7FFFFFFF, r = 0;
-    if (c < nc) {
-      cv = scratch_v[c];
-      ci = scratch_i[c];
-      for (int q = 0; q < nc; ++q) r += ahead(scratch_v[q], scratch_i[q], cv, ci);
-    }
+    const double cv = c < nc ? scratch_v[c] : -INFINITY;
+    const int ci = c < nc ? scratch_i[c] : 0x7FFFFFFF;
+    int r = 0;
+    int q = 0;
+    for (; q + 16 <= nc; q += 16)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) r += ahead(scratch_v[q + u], scratch_i[q + u], cv, ci);
+    for (; q < nc; ++q) r += ahead(scratch_v[q], scratch_i[q], cv, ci);
     if (c < nc && r < k) {  // results after the 512 candidate slots
       scratch_v[512 + r] = cv;
       scratch_i[512 + r] = ci;
@@ -293,8 +299,6 @@ __device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k
   }
 }
 
-// Softmax weights of the k selected logits in rank order (lane r holds the
-// r-th logit): exp(l_r - l_0) / sum_j exp(l_j - l_0), the sum taken j = 0..k-1.
 __device__ __forceinline__ float topk_softmax_weight(double my_v, int k) {
   const int lane = (int)(threadIdx.x & 63);
   const unsigned long long u = __double_as_longlong(my_v);
@@ -302,9 +306,7 @@ __device__ __forceinline__ float topk_softmax_weight(double my_v, int k) {
       ((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(u >> 32), 0) << 32) |
       (unsigned)__builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), 0));
   const double ex = lane < k ? exp(my_v - top) : 0.0;
-  double total = 0.0;
-  for (int j = 0; j < k; ++j) total += __shfl(ex, j);
-  return (float)(ex / total);
+  return (float)(ex / wave_sum_f64(ex));
 }
 
 // The s-th expert (0-based, ascending id) with a nonzero count in off[0..E].

@@ -115,26 +115,25 @@ __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ 
 constexpr int kGemvMaxT = 8;
 constexpr int kRdMaxT = 4;  // fused variant: one wave per token in the last workgroup
 constexpr int kRdMaxE = 512;
-constexpr int kRdMaxPairs = kRdMaxT * 32;
 
 struct RoutingLds {
   double sv[kRdMaxT][kTopkScratch];  // top-k scratch, one per token wave
   int si[kRdMaxT][kTopkScratch];
-  int e[kRdMaxPairs];  // expert of pair p = t*k + j
-  int cnt[kRdMaxE];    // pairs per expert
+  unsigned int tmask[kRdMaxE];  // tokens that chose expert e (bit t)
   int off[kRdMaxE + 1];
-  int nzr[kRdMaxE];    // experts with pairs and a smaller id (slot of the expert)
-  unsigned int tok[kRdMaxPairs];  // slot -> tokens of its rows, one byte each
-  int slot_e[kRdMaxPairs];
+  int nzr[kRdMaxE];  // experts with pairs and a smaller id (slot of the expert)
   int n_slots;
 };
 
-// The routing of all T tokens in one workgroup (wave t takes token t).
+// The routing of all T tokens in one workgroup (wave t takes token t).  Rows
+// of an expert are in token order, so a pair's row is the expert's offset
+// plus the number of earlier tokens in the expert's token mask.
 __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, RoutingLds& R) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = q.T, E = q.E, k = q.k, P = T * k;
-  for (int e = tid; e < E; e += 256) R.cnt[e] = 0;
-  for (int s = tid; s < P; s += 256) R.tok[s] = 0u;
+  for (int e = tid; e < E; e += 256) R.tmask[e] = 0u;
+  __syncthreads();
+  int my_e = 0;
   if (wave < T) {
     double v[8];
     int id[8];
@@ -145,37 +144,25 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
       id[j] = e < E ? e : 0x7FFFFFFF;
     }
     double my_v = 0.0;
-    int my_e = 0;
     wave_topk512(v, id, k, R.sv[wave], R.si[wave], &my_v, &my_e);
     const float wk = topk_softmax_weight(my_v, k);
     if (lane < k) {
-      R.e[wave * k + lane] = my_e;
+      atomicOr(&R.tmask[my_e], 1u << wave);
       q.idx[wave * k + lane] = my_e;
       q.w[wave * k + lane] = wk;
     }
   }
   __syncthreads();
-  for (int pi = tid; pi < P; pi += 256) atomicAdd(&R.cnt[R.e[pi]], 1);
-  __syncthreads();
   if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
-    int c[8], nz[8], sc = 0, snz = 0;
+    int c[8], sc = 0, snz = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = lane * 8 + j;
-      c[j] = e < E ? R.cnt[e] : 0;
-      nz[j] = c[j] > 0;
+      c[j] = e < E ? __popc(R.tmask[e]) : 0;
       sc += c[j];
-      snz += nz[j];
+      snz += c[j] > 0;
     }
-    int ic = sc, inz = snz;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int a = __shfl_up(ic, d), b = __shfl_up(inz, d);
-      if (lane >= d) {
-        ic += a;
-        inz += b;
-      }
-    }
+    const int ic = wave_incl_scan_i32(sc), inz = wave_incl_scan_i32(snz);
     int rc = ic - sc, rnz = inz - snz;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -183,9 +170,17 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
       if (e < E) {
         R.off[e] = rc;
         R.nzr[e] = rnz;
+        if (c[j] > 0) {  // slot entry: expert, first row, rows, tokens (one byte each, ascending)
+          unsigned int tm = R.tmask[e], toks = 0u;
+          for (int r = 0; r < c[j]; ++r) {
+            toks |= (unsigned)(__ffs(tm) - 1) << (8 * r);
+            tm &= tm - 1u;
+          }
+          q.slot_tab[rnz] = make_int4(e, rc, c[j], (int)toks);
+        }
       }
       rc += c[j];
-      rnz += nz[j];
+      rnz += c[j] > 0;
     }
     if (lane == 63) {
       R.off[E] = ic;
@@ -194,25 +189,12 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
   }
   __syncthreads();
   for (int e = tid; e <= E; e += 256) q.off[e] = R.off[e];
-  for (int pi = tid; pi < P; pi += 256) {
-    const int t = pi / k, ep = R.e[pi];
-    int before = 0;  // earlier tokens that chose the same expert (rows in token order)
-    for (int p2 = 0; p2 < t * k; ++p2) before += R.e[p2] == ep;
-    const int row = R.off[ep] + before;
+  for (int s = R.n_slots + tid; s < P; s += 256) q.slot_tab[s] = make_int4(-1, 0, 0, 0);
+  if (wave < T && lane < k) {
+    const int pi = wave * k + lane;
+    const int row = R.off[my_e] + __popc(R.tmask[my_e] & ((1u << wave) - 1u));
     q.p2r[pi] = row;
     q.r2p[row] = pi;
-    const int s = R.nzr[ep];
-    atomicOr(&R.tok[s], (unsigned)t << (8 * before));
-    if (before == 0) R.slot_e[s] = ep;
-  }
-  __syncthreads();
-  for (int s = tid; s < P; s += 256) {
-    int4 ent = make_int4(-1, 0, 0, 0);
-    if (s < R.n_slots) {
-      const int ep = R.slot_e[s];
-      ent = make_int4(ep, R.off[ep], R.cnt[ep], (int)R.tok[s]);
-    }
-    q.slot_tab[s] = ent;
   }
 }
 
@@ -274,9 +256,7 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
 #pragma unroll
   for (int t = 0; t < kGemvMaxT; ++t) {
     if (t < T) {
-      double a = acc[t][0] + acc[t][1];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m);
+      const double a = wave_sum_f64(acc[t][0] + acc[t][1]);
       if (lane == 0) part[wave >> 1][t][wave & 1] = a;
     }
   }
