@@ -13,18 +13,21 @@
  * counter-based generator.  Output i of stream `key` is the SplitMix64
  * finaliser applied to key + (i+1)*0x9E3779B97F4A7C15, i.e. the (i+1)-th
  * output of a SplitMix64 seeded with `key`.  Uniforms take the top 53 bits;
- * normals come from the Box-Muller transform on the pair (2j, 2j+1): element
- * 2j is the cosine branch and element 2j+1 the sine branch.  Every element is
- * a pure function of (key, index), so the result does not depend on the
- * number of OpenMP threads.
+ * normals of the hidden states and router rows come from the Box-Muller
+ * transform on the pair (2j, 2j+1): element 2j is the cosine branch and
+ * element 2j+1 the sine branch.  Expert weights (billions of draws per layer)
+ * use the ziggurat method of Marsaglia and Tsang (2000, 128 strips): normal n
+ * of stream `key` reads its own counter stream seeded by output n of `key`,
+ * so rejections never shift other elements.  Every element is a pure function
+ * of (key, index): the result does not depend on the number of threads.
  *
  * Weight encoding (the synthetic checkpoint): per expert and per packed
  * tensor, G = fl32(amax / (6*448)); per 16-element block the UE4M3 scale code
  * nearest to amax_block / (6*G) (ties to the even code, saturating at 448);
- * each element the E2M1 code nearest to w / (scale*G) (ties to the even code,
- * saturating at 6, sign = sign of w).  "Nearest" is taken on the FP64
- * quotient by scanning the whole grid, which is slow but leaves nothing to
- * interpret.
+ * each element the E2M1 code nearest to |w| / (scale*G) (ties to the even
+ * code, saturating at 6, sign = sign of w).  "Nearest" is decided on the
+ * exact quotient: |w| is compared with the grid midpoints times scale*G,
+ * products that are exact in FP64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,13 +57,56 @@ double gen_normal_at(uint64_t key, uint64_t j) {
   return (j & 1) ? r * sin(a) : r * cos(a);
 }
 
-/* normals 2p and 2p+1 of the stream at once (the same values as gen_normal_at) */
-static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
-  double u1 = u01(key, 2 * p), u2 = u01(key, 2 * p + 1);
-  double r = sqrt(-2.0 * log(u1));
-  double a = 6.283185307179586476925286766559 * u2;
-  *z0 = r * cos(a);
-  *z1 = r * sin(a);
+/* ---- ziggurat normals (Marsaglia and Tsang, 2000) ----
+ * 128 strips of equal area V under f(x) = exp(-x^2/2): strip 0 is the base
+ * rectangle of width V/f(R) (its part beyond R is the tail), strip i >= 1 the
+ * rectangle between heights f(zx[i]) and f(zx[i+1]) with zx[1] = R,
+ * zx[i+1] = f^-1(f(zx[i]) + V/zx[i]) and zx[128] = 0.  A draw picks a strip
+ * and a point z = U * zx[i]; inside the strip's inner rectangle (z <
+ * zx[i+1]) it is accepted at once, otherwise the wedge (or, for strip 0, the
+ * tail beyond R) is sampled exactly, and a rejection starts over. */
+#define ZIG_R 3.442619855899
+#define ZIG_V 9.91256303526217e-3
+static double zx[129], zf[129];
+static int zig_ready = 0;
+
+static void build_ziggurat(void) {
+  if (zig_ready) return;
+  zx[0] = ZIG_V / exp(-0.5 * ZIG_R * ZIG_R);
+  zx[1] = ZIG_R;
+  for (int i = 1; i < 127; ++i) zx[i + 1] = sqrt(-2.0 * log(exp(-0.5 * zx[i] * zx[i]) + ZIG_V / zx[i]));
+  zx[128] = 0.0;
+  for (int i = 0; i <= 128; ++i) zf[i] = exp(-0.5 * zx[i] * zx[i]);
+  zig_ready = 1;
+}
+
+/* uniform in (0, 1) from 53 bits */
+static inline double u53(uint64_t r) { return ((double)(r >> 11) + 0.5) * (1.0 / 9007199254740992.0); }
+
+static double zig_normal(uint64_t key, uint64_t n) {
+  const uint64_t sub = sm_mix(key + (n + 1) * GOLDEN); /* seed of this element's own stream */
+  uint64_t r = sub, j = 0;
+  for (;;) {
+    const int i = (int)(r & 127u);
+    const double sgn = (r & 128u) ? -1.0 : 1.0;
+    const double z = u53(r) * zx[i];
+    if (z < zx[i + 1]) return sgn * z;
+    if (i == 0) { /* tail beyond R */
+      for (;;) {
+        const double a = -log(u53(gen_splitmix64(sub, j++))) / ZIG_R;
+        const double b = -log(u53(gen_splitmix64(sub, j++)));
+        if (b + b > a * a) return sgn * (ZIG_R + a);
+      }
+    }
+    const double y = zf[i] + u53(gen_splitmix64(sub, j++)) * (zf[i + 1] - zf[i]);
+    if (y < exp(-0.5 * z * z)) return sgn * z;
+    r = gen_splitmix64(sub, j++);
+  }
+}
+
+double gen_ziggurat_at(uint64_t key, uint64_t n) {
+  build_ziggurat();
+  return zig_normal(key, n);
 }
 
 /* IEEE round-to-nearest-even FP32 -> BF16 (finite inputs) */
@@ -104,20 +150,25 @@ static void build_grids(void) {
   grids_ready = 1;
 }
 
-/* nearest grid point, ties to the even code; v >= 0; grid strictly ascending.
- * The distance to the grid is unimodal, so the nearest point is one of the two
- * neighbours of v, found by bisection. */
-static int nearest_code(const double* grid, int n, double v) {
-  if (v >= grid[n - 1]) return n - 1;
-  int lo = 0, hi = n - 1; /* grid[lo] <= v < grid[hi] */
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (grid[mid] <= v) lo = mid; else hi = mid;
+/* UE4M3 code nearest to amax / g6 (ties to the even code, saturating at 448),
+ * decided on the exact quotient: amax is compared with g6 times the midpoints
+ * of the grid (each midpoint has <= 5 significant bits, g6 = 6 * fl32 value:
+ * the products are exact in FP64). */
+static int scale_code_exact(double amax, double g6) {
+  int lo = 0, hi = 126; /* answer: number of midpoints below amax, in [lo, hi] */
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (0.5 * (ue4m3_val[mid] + ue4m3_val[mid + 1]) * g6 < amax) lo = mid + 1; else hi = mid;
   }
-  double dl = v - grid[lo], dh = grid[hi] - v;
-  if (dl < dh) return lo;
-  if (dh < dl) return hi;
-  return (lo & 1) ? hi : lo;
+  if (lo < 126 && 0.5 * (ue4m3_val[lo] + ue4m3_val[lo + 1]) * g6 == amax && ((lo + 1) & 1) == 0) lo += 1;
+  return lo;
+}
+
+/* E2M1 magnitude code nearest to a / s (a >= 0, s > 0), ties to the even
+ * code, saturating at 6: a against the midpoints times s (exact products). */
+static inline int elem_mag_exact(double a, double s) {
+  return (a > 0.25 * s) + (a >= 0.75 * s) + (a > 1.25 * s) + (a >= 1.75 * s) + (a > 2.5 * s) + (a >= 3.5 * s) +
+         (a > 5.0 * s);
 }
 
 /*
@@ -131,6 +182,7 @@ int gen_nvfp4_bank(uint64_t key, double sigma, int64_t n_exp, int64_t N, int64_t
                    uint8_t* scales, float* gscale) {
   if (K % 16 != 0) return -1;
   build_grids();
+  build_ziggurat();
   int bad = 0;
 #pragma omp parallel
   {
@@ -145,33 +197,30 @@ int gen_nvfp4_bank(uint64_t key, double sigma, int64_t n_exp, int64_t N, int64_t
       if (!w) continue;
       const int64_t base = e * N * K;
       double amax = 0.0;
-      for (int64_t i = 0; i < N * K; i += 2) { /* base and N*K are even */
-        double z0, z1;
-        normal_pair(key, (uint64_t)(base + i) >> 1, &z0, &z1);
-        w[i] = sigma * z0;
-        w[i + 1] = sigma * z1;
+      for (int64_t i = 0; i < N * K; ++i) {
+        w[i] = sigma * zig_normal(key, (uint64_t)(base + i));
         if (fabs(w[i]) > amax) amax = fabs(w[i]);
-        if (fabs(w[i + 1]) > amax) amax = fabs(w[i + 1]);
       }
-      float G = (float)(amax / (6.0 * 448.0));
+      const float G = (float)(amax / (6.0 * 448.0));
       gscale[e] = G;
+      const double g6 = 6.0 * (double)G;
       for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < K / 16; ++b) {
           const double* wb = w + n * K + b * 16;
           double bmax = 0.0;
           for (int j = 0; j < 16; ++j)
             if (fabs(wb[j]) > bmax) bmax = fabs(wb[j]);
-          int sc = G > 0.0f ? nearest_code(ue4m3_val, 127, bmax / (6.0 * (double)G)) : 0;
+          const int sc = G > 0.0f ? scale_code_exact(bmax, g6) : 0;
           scales[(e * N + n) * (K / 16) + b] = (uint8_t)sc;
-          double s = ue4m3_val[sc] * (double)G;
+          const double sv = ue4m3_val[sc] * (double)G;
+          uint8_t* dst = codes + (e * N + n) * (K / 2) + b * 8;
           for (int j = 0; j < 16; j += 2) {
-            uint8_t nib[2];
+            int nib[2];
             for (int h = 0; h < 2; ++h) {
-              double v = wb[j + h];
-              int mag = s > 0.0 ? nearest_code(e2m1_mag, 8, fabs(v) / s) : 0;
-              nib[h] = (uint8_t)(mag | (signbit(v) ? 8 : 0));
+              const double v = wb[j + h];
+              nib[h] = (sv > 0.0 ? elem_mag_exact(fabs(v), sv) : 0) | (signbit(v) ? 8 : 0);
             }
-            codes[(e * N + n) * (K / 2) + (b * 16 + j) / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+            dst[j / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
           }
         }
       }
