@@ -183,6 +183,15 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
                       float* y_rows, float* y_shared, uint16_t* out, const moe_debug* dbg, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/* Parameter-free RMS norm of BF16 rows, the composition that chains layers
+ * into a stack (the pages run 48 MoE layers, Richland article, "What
+ * shipped"; the block structure around them is not printed):
+ *   out[t][h] = RNE_BF16( x[t][h] / sqrt(mean_h x[t][h]^2 + eps) )
+ * with the sum of squares, the scale and the product in FP64.
+ *   x, out [T][H] BF16 device (16-byte aligned); 0 <= eps <= 1.
+ * Errors: MOE_ESHAPE (T < 0, H <= 0), MOE_EINVAL (pointers, eps).            */
+int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* out, hipStream_t stream);
+
 /* A4 encoding of a row-major [rows][cols] matrix (cols % 16 == 0):
  *   dtype MOE_DTYPE_BF16 (x is uint16 BF16 patterns) or MOE_DTYPE_F32
  *   gscale: power-of-two global scale (host)

@@ -64,14 +64,16 @@ def _load():
     L.moe_quantize_act.argtypes = [vp, ci, i64, ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     L.moe_layer_forward.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz,
                                     vp]
-    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward"):
+    L.moe_rms_norm.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_double, vp, vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
+              "moe_rms_norm"):
         getattr(L, f).restype = ci
     return L
 
 
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_quantize_act", "moe_layer_forward")
+           "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm")
 
 
 def strerror(code: int) -> str:
@@ -173,6 +175,12 @@ def moe_quantize_act(x, codes, scales, gscale=1.0, stream=None):
     rows, cols = x.shape
     _check(lib.moe_quantize_act(_ptr(x), dtype, rows, cols, gscale, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_act")
+
+
+def moe_rms_norm(x, out, eps=1e-6, stream=None):
+    """out = RNE_BF16(x / sqrt(mean(x^2) + eps)) row by row ([T][H] BF16 as int16)."""
+    T, H = x.shape
+    _check(lib.moe_rms_norm(_ptr(x), T, H, float(eps), _ptr(out), _stream(stream)), "moe_rms_norm")
 
 
 class Buffers:

@@ -333,6 +333,14 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   return launch_rc(launch_combine(T, L->H, L->k, y_rows, p.y_shared, pair2row, topk_w, residual, out, stream));
 }
 
+int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* out, hipStream_t stream) {
+  if (T < 0 || H <= 0) return MOE_ESHAPE;
+  if (!(eps >= 0.0) || eps > 1.0) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(x) || !ptr_ok(out)) return MOE_EINVAL;
+  return launch_rc(launch_rms_norm(x, T, H, eps, out, stream));
+}
+
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
                      uint8_t* scales, hipStream_t stream) {
   if (rows < 0 || cols <= 0 || cols % 16) return MOE_ESHAPE;

@@ -58,6 +58,7 @@ def lib():
         L.orc_expert_rows.argtypes = [i64, vp, vp, vp, vp, dbl, vp, vp, vp, vp, vp, vp, i64, i64, dbl, i64, i64,
                                       vp, vp, vp, vp, vp, vp, vp, vp]
         L.orc_combine.argtypes = [i64, ci, i64, vp, vp, vp, vp, vp, vp]
+        L.orc_rms_norm.argtypes = [vp, i64, i64, dbl, vp]
         _lib = L
     return _lib
 
@@ -193,6 +194,16 @@ def combine(y, w, ysh=None, residual=None):
     o16 = np.empty((n, H), np.uint16)
     lib().orc_combine(n, k, H, _p(y), _p(w), _p(ysh), _p(residual), _p(o64), _p(o16))
     return o64, o16
+
+
+def rms_norm(x_bf16, eps=1e-6):
+    """Parameter-free RMS norm of BF16 rows, rounded to BF16 (the stack's
+    composition between MoE layers)."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    out = np.empty_like(x)
+    lib().orc_rms_norm(_p(x), T, H, float(eps), _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- whole layer

@@ -319,3 +319,29 @@ void orc_combine(int64_t n, int k, int64_t H, const double* y, const float* w, c
     }
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* Stack composition (a reading; the pages chain 48 MoE layers, Richland
+ * article "What shipped", but print no block structure): before each MoE
+ * layer the residual stream is RMS-normalised without a learned weight,
+ * n = RNE_BF16( x / sqrt(mean_h x^2 + eps) ), everything in FP64; the layer's
+ * output is added back to x in its combine.                              */
+void orc_rms_norm(const uint16_t* x, int64_t T, int64_t H, double eps, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      uint32_t u = (uint32_t)x[t * H + h] << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      ss += (double)f * (double)f;
+    }
+    const double inv = 1.0 / sqrt(ss / (double)H + eps);
+    for (int64_t h = 0; h < H; ++h) {
+      uint32_t u = (uint32_t)x[t * H + h] << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      out[t * H + h] = orc_round_bf16((double)f * inv);
+    }
+  }
+}

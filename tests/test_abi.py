@@ -135,3 +135,12 @@ def test_null_event_entry_is_rejected():
     rc = moe.lib.moe_layer_forward(ctypes.byref(L), FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    ctypes.byref(dbg), FAKE, 1 << 30, None)
     assert rc == moe.MOE_EINVAL
+
+
+def test_rms_norm_validation():
+    assert moe.lib.moe_rms_norm(FAKE, -1, 2048, 1e-6, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_rms_norm(FAKE, 4, 0, 1e-6, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_rms_norm(FAKE, 4, 2048, -1.0, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_rms_norm(FAKE, 4, 2048, float("nan"), FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_rms_norm(None, 4, 2048, 1e-6, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_rms_norm(None, 0, 2048, 1e-6, None, None) == moe.MOE_OK

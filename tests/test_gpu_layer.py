@@ -282,3 +282,15 @@ def test_fused_path_repeated_calls(cfg, T):
         torch.cuda.synchronize()
         assert np.array_equal(buf.topk_idx.cpu().numpy(), ref["idx"])
         assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), ref["out"])
+
+
+def test_rms_norm_matches_oracle():
+    """The stack's RMS norm kernel: bit-exact against the FP64 oracle (both round an
+    FP64 product once to BF16), on decode-sized and ragged batches."""
+    for T, H, step in ((4, 2048, 31), (257, 2048, 32), (8, 256, 33)):
+        x = gen.make_tokens(1, T, step=step)[:, :H].copy()
+        x[0] = oracle.round_bf16(oracle.bf16_to_f64(x[0]) * 37.0)
+        out = torch.empty((T, H), dtype=torch.int16, device=gh.DEV)
+        moe.moe_rms_norm(gh.to_dev(x.view(np.int16)), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.rms_norm(x)), (T, H)

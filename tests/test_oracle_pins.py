@@ -437,3 +437,25 @@ def test_packed_size_matches_host_bank():
     I = 640
     per_expert = 3 * H * I / 2 + 3 * H * I / 16
     assert round(per_expert * E * layers / 2 ** 30, 1) == facts["host_expert_bank_gib"]
+
+
+def test_rms_norm_closed_forms():
+    """The stack's RMS norm: closed forms and invariants (one nonzero element gives
+    sign * sqrt(H); a constant row gives +-1; power-of-two scaling is invisible with
+    eps = 0; the output's mean square is 1 within BF16 rounding)."""
+    H = 2048
+    x = np.zeros((3, H), np.float64)
+    x[0, 5] = -3.25
+    x[1, :] = 0.75
+    x[2, :] = np.linspace(-2, 2, H)
+    xb = oracle.round_bf16(x)
+    n = oracle.bf16_to_f64(oracle.rms_norm(xb, eps=0.0))
+    assert n[0, 5] == -45.25 and np.count_nonzero(n[0]) == 1  # sqrt(2048) = 45.2548 -> BF16 45.25
+    assert np.all(n[1] == 1.0)
+    xs = gen.make_tokens(1, 4)
+    a = oracle.rms_norm(xs, eps=0.0)
+    scaled = oracle.round_bf16(oracle.bf16_to_f64(xs) * 2.0 ** -5)
+    assert np.array_equal(oracle.rms_norm(scaled, eps=0.0), a)
+    v = oracle.bf16_to_f64(a)
+    assert np.all(np.abs((v ** 2).mean(axis=1) - 1.0) < 2 ** -7)
+    assert np.all(np.sign(v) == np.sign(oracle.bf16_to_f64(xs)))
