@@ -155,6 +155,26 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
                    const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
                    size_t ws_bytes, hipStream_t stream);
 
+/* moe_expert_ffn with the down projection summed over the 16-element blocks
+ * [kb0, kb1) of I only: y_rows / y_shared receive that K-split partial (the
+ * gate/up, SwiGLU and A4(h) steps are the full ones).  Two calls with
+ * [0, I/32) and [I/32, I/16) give the two partial products that a
+ * two-way split of the down projection would exchange (Richland article, "Why
+ * it matters": partial sums exchanged in BF16 lose accuracy, FP16 with a 2^-k
+ * shift keeps it).  kb0 < kb1 <= I/16, both even; a partial range runs on the
+ * matrix-core kernels (T >= 32, kb0 and kb1 multiples of 4) or the generic
+ * ones.  Errors as moe_expert_ffn, MOE_ESHAPE for a bad range.               */
+int moe_expert_ffn_krange(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                          const int32_t* row2pair, int32_t kb0, int32_t kb1, float* y_rows, float* y_shared,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The un-rounded FP32 output of the combine without residual:
+ *   out[t] = sum_j topk_w[t][j] * y_rows[pair2row[t*k+j]] + y_shared[t]
+ * summed exactly as moe_combine sums before its rounding (j ascending, then
+ * the shared row).  out [T][H] FP32 device.                                  */
+int moe_combine_f32(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared,
+                    const int32_t* pair2row, const float* topk_w, float* out, hipStream_t stream);
+
 /* Combine: out[t] = RNE_BF16( sum_j topk_w[t][j] * y_rows[pair2row[t*k+j]]
  *                             + y_shared[t] + residual[t] ), summed in FP32 in
  * that order (j ascending).  y_shared nullable iff has_shared == 0; residual

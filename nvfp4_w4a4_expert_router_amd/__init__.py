@@ -65,15 +65,18 @@ def _load():
     L.moe_layer_forward.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz,
                                     vp]
     L.moe_rms_norm.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_double, vp, vp]
+    L.moe_expert_ffn_krange.argtypes = [pl, vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, sz, vp]
+    L.moe_combine_f32.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
-              "moe_rms_norm"):
+              "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32"):
         getattr(L, f).restype = ci
     return L
 
 
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm")
+           "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm", "moe_expert_ffn_krange",
+           "moe_combine_f32")
 
 
 def strerror(code: int) -> str:
@@ -175,6 +178,22 @@ def moe_quantize_act(x, codes, scales, gscale=1.0, stream=None):
     rows, cols = x.shape
     _check(lib.moe_quantize_act(_ptr(x), dtype, rows, cols, gscale, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_act")
+
+
+def moe_expert_ffn_krange(layer: MoELayer, x, expert_off, row2pair, kb0, kb1, y_rows, y_shared, ws, T=None,
+                          stream=None):
+    """moe_expert_ffn with the down projection over the I-blocks [kb0, kb1) only."""
+    T = x.shape[0] if T is None else T
+    _check(lib.moe_expert_ffn_krange(ctypes.byref(layer.desc), _ptr(x), T, _ptr(expert_off), _ptr(row2pair), kb0,
+                                     kb1, _ptr(y_rows), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_expert_ffn_krange")
+
+
+def moe_combine_f32(layer: MoELayer, y_rows, y_shared, pair2row, topk_w, out, T=None, stream=None):
+    """FP32 combine without residual or rounding: out [T][H] float32."""
+    T = out.shape[0] if T is None else T
+    _check(lib.moe_combine_f32(ctypes.byref(layer.desc), T, _ptr(y_rows), _ptr(y_shared), _ptr(pair2row),
+                               _ptr(topk_w), _ptr(out), _stream(stream)), "moe_combine_f32")
 
 
 def moe_rms_norm(x, out, eps=1e-6, stream=None):

@@ -159,12 +159,17 @@ static bool debug_ok(const moe_debug* d) {
   return true;
 }
 
-int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
-                   const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
-                   size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// moe_expert_ffn with the down projection restricted to the I-blocks [kb0, kb1)
+static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                      const int32_t* row2pair, int kb0, int kb1, float* y_rows, float* y_shared,
+                      const moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_layer(L, false, true);
   if (rc) return rc;
   if (T < 0) return MOE_ESHAPE;
+  const bool partial = kb0 != 0 || kb1 != L->I / 16;
+  if (partial && (kb0 < 0 || kb1 > L->I / 16 || kb0 >= kb1 || kb0 % 2 || kb1 % 2)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ptr_ok(x) || !ptr_ok(expert_off) || !ptr_ok(row2pair) || !ptr_ok(y_rows) || !ptr_ok(ws)) return MOE_EINVAL;
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
@@ -178,9 +183,11 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   hipEvent_t* ev = dbg ? dbg->events : nullptr;
   // path by batch size: decode kernels (T <= 4), matrix cores (T >= 32), weight
   // streaming in between; generic kernels for shapes the others do not cover
-  const bool decode_path = ffn_decode_supported(L->H, L->I, T);
-  const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E);
-  const bool stream_path = !decode_path && !mfma_path && ffn_stream_supported(L->H, L->I);
+  // (a K-split partial runs on the matrix cores or the generic kernels)
+  const bool decode_path = !partial && ffn_decode_supported(L->H, L->I, T);
+  const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E) && kb0 % 4 == 0 &&
+                         kb1 % 4 == 0;
+  const bool stream_path = !partial && !decode_path && !mfma_path && ffn_stream_supported(L->H, L->I);
   const bool self_encoding = stream_path;  // these kernels encode x themselves
   const bool want_xdump = dbg && (dbg->xq || dbg->xs);
   // kernel 0: A4(x) codes into the workspace (plus a dequantized FP16 copy for
@@ -227,6 +234,8 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   p.hs_dbg = dbg ? dbg->hs : nullptr;
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
+  p.kc0 = 16 * kb0;
+  p.kc1 = 16 * kb1;
   if (mfma_path)
     return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), xq, xs,
                                      reinterpret_cast<uint8_t*>(base + lay.hq),
@@ -242,6 +251,34 @@ int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32
   }
   if ((rc = launch_rc(launch_ffn_gateup(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
   return launch_rc(launch_ffn_down(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
+}
+
+extern "C" {
+
+int moe_expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                   const int32_t* row2pair, float* y_rows, float* y_shared, const moe_debug* dbg, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  if (check_shape(L) != MOE_OK) return check_shape(L);
+  return expert_ffn(L, x, T, expert_off, row2pair, 0, L->I / 16, y_rows, y_shared, dbg, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_krange(const moe_layer* L, const uint16_t* x, int64_t T, const int32_t* expert_off,
+                          const int32_t* row2pair, int32_t kb0, int32_t kb1, float* y_rows, float* y_shared,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (check_shape(L) != MOE_OK) return check_shape(L);
+  return expert_ffn(L, x, T, expert_off, row2pair, kb0, kb1, y_rows, y_shared, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_combine_f32(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared,
+                    const int32_t* pair2row, const float* topk_w, float* out, hipStream_t stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (T < 0) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ptr_ok(y_rows) || !ptr_ok(pair2row) || !ptr_ok(topk_w) || !ptr_ok(out)) return MOE_EINVAL;
+  if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
+  return launch_rc(launch_combine_f32(T, L->H, L->k, y_rows, L->has_shared ? y_shared : nullptr, pair2row, topk_w,
+                                      out, stream));
 }
 
 int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float* y_shared, const int32_t* pair2row,
@@ -328,6 +365,8 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;
   p.shared_split = 1;
+  p.kc0 = 0;
+  p.kc1 = L->I;
   if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
   if ((rc = launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr)))) return rc;
   return launch_rc(launch_combine(T, L->H, L->k, y_rows, p.y_shared, pair2row, topk_w, residual, out, stream));

@@ -62,6 +62,45 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
   *reinterpret_cast<uint2*>(out + t * H + c4) = make_uint2(lo, hi);
 }
 
+// The un-rounded FP32 layer output without residual (a K-split partial when
+// the rows are partials): out[t] = sum_j w[t][j] y[pair2row[t*k+j]] + y_shared[t].
+__global__ __launch_bounds__(256) void k_combine_f32(int64_t T, int H, int k, const float* __restrict__ y_rows,
+                                                     const float* __restrict__ y_shared,
+                                                     const int32_t* __restrict__ p2r, const float* __restrict__ w,
+                                                     float* __restrict__ out) {
+  const int per_row = H / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= T * per_row) return;
+  const int64_t t = gid / per_row;
+  const int c4 = (int)(gid % per_row) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const float4 y = *reinterpret_cast<const float4*>(y_rows + (int64_t)p2r[t * k + j] * H + c4);
+    acc.x += wj * y.x;
+    acc.y += wj * y.y;
+    acc.z += wj * y.z;
+    acc.w += wj * y.w;
+  }
+  if (y_shared) {
+    const float4 y = *reinterpret_cast<const float4*>(y_shared + t * H + c4);
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  *reinterpret_cast<float4*>(out + t * H + c4) = acc;
+}
+
+hipError_t launch_combine_f32(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
+                             const float* w, float* out, hipStream_t s) {
+  const int64_t n = T * (H / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, H, k, y_rows, y_shared,
+                     p2r, w, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
                           const float* w, const uint16_t* residual, uint16_t* out, hipStream_t s) {
   const int64_t n = T * (H / 4);

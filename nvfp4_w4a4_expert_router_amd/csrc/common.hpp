@@ -359,6 +359,10 @@ struct FfnParams {
   // decode kernels, fused path: routed slot s -> {expert (or -1), first row,
   // rows, tokens of the rows (one byte each)}; null: slots from expert_off
   const int4* slot_tab;
+  // down projection over the elements [kc0, kc1) of I only (a K-split
+  // partial; the full sum is kc0 = 0, kc1 = I).  Generic and matrix-core
+  // kernels; kc0, kc1 multiples of 32 (of 64 on the matrix cores).
+  int kc0, kc1;
 };
 
 // Fused decode routing (moe_layer_forward, T <= 4): FP64 logits and A4(x),
@@ -429,6 +433,8 @@ bool ffn_stream_supported(int H, int I);
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_down_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_rms_norm(const uint16_t* x, int64_t T, int H, double eps, uint16_t* out, hipStream_t s);
+hipError_t launch_combine_f32(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
+                             const float* w, float* out, hipStream_t s);
 hipError_t launch_combine(int64_t T, int H, int k, const float* y_rows, const float* y_shared, const int32_t* p2r,
                           const float* w, const uint16_t* residual, uint16_t* out, hipStream_t s);
 

@@ -157,13 +157,13 @@ __global__ __launch_bounds__(256) void k_ffn_down(FfnParams p) {
   const int64_t n = (int64_t)nb * kWRows + wr;
   const uint8_t* q_row = Q + n * rowb;
   const uint8_t* s_row = S + n * srow;
-  const int nch = I / 32;
+  const int ch0 = p.kc0 / 32, ch1 = p.kc1 / 32;  // K range of the down projection
   __shared__ float part[kRB][kWRows][kSub + 1];
 
   for (int r0 = 0; r0 < si.nrows; r0 += kRB) {
     const int nr = min(kRB, si.nrows - r0);
     float acc[kRB] = {};
-    for (int ch = sub; ch < nch; ch += kSub) {
+    for (int ch = ch0 + sub; ch < ch1; ch += kSub) {
       const uint4 q = *reinterpret_cast<const uint4*>(q_row + ch * 16);
       const uint32_t s0 = s_row[2 * ch], s1 = s_row[2 * ch + 1];
 #pragma unroll

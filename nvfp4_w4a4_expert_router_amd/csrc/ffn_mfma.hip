@@ -207,8 +207,9 @@ __global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* _
   const int64_t hrow = shared ? (int64_t)T * p.k + arow_i : (int64_t)seg_row0 + arow_i;
   const int64_t wrow = (int64_t)nt * kBN + r;
   floatx16 acc[2][2] = {};
-  tile_mma<false>(hq + hrow * (I / 2), hs + hrow * (I / 16), codes + wrow * (I / 2), scales + wrow * (I / 16), I,
-                  As, Bs, acc);
+  const int kc0 = p.kc0;  // K range [kc0, kc1) of I (the full sum: 0, I)
+  tile_mma<false>(hq + hrow * (I / 2) + kc0 / 2, hs + hrow * (I / 16) + kc0 / 16, codes + wrow * (I / 2) + kc0 / 2,
+                  scales + wrow * (I / 16) + kc0 / 16, p.kc1 - kc0, As, Bs, acc);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 #pragma unroll
   for (int i = 0; i < 2; ++i)

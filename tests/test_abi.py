@@ -144,3 +144,12 @@ def test_rms_norm_validation():
     assert moe.lib.moe_rms_norm(FAKE, 4, 2048, float("nan"), FAKE, None) == moe.MOE_EINVAL
     assert moe.lib.moe_rms_norm(None, 4, 2048, 1e-6, FAKE, None) == moe.MOE_EINVAL
     assert moe.lib.moe_rms_norm(None, 0, 2048, 1e-6, None, None) == moe.MOE_OK
+
+
+def test_krange_validation():
+    L = layer()
+    args = lambda kb0, kb1: (ctypes.byref(L), FAKE, 64, FAKE, FAKE, kb0, kb1, FAKE, FAKE, FAKE, 1 << 30, None)
+    for kb0, kb1 in ((0, 33), (-2, 16), (16, 16), (3, 16), (0, 15), (20, 10)):
+        assert moe.lib.moe_expert_ffn_krange(*args(kb0, kb1)) == moe.MOE_ESHAPE, (kb0, kb1)
+    assert moe.lib.moe_combine_f32(ctypes.byref(L), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_combine_f32(ctypes.byref(L), 4, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
