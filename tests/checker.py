@@ -5,13 +5,17 @@ Rules (where floating point may legitimately change an integer decision):
     experts involved differ by less than 1e-6 (and are not exactly equal): a
     reordered sum may then pick the other one (capy-flash README v0.5.4,
     "Measured", footnote on the tensor-core router).  Exactly equal logits are
-    decided by the tie rule (lower id first), with no exemption.  Accepted
-    tokens are teacher-forced: the oracle continues with the GPU's ids.
+    decided by the tie rule (lower id first), with no exemption.  For an
+    accepted token the oracle continues with that valid alternative selection
+    (its own weights for it, from its own logits).
   * A4(x) codes and scales are bit-exact (x is BF16, both sides exact).
   * the permutation is bit-exact (recomputed by the oracle from the adopted ids).
   * A4(h) codes may differ only where the oracle's h lies within the FP32
     rounding band of a decision threshold (the GPU's h is an FP32 sum in
-    another order); such rows are teacher-forced for the down projection.
+    another order); for the down projection the oracle then encodes its own h
+    with the decision taken on the other side of that threshold.
+Every expected value is computed by the oracle; a GPU result only says which of
+the oracle's valid alternatives (above) to continue with.
   * the BF16 output meets rel-L2 <= 2e-3 against the oracle's BF16 output and
     max-abs <= 1e-2 * RMS against the FP64 value, where a one-BF16-ulp
     difference across a rounding midpoint is accepted.
@@ -74,7 +78,7 @@ def check_topk(idx_g, w_g, logits64, k, rep: Report):
     s = w_g.astype(np.float64).sum(axis=1)
     assert np.all(np.abs(s - 1.0) <= 16 * 2.0 ** -24), "router weights do not sum to 1: %g" % np.abs(s - 1).max()
     rep["w_maxerr"] = float(err.max()) if err.size else 0.0
-    return idx_ad.astype(np.int32), w_g.astype(np.float32)
+    return idx_ad.astype(np.int32), w_ad.astype(np.float32)
 
 
 def check_permutation(idx_ad, E, off_g, r2p_g, p2r_g):
@@ -94,7 +98,10 @@ def _unpack(codes):
 def check_h_codes(h_o, hq_o, hs_o, hq_g, hs_g, g_mid, rep: Report, prefix="h"):
     """Compare GPU A4(h) codes with the oracle's; accept flips inside the rounding band.
 
-    h_o: oracle h (FP32 values), [n][I].  Returns the number of accepted flips."""
+    h_o: oracle h (FP32 values), [n][I].  Returns the oracle's codes (hq, hs) with
+    every accepted decision taken on the other side of its threshold: a block scale
+    moved to the neighbouring code (and the block's elements re-encoded from the
+    oracle's h under it), an element code moved to the neighbouring magnitude."""
     n, I = h_o.shape
     h = h_o.astype(np.float64)
     blocks = h.reshape(n, I // 16, 16)
@@ -141,7 +148,23 @@ def check_h_codes(h_o, hq_o, hs_o, hq_g, hs_g, g_mid, rep: Report, prefix="h"):
             assert abs(abs(h[r, col]) - thr) <= BAND_REL * thr, "row %d col %d: code under flipped scale" % (r, col)
     rep[prefix + "_flips"] = flips
     assert flips <= max(1, 1e-4 * n * I), "%d A4(h) flips exceed 1e-4 of %d elements" % (flips, n * I)
-    return flips
+    # the oracle's codes with the accepted decisions on their other side
+    hs_ad = np.array(hs_o, copy=True)
+    q_ad = qo.copy()
+    for r, b in sd:
+        hs_ad[r, b] = int(hs_o[r, b]) + (1 if hs_g[r, b] > hs_o[r, b] else -1)
+        s = oracle.ue4m3(int(hs_ad[r, b])) * g_mid
+        for i in range(16):
+            col = b * 16 + i
+            q_ad[r, col] = oracle.elem_code(float(h[r, col]), s)
+    for r, i in np.argwhere(q_ad != qg):  # element decisions in the band (validated above)
+        co = int(q_ad[r, i])
+        if (co & 7) == 0 and (int(qg[r, i]) & 7) == 0:
+            continue
+        q_ad[r, i] = co + (1 if (int(qg[r, i]) & 7) > (co & 7) else -1)
+    assert np.array_equal(q_ad & 7, qg & 7) and np.array_equal(hs_ad, hs_g)
+    hq_ad = (q_ad[..., 0::2] | (q_ad[..., 1::2] << 4)).astype(np.uint8)
+    return hq_ad, hs_ad
 
 
 # ---------------------------------------------------------------- output

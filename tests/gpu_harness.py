@@ -79,7 +79,7 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     t0 = time.time()
     if logits64 is None:
         logits64 = oracle.router_logits(x, L.router_w)
-    idx_ad, w_g = checker.check_topk(g["idx"], g["w"], logits64, sh.k, rep)
+    idx_ad, w_ad = checker.check_topk(g["idx"], g["w"], logits64, sh.k, rep)
     checker.check_permutation(idx_ad, sh.E, g["off"], g["r2p"], g["p2r"])
     xq_o, xs_o = oracle.quantize(oracle.bf16_to_f64(x), L.a_gscale_in)
     assert np.array_equal(g["xq"], xq_o), "A4(x) codes differ"
@@ -93,22 +93,24 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     r_o = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
     s_o = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
                              L.a_gscale_mid)
-    checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid, rep, "h")
-    checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows], L.a_gscale_mid, rep,
-                          "hsh")
+    hq_r, hs_r = checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid,
+                                       rep, "h")
+    hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
+                                       L.a_gscale_mid, rep, "hsh")
     if "h" in g:
         hr = g["h"][rows].astype(np.float64)
         d = np.abs(hr - r_o["h"]) / (np.abs(r_o["h"]).max() + 1e-30)
         rep["h_fp32_maxrel"] = float(d.max()) if d.size else 0.0
-    # teacher-forced down projection with the GPU's h codes
+    # down projection on the oracle's own h codes, accepted band decisions taken on
+    # their other side (identical to the oracle's codes when nothing flipped)
     r_t = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid,
-                             hq_in=g["hq"][rows], hs_in=g["hs"][rows])
+                             hq_in=hq_r, hs_in=hs_r)
     s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
-                             L.a_gscale_mid, hq_in=g["hq"][srows], hs_in=g["hs"][srows])
+                             L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s)
     checker.check_fp32_rows(g["y_rows"][rows], r_t["y"], rep, "y_rows")
     checker.check_fp32_rows(g["y_shared"][tok], s_t["y"], rep, "y_shared")
     resid = None if residual is None else residual[tok]
-    o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_g[tok], s_t["y"], resid)
+    o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_ad[tok], s_t["y"], resid)
     checker.check_output(g["out"][tok], o64, o16, rep)
     rep["oracle_s"] = round(time.time() - t0, 2)
     rep["checked_tokens"] = n
