@@ -185,7 +185,7 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   // streaming in between; generic kernels for shapes the others do not cover
   // (a K-split partial runs on the matrix cores or the generic kernels)
   const bool decode_path = !partial && ffn_decode_supported(L->H, L->I, T);
-  const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E) && kb0 % 4 == 0 &&
+  const bool mfma_path = !decode_path && T >= 32 && ffn_mfma_supported(L->H, L->I, L->E, T, L->k) && kb0 % 4 == 0 &&
                          kb1 % 4 == 0;
   const bool stream_path = !partial && !decode_path && !mfma_path && ffn_stream_supported(L->H, L->I);
   const bool self_encoding = stream_path;  // these kernels encode x themselves
@@ -194,7 +194,7 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   // the generic kernels)
   if (!self_encoding || want_xdump) {
     if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
-                                         self_encoding || mfma_path || decode_path ? nullptr : xh, stream,
+                                         self_encoding || decode_path ? nullptr : xh, stream,
                                          ev ? ev[0] : nullptr,
                                          ev ? ev[1] : nullptr))))
       return rc;
@@ -237,9 +237,7 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   p.kc0 = 16 * kb0;
   p.kc1 = 16 * kb1;
   if (mfma_path)
-    return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), xq, xs,
-                                     reinterpret_cast<uint8_t*>(base + lay.hq),
-                                     reinterpret_cast<uint8_t*>(base + lay.hs), stream, ev));
+    return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), stream, ev));
   if (decode_path) {
     p.shared_split = 1;
     if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;

@@ -77,6 +77,19 @@ __device__ __forceinline__ uint32_t elem_code(float v, float s) {
   return mag | (__float_as_uint(v) >> 31 << 3);
 }
 
+// elem_code for a block whose scale is known: s > 0, or +inf for scale code 0
+// (then every magnitude code is 0).  The same seven thresholds and tie rules as
+// elem_code, searched in three exact comparisons: 1.75s (>=), then 3.5s or .75s
+// (>=), then 5s, 2.5s, 1.25s or .25s (>).
+__device__ __forceinline__ uint32_t elem_code_s(float v, float s) {
+  const float a = fabsf(v);
+  const bool c4 = a >= 1.75f * s;
+  const bool c2 = a >= (c4 ? 3.5f : 0.75f) * s;
+  const bool c1 = a > (c4 ? (c2 ? 5.0f : 2.5f) : (c2 ? 1.25f : 0.25f)) * s;
+  const uint32_t mag = (c4 ? 4u : 0u) + (c2 ? 2u : 0u) + (c1 ? 1u : 0u);
+  return mag | (__float_as_uint(v) >> 31 << 3);
+}
+
 // A4 encoding of one 16-element block (global scale g, g6 = 6g): returns the
 // UE4M3 scale code; the 16 E2M1 codes go to *packed, element i in bits
 // 4(i % 8).. of word i / 8 (the low nibble of each byte first).
@@ -102,12 +115,22 @@ __device__ __forceinline__ half2_t fp4x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
 }
 
+// Two UE4M3 codes (low byte first) -> their values as FP16, exactly.  A code
+// c = e:m (4 + 3 bits) placed at bit 7 of an FP16 word has the same exponent and
+// mantissa fields, i.e. the value 2^(e-15)(1 + m/8) (or m 2^-17 when e = 0); FP16's
+// bias exceeds UE4M3's by 8, so one multiply by 2^8 gives 2^(e-7)(1 + m/8) and
+// m 2^-9 (codes up to 126: at most 448).
+__device__ __forceinline__ half2_t ue4m3x2_to_half2(uint32_t sc2) {
+  const uint32_t w = ((sc2 & 0xFFu) << 7) | ((sc2 & 0xFF00u) << 15);
+  return __builtin_bit_cast(half2_t, w) * half2_t{(half_t)256.0f, (half_t)256.0f};
+}
+
 // 32 codes (16 B: two 16-element blocks) times their UE4M3 scales (sc2: low
 // byte = first block) -> 32 FP16 values at dst (16-byte aligned).  Each
 // product has at most 6 significant bits and lies in [2^-10, 2688]: exact.
 __device__ __forceinline__ void decode32_fp16(uint4 q, uint32_t sc2, half_t* dst) {
-  const half_t s0 = (half_t)ue4m3_value(sc2 & 0xFFu), s1 = (half_t)ue4m3_value((sc2 >> 8) & 0xFFu);
-  const half2_t S0 = half2_t{s0, s0}, S1 = half2_t{s1, s1};
+  const half2_t sv = ue4m3x2_to_half2(sc2);
+  const half2_t S0 = half2_t{sv[0], sv[0]}, S1 = half2_t{sv[1], sv[1]};
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   half8_t out[4];
 #pragma unroll
@@ -131,7 +154,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (a few ulp; far
+// inside the FP32 accumulation error of the sums that produce z).  Large negative
+// z gives exp = inf and a signed zero, keeping the sign of the exact value.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resource over [base, base + bytes): 32-bit per-lane offsets, a
@@ -152,6 +180,12 @@ __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint3
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
+// 4-byte store through a buffer resource; offsets at or past the resource's size
+// are dropped (the offset is all in voff: the range check covers it).
+__device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
@@ -163,6 +197,35 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 template <int kCtrl, int kRowMask, bool kZeroOld>
 __device__ __forceinline__ int dpp_mov(int v) {
   return __builtin_amdgcn_update_dpp(kZeroOld ? 0 : v, v, kCtrl, kRowMask, 0xF, true);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+// max of |v| over each row of 16 lanes, returned in every lane of the row
+// (non-negative floats order like their bit patterns)
+__device__ __forceinline__ float row16_absmax(float v) {
+  uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));  // row_mirror
+  return __uint_as_float(u);
+}
+
+// compile-time loop: f(IntC<0>{}) .. f(IntC<kN - 1>{})
+template <int kV>
+struct IntC {
+  static constexpr int value = kV;
+};
+template <int kI, int kN, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (kI < kN) {
+    f(IntC<kI>{});
+    static_for<kI + 1, kN>(f);
+  }
 }
 
 template <int kCtrl, int kRowMask, bool kZeroOld>
@@ -424,10 +487,9 @@ bool route_decode_supported(int H, int E, int k, int64_t T);
 hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 // matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
-bool ffn_mfma_supported(int H, int I, int E);
+bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k);
 size_t ffn_mfma_ws_bytes(int E);
-hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, const uint8_t* xq, const uint8_t* xs,
-                           uint8_t* hq, uint8_t* hs, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev);
 // weight-streaming kernels (H % 256 == 0, I / 32 a power of two <= 64)
 bool ffn_stream_supported(int H, int I);
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);

@@ -6,8 +6,11 @@
 // exact FP16 normal number.  The block scale therefore rides on the element and
 // the product of two decoded operands is exact in FP32; the matrix core sums in
 // FP32 (Richland article, "Why it matters": FP32 partials) and the per-expert
-// FP32 scales multiply the result once.  The A4 activations arrive already
-// dequantized to FP16 (x from the A4 kernel, h from this file's epilogue).
+// FP32 scales multiply the result once.  The A4 activations are read already
+// dequantized to FP16 (x from the A4 kernel, h from the gate/up epilogue): each
+// is decoded once instead of once per column tile, and a 64-wide K step of an
+// FP16 row is one 128-byte line, so 8 lanes load a row with full-line requests.
+// The weights are read as codes and scales and decoded by the workgroup.
 //
 // Work decomposition: the rows of each expert segment (permuted-row order) are
 // cut into 128-row tiles; a work item is (row tile, column tile).  A small
@@ -27,8 +30,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdsStride = kBK + 8;  // halfs per LDS row (+16 B against bank conflicts)
+constexpr int kBM = 128, kBN = 256, kBK = 64;  // tile rows, tile B rows (columns), K step
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
@@ -63,72 +65,129 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
   if (tid <= E + 1) tile_start[tid] = tid > 0 ? part[tid - 1] : 0;
 }
 
-// One K step of 64: each thread carries 16 B of codes and the two UE4M3 scales
-// of one A row and of one B row (32 elements each).
-struct Stage {
-  uint4 aq, bq;
-  uint32_t as, bs;
+// LDS ring of kStages K steps.  Each stage holds the tile's A rows (128 rows x 64
+// FP16 = 128 B, as 8 chunks of 16 B; chunk c of row r sits in slot c ^ (r % 8) so
+// that the MFMA reads of 8 consecutive rows hit 8 different bank groups), the
+// step's 32 B of codes of each of the 256 B rows (two 16-byte halves; half h of
+// row r sits in slot h ^ (r / 4 % 2), for the same reason) and the step's four
+// UE4M3 scales of each B row.  All of it arrives by buffer loads that write LDS
+// directly (64 lanes x 16 B per transfer: 8 A rows or 32 B rows; 64 lanes x 4 B:
+// 64 scale words), so the ring costs no registers and is filled 2 steps ahead.
+constexpr int kStages = 3;
+struct Ring {
+  uint4 a[kStages][kBM * 8];
+  uint4 b[kStages][kBN * 2];
+  uint32_t s[kStages][kBN];
 };
 
-// A (activation rows, A4 codes) x B (weight rows, NVFP4 codes), both decoded to
-// FP16 in LDS; 4 waves, wave (wm, wn) owns a 64 x 64 quadrant as 2 x 2 MFMA tiles.
-// kGateUp: B rows 0..63 are gate columns, 64..127 the matching up columns, and
-// wave w covers h columns 32*(w%2).. of both.
-template <bool kGateUp>
-__device__ __forceinline__ void tile_mma(const uint8_t* __restrict__ arow_q, const uint8_t* __restrict__ arow_s,
-                                         const uint8_t* __restrict__ brow_q, const uint8_t* __restrict__ brow_s,
-                                         int K, half_t* As, half_t* Bs, floatx16 (&acc)[2][2]) {
+// One operand set: buffer resources and per-lane byte offsets (a K step at element
+// k0 adds 2 k0 for A, k0 / 2 for B codes and k0 / 16 for B scales as wave-uniform
+// offsets).  adma[c] / bdma[c]: the row (and swizzled chunk) this lane moves in
+// the wave's c-th A / B transfer; sdma: the B row whose scales this lane moves.
+struct Operands {
+  __amdgpu_buffer_rsrc_t a, bq, bs;
+  uint32_t adma[4], bdma[2], sdma;
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
+// registers) over K = [k_begin, k_begin + K).  Wave (wm, wn) owns 64 rows x 128
+// B rows as 2 x 4 MFMA tiles.  K is taken in a lane-contiguous order: in MFMA s
+// (0..3) of a step, lanes 0..31 supply elements 8s..8s+7 and lanes 32..63
+// elements 32+8s..32+8s+7, for A and B alike, so a lane's B codes for the step
+// are one 16-byte half-row (two whole 16-element blocks).  Each wave decodes the
+// B codes it needs after reading them from the ring.  One barrier per step.
+// bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
+template <typename BRow>
+__device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, Ring& ring, BRow bj,
+                                         floatx16 (&acc)[2][4]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int r = tid >> 1, hf = tid & 1;  // loader row and 32-element half of the K step
   const int wm = (wave >> 1) * 64;
-  const int wn = kGateUp ? (wave & 1) * 32 : (wave & 1) * 64;
-  auto fetch = [&](int k0, Stage& st) {
-    st.aq = *reinterpret_cast<const uint4*>(arow_q + k0 / 2 + hf * 16);
-    st.as = *reinterpret_cast<const uint16_t*>(arow_s + k0 / 16 + hf * 2);
-    st.bq = *reinterpret_cast<const uint4*>(brow_q + k0 / 2 + hf * 16);
-    st.bs = *reinterpret_cast<const uint16_t*>(brow_s + k0 / 16 + hf * 2);
+  const int n = K / kBK;
+  const int hk = lane >> 5;
+  auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
+  // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
+  auto dma = [&](int t, int stage) {
+    const uint32_t k0 = kof(t);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.a, (lds_ptr_t)&ring.a[stage][(32 * wave + 8 * c) * 8], 16, O.adma[c],
+                                               k0 * 2, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bq, (lds_ptr_t)&ring.b[stage][(64 * wave + 32 * c) * 2], 16, O.bdma[c],
+                                               k0 / 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&ring.s[stage][64 * wave], 4, O.sdma, k0 / 16, 0, 0);
   };
-  Stage st;
-  fetch(0, st);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();  // the previous step's fragments are read
-    decode32_fp16(st.aq, st.as, &As[r * kLdsStride + hf * 32]);
-    decode32_fp16(st.bq, st.bs, &Bs[r * kLdsStride + hf * 32]);
-    __syncthreads();
-    if (k0 + kBK < K) fetch(k0 + kBK, st);  // next step in flight during the MFMAs
+  auto compute = [&](int stage) {
+    uint4 bq[4];
+    half2_t sv[4];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      const int ko = kk + 8 * (lane >> 5);
-      half8_t a[2], b[2];
+    for (int j = 0; j < 4; ++j) {
+      const int r = bj(j) + (lane & 31);
+      bq[j] = ring.b[stage][r * 2 + (hk ^ ((r >> 2) & 1))];
+      sv[j] = ue4m3x2_to_half2(ring.s[stage][r] >> (16 * hk));
+    }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const half8_t*>(&As[(wm + 32 * i + (lane & 31)) * kLdsStride + ko]);
-      if (kGateUp) {
-        b[0] = *reinterpret_cast<const half8_t*>(&Bs[(wn + (lane & 31)) * kLdsStride + ko]);
-        b[1] = *reinterpret_cast<const half8_t*>(&Bs[(64 + wn + (lane & 31)) * kLdsStride + ko]);
-      } else {
+    for (int s4 = 0; s4 < 4; ++s4) {
+      half8_t a[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          b[j] = *reinterpret_cast<const half8_t*>(&Bs[(wn + 32 * j + (lane & 31)) * kLdsStride + ko]);
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm + 32 * i + (lane & 31);
+        a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7))]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 4; ++j) {
+        const half2_t S = half2_t{sv[j][s4 >> 1], sv[j][s4 >> 1]};
+        const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
+        const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
+        const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
+      }
     }
-  }
+  };
+  // vmcnt(7) (expcnt, lgkmcnt untouched): the wave's 7 newest transfers (the step
+  // issued last) may still be in flight; the one before is complete, and the
+  // barrier then publishes it to the other waves
+  auto wait_ring = [&]() { __builtin_amdgcn_s_waitcnt(0xF77); };  // vmcnt 7, expcnt 7, lgkmcnt 15
+  dma(0, 0);
+  dma(1, 1);
+  wait_ring();
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  // step t: transfers for step t + 2 into stage (t + 2) % 3 (last read in step
+  // t - 1, before the previous barrier), then the MFMAs of step t
+  auto phase = [&](auto pc, int t) {
+    constexpr int P = decltype(pc)::value;  // t % 3
+    dma(t + 2, (P + 2) % kStages);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(P);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_ring();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int t = 0;
+  for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
+  const int rem = n - t;
+  static_for<0, 2>([&](auto pc) {
+    if (decltype(pc)::value < rem) phase(pc, t + decltype(pc)::value);
+  });
+  __builtin_amdgcn_s_waitcnt(0);  // no transfer into LDS outlives the loop
 }
 
 // ---------------------------------------------------------------- G1
-// h codes + scales of every row go to hq / hs (permuted rows, then shared rows);
-// the down GEMM reads them back as its A operand.
-__global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
-                                                     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
-                                                     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ __align__(16) half_t As[kBM * kLdsStride];
-  __shared__ __align__(16) half_t Bs[kBN * kLdsStride];
+// Tile: 128 rows x (128 gate + 128 up) columns; wave (wm, wn) holds h columns
+// nt*128 + wn .. + 63 as gate blocks j = 0, 1 and up blocks j = 2, 3, so SwiGLU
+// pairs (j, j + 2) meet in the same lane.  Dequantized A4(h) of every row goes
+// to hh (permuted rows, then shared rows); the down GEMM reads it back as its A
+// operand.  Codes and scales are written only to the debug dumps.
+__global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+  __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
-  const int n_nt = I / 64;
+  const int n_nt = I / 128;
   const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const int nseg = E + 1;
   if (mt >= tile_start[nseg]) return;
@@ -141,53 +200,106 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnParams p, const int32_t*
   const uint8_t* scales = shared ? p.sh13.scales : p.w13.scales + (int64_t)seg * 2 * I * (H / 16);
   const float G = (shared ? p.sh13.gscale[0] : p.w13.gscale[seg]) * p.g_in;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int r = tid >> 1;
-  // A row r: the token of tile row r (rows past the segment reuse token 0; dropped)
-  int atok = 0;
-  if (m0 + r < seg_rows) atok = shared ? m0 + r : p.row2pair[seg_row0 + m0 + r] / p.k;
-  // B row r: 0..63 gate columns nt*64.., 64..127 the up columns
-  const int64_t wrow = r < 64 ? (int64_t)nt * 64 + r : (int64_t)I + nt * 64 + (r - 64);
-  floatx16 acc[2][2] = {};
-  tile_mma<true>(xq + (int64_t)atok * (H / 2), xs + (int64_t)atok * (H / 16), codes + wrow * (H / 2),
-                 scales + wrow * (H / 16), H, As, Bs, acc);
-  // epilogue: lane holds h column wn + (lane & 31) of rows 8*(q/4) + 4*(lane/32) + q%4
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 32;
-  const int col = nt * 64 + wn + (lane & 31);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  // ring B row r: gate column nt*128 + r (r < 128), up column I + nt*128 + r - 128
+  auto wrow = [&](int r) { return (uint32_t)(r < 128 ? nt * 128 + r : I + nt * 128 + (r - 128)); };
+  auto bj = [&](int j) { return j < 2 ? wn + 32 * j : 128 + wn + 32 * (j - 2); };
+  Operands O;
+  O.a = buffer_rsrc(p.xh, (uint32_t)T * H * 2u);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // A row: the token of tile row 32 w + 8 c + lane / 8 (rows past the segment read token 0; dropped)
+    const int m = 32 * wave + 8 * c + (lane >> 3);
+    const int tok = m0 + m < seg_rows ? (shared ? m0 + m : p.row2pair[seg_row0 + m0 + m] / p.k) : 0;
+    O.adma[c] = (uint32_t)tok * H * 2u + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+  }
+  O.bq = buffer_rsrc(codes, 2u * I * (H / 2));
+  O.bs = buffer_rsrc(scales, 2u * I * (H / 16));
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    // B transfer c: ring rows 64 w + 32 c + lane / 2, half (lane % 2) ^ (row / 4 % 2)
+    const int r = 64 * wave + 32 * c + (lane >> 1);
+    O.bdma[c] = wrow(r) * (H / 2) + (uint32_t)((lane & 1) ^ ((r >> 2) & 1)) * 16u;
+  }
+  O.sdma = wrow(64 * wave + lane) * (H / 16);
+  floatx16 acc[2][4] = {};
+  tile_mma(O, 0, H, ring, bj, acc);
+  // Epilogue.  Lane holds h column nt*128 + wn + 32 jg + (lane & 31) of rows
+  // 8*(q/4) + 4*(lane/32) + q%4 (q = 0..15) of each 32-row block i; a 16-column A4
+  // block of one row is one DPP row of 16 lanes.  Block amax by DPP max; lane r
+  // of each DPP row then owns row q = r: it computes that row's scale code once
+  // and broadcasts the scale back with row_newbcast.  Codes of lanes 2c, 2c+1 are
+  // paired, converted to FP16 and scaled together, and the even lane stores the
+  // pair.  Stores go through a buffer resource sized to the segment's rows in this
+  // tile: rows past the segment are dropped by its range check.
+  const int rr = lane & 15;
   const float g6 = 6.0f * p.g_mid;
+  const int64_t orow0 = (shared ? (int64_t)T * p.k : (int64_t)seg_row0) + m0;
+  const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
+  const __amdgpu_buffer_rsrc_t hh_r = buffer_rsrc(p.hh + orow0 * I, (uint32_t)nrows * I * 2u);
+  // (the debug dumps take a separate copy of the epilogue)
+  auto epilogue = [&](auto dumps_c) {
+    constexpr bool kDumps = decltype(dumps_c)::value != 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = wm + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-      const float g = G * acc[i][0][q], u = G * acc[i][1][q];
-      const float h = silu(g) * u;
-      float amax = fabsf(h);
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
-      amax = fmaxf(amax, __shfl_xor(amax, 8));
-      const uint32_t scode = scale_code(amax, g6);
-      const float sv = ue4m3_value(scode);
-      const uint32_t c = elem_code(h, sv * p.g_mid);
-      const uint32_t c_hi = __shfl_xor(c, 1);
-      if (m0 + m < seg_rows) {
-        const int64_t orow = shared ? (int64_t)T * p.k + m0 + m : (int64_t)seg_row0 + m0 + m;
-        const uint8_t byte = (uint8_t)(c | (c_hi << 4));
-        if ((col & 1) == 0) hq[orow * (I / 2) + col / 2] = byte;
-        if ((col & 15) == 0) hs[orow * (I / 16) + col / 16] = (uint8_t)scode;
-        if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-        if (p.hq_dbg && (col & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = byte;
-        if (p.hs_dbg && (col & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
+      for (int jg = 0; jg < 2; ++jg) {
+        const int col = nt * 128 + wn + 32 * jg + (lane & 31);
+        float hv[16], amx[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          hv[q] = silu(G * acc[i][jg][q]) * (G * acc[i][jg + 2][q]);
+          amx[q] = row16_absmax(hv[q]);
+        }
+        float my = amx[0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) my = rr == q ? amx[q] : my;
+        const uint32_t scode = scale_code(my, g6);
+        const float uv = ue4m3_value(scode);                        // 0 for code 0
+        const float sv = scode ? uv * p.g_mid : __builtin_inff();  // unit of the element thresholds
+        const int mrow = wm + 32 * i + 4 * (lane >> 5);             // tile row of q = 0
+        const uint32_t voff0 = (uint32_t)(mrow * I + col) * 2u;
+        if (kDumps && p.hs_dbg) {
+          const int m = mrow + 8 * (rr >> 2) + (rr & 3);
+          if (m < nrows) p.hs_dbg[(orow0 + m) * (I / 16) + (col - (lane & 15)) / 16] = (uint8_t)scode;
+        }
+        static_for<0, 16>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          constexpr int dm = 8 * (q >> 2) + (q & 3);
+          const float s = dpp_f32<0x150 + q>(sv);  // row_newbcast: lane q of the DPP row
+          const float u = dpp_f32<0x150 + q>(uv);
+          const uint32_t c = elem_code_s(hv[q], s);
+          const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
+          const half_t uh = (half_t)u;  // exact: a UE4M3 value
+          const half2_t hd = fp4x2<0>(c2) * half2_t{uh, uh};  // exact: <= 6 significant bits
+          if ((lane & 1) == 0) buffer_store4(__builtin_bit_cast(uint32_t, hd), hh_r, voff0 + (uint32_t)(dm * I * 2));
+          if (kDumps) {
+            const int m = mrow + dm;
+            if (m < nrows) {
+              const int64_t orow = orow0 + m;
+              if (p.hq_dbg) {
+                uint32_t t = c2 | (uint32_t)__builtin_amdgcn_mov_dpp((int)c2, 0x102, 0xF, 0xF, true) << 8;  // row_shl:2
+                t |= (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x104, 0xF, 0xF, true) << 16;               // row_shl:4
+                if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(p.hq_dbg + orow * (I / 2) + col / 2) = t;
+              }
+              if (p.h_dbg) p.h_dbg[orow * I + col] = hv[q];
+            }
+          }
+        });
       }
     }
-  }
+  };
+  if (p.h_dbg || p.hq_dbg || p.hs_dbg)
+    epilogue(IntC<1>{});
+  else
+    epilogue(IntC<0>{});
 }
 
 // ---------------------------------------------------------------- G2
-__global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
-                                                   const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs) {
-  __shared__ __align__(16) half_t As[kBM * kLdsStride];
-  __shared__ __align__(16) half_t Bs[kBN * kLdsStride];
+// Tile: 128 rows x 256 output columns; wave (wm, wn) holds columns nt*256 + wn ..
+// + 127 as blocks j = 0..3.
+__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+  __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = H / kBN;
   const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
@@ -202,50 +314,67 @@ __global__ __launch_bounds__(256) void k_down_mfma(FfnParams p, const int32_t* _
   const uint8_t* scales = shared ? p.sh2.scales : p.w2.scales + (int64_t)seg * H * (I / 16);
   const float G = (shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int r = tid >> 1;
-  const int arow_i = m0 + r < seg_rows ? m0 + r : 0;
-  const int64_t hrow = shared ? (int64_t)T * p.k + arow_i : (int64_t)seg_row0 + arow_i;
-  const int64_t wrow = (int64_t)nt * kBN + r;
-  floatx16 acc[2][2] = {};
-  const int kc0 = p.kc0;  // K range [kc0, kc1) of I (the full sum: 0, I)
-  tile_mma<false>(hq + hrow * (I / 2) + kc0 / 2, hs + hrow * (I / 16) + kc0 / 16, codes + wrow * (I / 2) + kc0 / 2,
-                  scales + wrow * (I / 16) + kc0 / 16, p.kc1 - kc0, As, Bs, acc);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+  auto bj = [&](int j) { return wn + 32 * j; };
+  // A rows: the tile's rows of hh; rows past the segment read zeros (range check)
+  const int64_t row0 = (shared ? (int64_t)T * p.k : (int64_t)seg_row0) + m0;
+  const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
+  Operands O;
+  O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)nrows * I * 2u);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+  O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
+  O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 64 * wave + 32 * c + (lane >> 1);
+    O.bdma[c] = (uint32_t)(nt * kBN + r) * (I / 2) + (uint32_t)((lane & 1) ^ ((r >> 2) & 1)) * 16u;
+  }
+  O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * (I / 16);
+  floatx16 acc[2][4] = {};
+  // K range [kc0, kc1) of I (the full sum: 0, I)
+  tile_mma(O, p.kc0, p.kc1 - p.kc0, ring, bj, acc);
+  // output rows of the tile through a resource sized to the segment's rows in it
+  float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
+  const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
+  const uint32_t voff0 = (uint32_t)((wm + 4 * (lane >> 5)) * H) * 4u;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = nt * kBN + wn + 32 * j + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int n = nt * kBN + bj(j) + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int m = wm + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (m0 + m < seg_rows) {
-          float* dst = shared ? p.y_shared + (int64_t)(m0 + m) * H : p.y_rows + (int64_t)(seg_row0 + m0 + m) * H;
-          dst[n] = G * acc[i][j][q];
-        }
+        const int dm = 32 * i + 8 * (q >> 2) + (q & 3);
+        buffer_store4(__float_as_uint(G * acc[i][j][q]), y_r, voff0 + (uint32_t)(dm * H * 4) + (uint32_t)(n * 4));
       }
     }
 }
 
 // ---------------------------------------------------------------- launchers
-bool ffn_mfma_supported(int H, int I, int E) {
-  return H % kBN == 0 && H % kBK == 0 && I % 64 == 0 && I % kBK == 0 && E <= 1000;
+// Buffer resources address at most 2^32 bytes: the FP16 rows of x (gathered by
+// token) and one expert's weights must stay below 2^31 (h and output rows are
+// addressed per 128-row tile).
+bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k) {
+  const int64_t lim = (int64_t)1 << 31;
+  return H % kBN == 0 && H % kBK == 0 && I % 128 == 0 && I % kBK == 0 && E <= 1000 && T * H * 2 < lim &&
+         (int64_t)I * H < lim;
 }
 
 size_t ffn_mfma_ws_bytes(int E) { return (size_t)(E + 2) * sizeof(int32_t); }
 
-hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, const uint8_t* xq, const uint8_t* xs,
-                           uint8_t* hq, uint8_t* hs, hipStream_t s, hipEvent_t* ev) {
+hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev) {
   const int64_t P = (int64_t)p.T * p.k;
   const int64_t max_tiles = (P + kBM - 1) / kBM + (P < p.E ? P : p.E) + (p.has_shared ? (p.T + kBM - 1) / kBM : 0);
   hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, p.off, p.E, p.T, p.has_shared, tile_start);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_timed(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 64))), dim3(256), 0, s, ev ? ev[2] : nullptr,
-                   ev ? ev[3] : nullptr, p, (const int32_t*)tile_start, xq, xs, hq, hs);
+  e = launch_timed(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 128))), dim3(256), 0, s, ev ? ev[2] : nullptr,
+                   ev ? ev[3] : nullptr, p, (const int32_t*)tile_start);
   if (e != hipSuccess) return e;
   return launch_timed(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, ev ? ev[4] : nullptr,
-                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start, (const uint8_t*)hq, (const uint8_t*)hs);
+                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start);
 }
 
 }  // namespace moe
