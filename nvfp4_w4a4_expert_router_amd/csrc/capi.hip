@@ -54,7 +54,7 @@ int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
 
 // workspace of each call, laid out from offset 0 (calls never overlap in time)
 
-size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E)); }
+size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E, L->H)); }
 
 size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
 

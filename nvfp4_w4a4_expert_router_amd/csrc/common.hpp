@@ -471,7 +471,7 @@ inline hipError_t record_idle(hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
 hipError_t launch_quant_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
                             uint8_t* scales, half_t* deq, hipStream_t s, hipEvent_t e0 = nullptr,
                             hipEvent_t e1 = nullptr);
-size_t route_ws_bytes(int64_t T, int E);
+size_t route_ws_bytes(int64_t T, int E, int H);
 hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int E, int k, const float* logits_in,
                         int32_t* idx, float* w, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int64_t T, int E);

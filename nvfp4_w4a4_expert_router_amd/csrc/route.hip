@@ -80,6 +80,126 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
   }
 }
 
+// ---------------------------------------------------------------- pass A on the matrix cores
+// The same FP32 logits with a proven radius, from BF16 matrix-core products.
+// Every FP32 router weight is the exact sum of three BF16 pieces (truncation
+// leaves at most 16, then 8 significant bits: w = w1 + w2 + w3), and a BF16
+// hidden state times a BF16 piece is exact in FP32, so the only errors are the
+// FP32 additions.  Each K step of 32 sums the 3 pieces x 2 MFMAs (16 products
+// each) into a fresh accumulator: at most 96 additions on any path, counting
+// the MFMA's internal sum as sequential.  Step sums join a group sum (8 steps)
+// and group sums the running sum: depth 96 + 8 + H/256.  The terms' absolute
+// sum is at most (1 + 2^-7 + 2^-14) sum_h |x_h W_eh|; the radius takes unit
+// roundoff 2^-23 (any rounding of the MFMA's FP32 adds, not only to nearest).
+constexpr int RM_T = 64, RM_E = 128, RM_K = 32;
+
+// W [E][H] FP32 -> Wp [3][E][H] BF16 pieces (truncation; exact split)
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ W, int64_t n,
+                                                      uint16_t* __restrict__ Wp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t u = __float_as_uint(W[i]);
+  const float r1 = W[i] - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t u2 = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(u2);
+  Wp[i] = (uint16_t)(u >> 16);
+  Wp[n + i] = (uint16_t)(u2 >> 16);
+  Wp[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
+}
+
+// LDS stage: 64 token rows and 3 x 128 expert rows of a K step (64 B = 4 chunks
+// of 16 B per row; chunk c of row r sits in slot c ^ (r / 2 % 4), so the MFMA
+// reads of 8 consecutive rows fall in 8 different bank groups).  Filled by
+// buffer loads that write LDS directly, one step ahead.
+struct RouterRing {
+  uint4 a[2][RM_T * 4];
+  uint4 b[2][3][RM_E * 4];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+
+// logits[t][e] for a 64-token x 128-expert tile; 4 waves, wave (wt, we) owns
+// tokens 32 wt.. x experts 64 we.. as 2 MFMA tiles.  K order inside a step is
+// lane-contiguous (lanes 0..31 supply elements 8s.., lanes 32..63 16+8s.. in
+// MFMA s), the same for both operands.
+__global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ Wp, int T, int H, int E,
+                                                            float* __restrict__ logits) {
+  __shared__ RouterRing ring;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
+  const int wt = wave >> 1, we = wave & 1;
+  const int n = H / RM_K;
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * H * 2u);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(Wp, 3u * E * H * 2u);
+  // transfers: lane -> row (lane / 4) of a 16-row group, slot lane % 4
+  const uint32_t sw = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
+  const int ta = t0 + 16 * wave + (lane >> 2);
+  const uint32_t aoff = (uint32_t)(ta < T ? ta : T - 1) * H * 2u + sw;  // rows past T repeat the last; dropped
+  const uint32_t boff = (uint32_t)(e0 + (lane >> 2)) * H * 2u + sw;
+  auto dma = [&](int t, int st) {
+    const uint32_t k0 = (uint32_t)((t < n ? t : n - 1) * RM_K);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&ring.a[st][16 * wave * 4], 16, aoff, k0 * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int q = 6 * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&ring.b[st][pc][16 * c * 4], 16, boff,
+                                               k0 * 2 + (uint32_t)(pc * E + 16 * c) * H * 2u, 0, 0);
+    }
+  };
+  floatx16 fresh[2], grp[2], run[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    grp[j] = floatx16{};
+    run[j] = floatx16{};
+  }
+  const int hk = lane >> 5, r32 = lane & 31;
+  const int swz = (r32 >> 1) & 3;
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt 0
+  __syncthreads();
+  for (int t = 0; t < n; ++t) {
+    const int st = t & 1;
+    dma(t + 1, st ^ 1);  // stage st ^ 1 was last read in step t - 1, before the barrier
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fresh[j] = floatx16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int slot = (2 * hk + s2) ^ swz;
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring.a[st][(32 * wt + r32) * 4 + slot]);
+#pragma unroll
+      for (int pc = 2; pc >= 0; --pc)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ring.b[st][pc][(64 * we + 32 * j + r32) * 4 + slot]);
+          fresh[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, fresh[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) grp[j] += fresh[j];
+    if ((t & 7) == 7 || t == n - 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        run[j] += grp[j];
+        grp[j] = floatx16{};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // this wave's transfers for step t + 1 are complete
+    __syncthreads();
+  }
+  // lane holds experts 64 we + 32 j + lane % 32 of tokens 8 (q / 4) + 4 (lane / 32) + q % 4
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 64 * we + 32 * j + r32;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tt = t0 + 32 * wt + 8 * (q >> 2) + 4 * hk + (q & 3);
+      if (tt < T) logits[(int64_t)tt * E + e] = run[j][q];
+    }
+  }
+}
+
 // ||W_e||_2 for every expert (FP32 sum of squares, one wave per expert).
 __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ W, int H, int E,
                                                       float* __restrict__ wnorm) {
@@ -509,9 +629,14 @@ static float gamma_for_depth(int d) {
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-size_t route_ws_bytes(int64_t T, int E) {
+static bool router_mfma_ok(int64_t T, int H, int E) { return T > kGemvMaxT && E % RM_E == 0 && H % RM_K == 0; }
+
+// logits (FP64 at decode, FP32 otherwise), ||W_e|| and, on the matrix-core
+// path, the three BF16 pieces of W
+size_t route_ws_bytes(int64_t T, int E, int H) {
   const size_t lg = T <= kGemvMaxT ? (size_t)(T * E) * sizeof(double) : (size_t)(T * E) * sizeof(float);
-  return align256(lg) + align256((size_t)E * sizeof(float));
+  const size_t pieces = router_mfma_ok(T, H, E) ? 3 * (size_t)E * H * sizeof(uint16_t) : 0;
+  return align256(lg) + align256((size_t)E * sizeof(float)) + align256(pieces);
 }
 
 hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int E, int k, const float* logits_in,
@@ -542,13 +667,24 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
     p.mode = kSelF64;
   } else {
     float* lg = static_cast<float*>(ws);
-    float* wn = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)(T * E) * sizeof(float)));
-    const dim3 grid((unsigned)((E + RE - 1) / RE), (unsigned)((T + RT - 1) / RT));
-    hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(256), 0, s, x, W, (int)T, H, E, lg);
+    char* after_lg = static_cast<char*>(ws) + align256((size_t)(T * E) * sizeof(float));
+    float* wn = reinterpret_cast<float*>(after_lg);
+    if (router_mfma_ok(T, H, E)) {
+      uint16_t* wp = reinterpret_cast<uint16_t*>(after_lg + align256((size_t)E * sizeof(float)));
+      const int64_t nw = (int64_t)E * H;
+      hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
+      const dim3 grid((unsigned)(E / RM_E), (unsigned)((T + RM_T - 1) / RM_T));
+      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(256), 0, s, x, (const uint16_t*)wp, (int)T, H, E, lg);
+      // u = 2^-23 (twice the FP32 unit roundoff), and the pieces' 1 + 2^-7 + 2^-14
+      p.gamma = 2.0f * gamma_for_depth(3 * 2 * 16 + 8 + (H / RM_K + 7) / 8) * (1.0f + 0x1p-6f);
+    } else {
+      const dim3 grid((unsigned)((E + RE - 1) / RE), (unsigned)((T + RT - 1) / RT));
+      hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(256), 0, s, x, W, (int)T, H, E, lg);
+      p.gamma = gamma_for_depth(RK + H / RK);
+    }
     hipLaunchKernelGGL(k_router_norms, dim3((E + 3) / 4), dim3(256), 0, s, W, H, E, wn);
     p.l32 = lg;
     p.wnorm = wn;
-    p.gamma = gamma_for_depth(RK + H / RK);
     p.mode = kSelRefine;
   }
   hipLaunchKernelGGL(k_route_select, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, p);
