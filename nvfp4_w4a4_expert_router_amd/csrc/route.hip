@@ -609,6 +609,134 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
   }
 }
 
+// Pass B for E <= 512 (8 logits per lane), one wave per token.  The k-th largest
+// lower end comes from the wave top-k on the lower ends; the candidates' FP64
+// dot products run four at a time with every load of the four issued first;
+// the final top k is the wave top-k on the candidates.
+constexpr int kSelScratch = 512 + 32;  // wave_topk512: candidate slots, then k results
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// FP64 dots of x_t with four router rows, summed over the wave (exact products:
+// BF16 x FP32 fits in 53 bits).  Lane l takes elements 256 i + 4 l .. + 3, so
+// every load instruction of the wave reads one contiguous run (1 KB of a router
+// row, 512 B of x).
+__device__ __forceinline__ void dot64x4(const uint16_t* __restrict__ xr, const float* __restrict__ W, int H,
+                                        const int (&e)[4], int lane, double (&out)[4]) {
+  double a[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int h0 = lane * 4; h0 < H; h0 += kWave * 4 * 8) {
+    uint2 xv[8];
+    float4 w[4][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = *reinterpret_cast<const uint2*>(xr + h0 + 256 * i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[c][i] = *reinterpret_cast<const float4*>(W + (int64_t)e[c] * H + h0 + 256 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double x0 = (double)__uint_as_float(xv[i].x << 16), x1 = (double)__uint_as_float(xv[i].x & 0xFFFF0000u);
+      const double x2 = (double)__uint_as_float(xv[i].y << 16), x3 = (double)__uint_as_float(xv[i].y & 0xFFFF0000u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        a[c] = fma(x0, (double)w[c][i].x, a[c]);
+        a[c] = fma(x1, (double)w[c][i].y, a[c]);
+        a[c] = fma(x2, (double)w[c][i].z, a[c]);
+        a[c] = fma(x3, (double)w[c][i].w, a[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) out[c] = wave_sum_f64(a[c]);
+}
+
+__global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
+  __shared__ double sv[4][kSelScratch];
+  __shared__ int si[4][kSelScratch];
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= p.T) return;
+  const int lane = lane_id();
+  const int E = p.E, H = p.H, k = p.k;
+  const uint16_t* xr = p.x + t * H;
+  // ||x_t||_2, inflated for its own rounding
+  float sq = 0.0f;
+  for (int h0 = lane * 8; h0 < H; h0 += kWave * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(xr + h0);
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
+      sq = fmaf(lo, lo, sq);
+      sq = fmaf(hi, hi, sq);
+    }
+  }
+  const float xn = sqrtf((float)wave_sum_f64((double)sq)) * 1.001f;
+  // lower ends of the intervals; k-th largest of them
+  double v[8], lo[8];
+  float rad[8];
+  int id[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = lane + kWave * j;
+    const bool ok = e < E;
+    id[j] = ok ? e : 0x7FFFFFFF;
+    v[j] = ok ? (double)p.l32[t * E + e] : -INFINITY;
+    rad[j] = ok ? p.gamma * xn * (p.wnorm[e] * 1.001f) + 1e-30f : 0.0f;
+    lo[j] = v[j] - (double)rad[j];
+  }
+  double my_lo = 0.0;
+  int my_id = 0;
+  wave_topk512(lo, id, k, sv[wave], si[wave], &my_lo, &my_id);
+  const double lk = readlane_f64(my_lo, k - 1);
+  // candidates: upper end reaches lk; listed in lane order
+  bool cand[8];
+  int m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    cand[j] = id[j] != 0x7FFFFFFF && v[j] + (double)rad[j] >= lk;
+    m += cand[j];
+  }
+  const int incl = wave_incl_scan_i32(m);
+  const int nc = __builtin_amdgcn_readlane(incl, 63);
+  int pos = incl - m;
+  wave_sync_lds();  // the top-k scratch is read
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (cand[j]) si[wave][pos++] = id[j];
+  wave_sync_lds();
+  // FP64 logits of the candidates, four at a time
+  for (int c0 = 0; c0 < nc; c0 += 4) {
+    int e4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) e4[c] = si[wave][c0 + c < nc ? c0 + c : c0];
+    double d4[4];
+    dot64x4(xr, p.W, H, e4, lane, d4);
+    if (lane < 4 && c0 + lane < nc) sv[wave][c0 + lane] = lane == 0 ? d4[0] : lane == 1 ? d4[1] : lane == 2 ? d4[2] : d4[3];
+  }
+  wave_sync_lds();
+  // final top k among the candidates (lane owns candidates lane + 64 q)
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int c = lane + kWave * q;
+    v[q] = c < nc ? sv[wave][c] : -INFINITY;
+    id[q] = c < nc ? si[wave][c] : 0x7FFFFFFF;
+  }
+  wave_sync_lds();
+  double my_v = 0.0;
+  int my_e = 0;
+  wave_topk512(v, id, k, sv[wave], si[wave], &my_v, &my_e);
+  const float wk = topk_softmax_weight(my_v, k);
+  if (lane < k) {
+    p.idx[t * k + lane] = my_e;
+    p.w[t * k + lane] = wk;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 bool route_decode_supported(int H, int E, int k, int64_t T) {
   return T >= 1 && T <= kRdMaxT && E <= kRdMaxE && k <= 32 && H % 32 == 0;
@@ -687,7 +815,10 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
     p.wnorm = wn;
     p.mode = kSelRefine;
   }
-  hipLaunchKernelGGL(k_route_select, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, p);
+  if (p.mode == kSelRefine && E <= 512 && k <= 32 && H % 2048 == 0)
+    hipLaunchKernelGGL(k_route_select_refine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_route_select, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
