@@ -263,21 +263,28 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
   return v;
 }
 
-// Top k (k <= 32) of up to 512 values held 8 per lane (value v[j], id[j];
-// unused entries -inf / 0x7FFFFFFF), ordered by (value descending, id
-// ascending).  tau = the k-th best of the 64 lane heads (the best entry of each
-// lane).  The k best heads are all at least tau, so every entry of the true
-// top k is at least tau: only the entries >= tau (~k in total) are ranked
-// against each other.  Lane r < k receives the r-th entry.  The heads and the
-// candidates go through LDS and every lane compares against all of them with
-// broadcast reads, 16 in flight (a single wave has no other wave to hide
-// latency behind).  scratch_v / scratch_i: LDS of kTopkScratch entries for
-// this wave.
+// Top k (k <= 32) of up to 512 values held 8 per lane (value v[j], id[j] < 1024;
+// unused entries -inf), ordered by (value descending, id ascending).  Each entry
+// is ranked by one 64-bit key: the double's bits mapped to an unsigned order
+// with its lowest 10 bits replaced by 1023 - id, so a larger key ranks first
+// (values within 2^-42 relative of each other rank by id: far inside the
+// near-tie margin of a reordered FP64 sum).  tau = the k-th best of the 64
+// lane heads (the best entry of each lane).  The k best heads are all at least
+// tau, so every entry of the true top k is at least tau: only the entries >= tau
+// (~k in total) are ranked against each other.  Lane r < k receives the r-th
+// entry.  The heads and the candidates go through LDS and every lane compares
+// against all of them with broadcast reads, 16 in flight (a single wave has no
+// other wave to hide latency behind).  S: this wave's LDS scratch.
 constexpr int kTopkScratch = 512 + 32;
+struct TopkScratch {
+  uint64_t key[kTopkScratch];
+  double val[kTopkScratch];
+};
 
-// (va, ia) ranks before (vb, ib); evaluated without short circuit (no branch)
-__device__ __forceinline__ bool ahead(double va, int ia, double vb, int ib) {
-  return (va > vb) | ((va == vb) & (ia < ib));
+__device__ __forceinline__ uint64_t rank_key(double v, int id) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t u = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (u & ~0x3FFull) | (uint64_t)(1023 - (id & 1023));
 }
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
@@ -287,37 +294,39 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double(((unsigned long long)hi << 32) | lo);
 }
 
-__device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k, double* scratch_v, int* scratch_i,
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const unsigned lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFull), l);
+  const unsigned hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void wave_topk512(const double (&v)[8], const int (&id)[8], int k, TopkScratch& S,
                                              double* out_v, int* out_id) {
   const int lane = (int)(threadIdx.x & 63);
-  // this lane's head
-  double hv = v[0];
-  int hi = id[0];
+  uint64_t key[8];
 #pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    const bool b = ahead(v[j], id[j], hv, hi);
-    hv = b ? v[j] : hv;
-    hi = b ? id[j] : hi;
-  }
+  for (int j = 0; j < 8; ++j) key[j] = rank_key(v[j], id[j]);
+  // this lane's head
+  uint64_t hk = key[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) hk = key[j] > hk ? key[j] : hk;
   // rank of this lane's head among the 64 heads
-  scratch_v[lane] = hv;
-  scratch_i[lane] = hi;
+  S.key[lane] = hk;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int hr = 0;
 #pragma unroll 16
-  for (int q = 0; q < 64; ++q) hr += ahead(scratch_v[q], scratch_i[q], hv, hi);
+  for (int q = 0; q < 64; ++q) hr += S.key[q] > hk;
   const uint64_t at = __ballot(hr == k - 1);
   const int L = __ffsll((long long)at) - 1;
-  const double tau = readlane_f64(hv, L);
-  const int tau_id = __builtin_amdgcn_readlane(hi, L);
+  const uint64_t tau = readlane_u64(hk, L);
   // candidates: the entries not behind tau, compacted in lane order
   bool cand[8];
   int m = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    cand[j] = !ahead(tau, tau_id, v[j], id[j]);
+    cand[j] = key[j] >= tau;
     m += cand[j];
   }
   const int incl = wave_incl_scan_i32(m);
@@ -329,8 +338,8 @@ __device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (cand[j]) {
-      scratch_v[pos] = v[j];
-      scratch_i[pos] = id[j];
+      S.key[pos] = key[j];
+      S.val[pos] = v[j];
       ++pos;
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -340,25 +349,25 @@ __device__ __forceinline__ void wave_topk512(double (&v)[8], int (&id)[8], int k
   // rank r < k goes to result slot r
   for (int c0 = 0; c0 < nc; c0 += kWave) {
     const int c = c0 + lane;
-    const double cv = c < nc ? scratch_v[c] : -INFINITY;
-    const int ci = c < nc ? scratch_i[c] : 0x7FFFFFFF;
+    const uint64_t ck = c < nc ? S.key[c] : 0ull;
+    const double cv = c < nc ? S.val[c] : 0.0;
     int r = 0;
     int q = 0;
     for (; q + 16 <= nc; q += 16)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) r += ahead(scratch_v[q + u], scratch_i[q + u], cv, ci);
-    for (; q < nc; ++q) r += ahead(scratch_v[q], scratch_i[q], cv, ci);
+      for (int u = 0; u < 16; ++u) r += S.key[q + u] > ck;
+    for (; q < nc; ++q) r += S.key[q] > ck;
     if (c < nc && r < k) {  // results after the 512 candidate slots
-      scratch_v[512 + r] = cv;
-      scratch_i[512 + r] = ci;
+      S.key[512 + r] = ck;
+      S.val[512 + r] = cv;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < k) {
-    *out_v = scratch_v[512 + lane];
-    *out_id = scratch_i[512 + lane];
+    *out_v = S.val[512 + lane];
+    *out_id = 1023 - (int)(S.key[512 + lane] & 0x3FFull);
   }
 }
 

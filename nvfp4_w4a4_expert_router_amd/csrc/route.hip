@@ -237,8 +237,7 @@ constexpr int kRdMaxT = 4;  // fused variant: one wave per token in the last wor
 constexpr int kRdMaxE = 512;
 
 struct RoutingLds {
-  double sv[kRdMaxT][kTopkScratch];  // top-k scratch, one per token wave
-  int si[kRdMaxT][kTopkScratch];
+  TopkScratch ts[kRdMaxT];  // top-k scratch, one per token wave
   unsigned int tmask[kRdMaxE];  // tokens that chose expert e (bit t)
   int off[kRdMaxE + 1];
   int nzr[kRdMaxE];  // experts with pairs and a smaller id (slot of the expert)
@@ -264,7 +263,7 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
       id[j] = e < E ? e : 0x7FFFFFFF;
     }
     double my_v = 0.0;
-    wave_topk512(v, id, k, R.sv[wave], R.si[wave], &my_v, &my_e);
+    wave_topk512(v, id, k, R.ts[wave], &my_v, &my_e);
     const float wk = topk_softmax_weight(my_v, k);
     if (lane < k) {
       atomicOr(&R.tmask[my_e], 1u << wave);
@@ -439,8 +438,11 @@ __device__ __forceinline__ double dot64_lane(const uint16_t* __restrict__ xr, co
 
 // One wave per token, 4 tokens per workgroup.
 __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
-  __shared__ double cval[4][kMaxCand];
-  __shared__ int cid[4][kMaxCand];
+  // per wave: candidate values and ids, later the top-k scratch (same bytes)
+  static_assert(sizeof(TopkScratch) <= kMaxCand * (sizeof(double) + sizeof(int)), "scratch fits");
+  __shared__ __align__(16) unsigned char cbuf[4][kMaxCand * (sizeof(double) + sizeof(int))];
+  double* const cvalw = reinterpret_cast<double*>(cbuf[threadIdx.x >> 6]);
+  int* const cidw = reinterpret_cast<int*>(cbuf[threadIdx.x >> 6] + kMaxCand * sizeof(double));
   const int wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= p.T) return;
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
       const int e = lane + kWave * j;
       const bool c = j < nper && e < E && v[j] + (double)rad[j] >= lk;
       const uint64_t m = __ballot(c);
-      if (c) cid[wave][ncand + __popcll(m & ((1ull << lane) - 1ull))] = e;
+      if (c) cidw[ncand + __popcll(m & ((1ull << lane) - 1ull))] = e;
       ncand += __popcll(m);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -521,8 +523,8 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const uint16_t* xr = p.x + t * H;
     for (int c = 0; c < ncand; c += 2) {
-      const int e0 = cid[wave][c];
-      const int e1 = c + 1 < ncand ? cid[wave][c + 1] : e0;
+      const int e0 = cidw[c];
+      const int e1 = c + 1 < ncand ? cidw[c + 1] : e0;
       double a0 = dot64_lane(xr, p.W + (int64_t)e0 * H, H, lane);
       double a1 = dot64_lane(xr, p.W + (int64_t)e1 * H, H, lane);
 #pragma unroll
@@ -531,8 +533,8 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
         a1 += __shfl_xor(a1, m);
       }
       if (lane == 0) {
-        cval[wave][c] = a0;
-        if (c + 1 < ncand) cval[wave][c + 1] = a1;
+        cvalw[c] = a0;
+        if (c + 1 < ncand) cvalw[c + 1] = a1;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -542,8 +544,8 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
 #pragma unroll
     for (int q = 0; q < kMaxPerLane; ++q) {
       const int c = lane + kWave * q;
-      v[q] = c < ncand ? cval[wave][c] : -INFINITY;
-      vid[q] = c < ncand ? cid[wave][c] : 0x7FFFFFFF;
+      v[q] = c < ncand ? cvalw[c] : -INFINITY;
+      vid[q] = c < ncand ? cidw[c] : 0x7FFFFFFF;
     }
   }
   // top k by (value desc, id asc) over the entries with a valid id
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    wave_topk512(v8, id8, k, cval[wave], cid[wave], &my_v, &my_e);
+    wave_topk512(v8, id8, k, *reinterpret_cast<TopkScratch*>(cbuf[wave]), &my_v, &my_e);
     const float wk = topk_softmax_weight(my_v, k);
     if (lane < k) {
       p.idx[t * k + lane] = my_e;
@@ -613,8 +615,6 @@ __global__ __launch_bounds__(256) void k_route_select(RouteB p) {
 // lower end comes from the wave top-k on the lower ends; the candidates' FP64
 // dot products run four at a time with every load of the four issued first;
 // the final top k is the wave top-k on the candidates.
-constexpr int kSelScratch = 512 + 32;  // wave_topk512: candidate slots, then k results
-
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -655,8 +655,7 @@ __device__ __forceinline__ void dot64x4(const uint16_t* __restrict__ xr, const f
 }
 
 __global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
-  __shared__ double sv[4][kSelScratch];
-  __shared__ int si[4][kSelScratch];
+  __shared__ TopkScratch ts[4];  // per wave; between the two top-k passes it holds the candidates
   const int wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= p.T) return;
@@ -691,7 +690,7 @@ __global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
   }
   double my_lo = 0.0;
   int my_id = 0;
-  wave_topk512(lo, id, k, sv[wave], si[wave], &my_lo, &my_id);
+  wave_topk512(lo, id, k, ts[wave], &my_lo, &my_id);
   const double lk = readlane_f64(my_lo, k - 1);
   // candidates: upper end reaches lk; listed in lane order
   bool cand[8];
@@ -707,29 +706,29 @@ __global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
   wave_sync_lds();  // the top-k scratch is read
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (cand[j]) si[wave][pos++] = id[j];
+    if (cand[j]) ts[wave].key[pos++] = (uint64_t)id[j];
   wave_sync_lds();
   // FP64 logits of the candidates, four at a time
   for (int c0 = 0; c0 < nc; c0 += 4) {
     int e4[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) e4[c] = si[wave][c0 + c < nc ? c0 + c : c0];
+    for (int c = 0; c < 4; ++c) e4[c] = (int)ts[wave].key[c0 + c < nc ? c0 + c : c0];
     double d4[4];
     dot64x4(xr, p.W, H, e4, lane, d4);
-    if (lane < 4 && c0 + lane < nc) sv[wave][c0 + lane] = lane == 0 ? d4[0] : lane == 1 ? d4[1] : lane == 2 ? d4[2] : d4[3];
+    if (lane < 4 && c0 + lane < nc) ts[wave].val[c0 + lane] = lane == 0 ? d4[0] : lane == 1 ? d4[1] : lane == 2 ? d4[2] : d4[3];
   }
   wave_sync_lds();
   // final top k among the candidates (lane owns candidates lane + 64 q)
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int c = lane + kWave * q;
-    v[q] = c < nc ? sv[wave][c] : -INFINITY;
-    id[q] = c < nc ? si[wave][c] : 0x7FFFFFFF;
+    v[q] = c < nc ? ts[wave].val[c] : -INFINITY;
+    id[q] = c < nc ? (int)ts[wave].key[c] : 0x7FFFFFFF;
   }
   wave_sync_lds();
   double my_v = 0.0;
   int my_e = 0;
-  wave_topk512(v, id, k, sv[wave], si[wave], &my_v, &my_e);
+  wave_topk512(v, id, k, ts[wave], &my_v, &my_e);
   const float wk = topk_softmax_weight(my_v, k);
   if (lane < k) {
     p.idx[t * k + lane] = my_e;
