@@ -66,11 +66,11 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
 }
 
 // LDS ring of kStages K steps.  Each stage holds the tile's A rows (128 rows x 64
-// FP16 = 128 B, as 8 chunks of 16 B; chunk c of row r sits in slot c ^ (r % 8) so
-// that the MFMA reads of 8 consecutive rows hit 8 different bank groups), the
-// step's 32 B of codes of each of the 256 B rows (two 16-byte halves; half h of
-// row r sits in slot h ^ (r / 4 % 2), for the same reason) and the step's four
-// UE4M3 scales of each B row.  All of it arrives by buffer loads that write LDS
+// FP16 = 128 B, as 8 chunks of 16 B; chunk c of row r sits in slot
+// c ^ (r % 8) ^ (r / 8 % 2), so that the MFMA reads of 16 consecutive rows hit 16
+// different 16-byte bank groups), the step's 32 B of codes of each of the 256 B
+// rows (two 16-byte halves; half h of row r sits in slot h ^ (r / 4 % 2) ^
+// (r / 8 % 2), for the same reason) and the step's four UE4M3 scales of each B row.  All of it arrives by buffer loads that write LDS
 // directly (64 lanes x 16 B per transfer: 8 A rows or 32 B rows; 64 lanes x 4 B:
 // 64 scale words), so the ring costs no registers and is filled 2 steps ahead.
 constexpr int kStages = 3;
@@ -126,7 +126,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = bj(j) + (lane & 31);
-      bq[j] = ring.b[stage][r * 2 + (hk ^ ((r >> 2) & 1))];
+      bq[j] = ring.b[stage][r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
       sv[j] = ue4m3x2_to_half2(ring.s[stage][r] >> (16 * hk));
     }
 #pragma unroll
@@ -135,7 +135,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm + 32 * i + (lane & 31);
-        a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7))]);
+        a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
     // A row: the token of tile row 32 w + 8 c + lane / 8 (rows past the segment read token 0; dropped)
     const int m = 32 * wave + 8 * c + (lane >> 3);
     const int tok = m0 + m < seg_rows ? (shared ? m0 + m : p.row2pair[seg_row0 + m0 + m] / p.k) : 0;
-    O.adma[c] = (uint32_t)tok * H * 2u + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+    O.adma[c] = (uint32_t)tok * H * 2u + (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
   }
   O.bq = buffer_rsrc(codes, 2u * I * (H / 2));
   O.bs = buffer_rsrc(scales, 2u * I * (H / 16));
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   for (int c = 0; c < 2; ++c) {
     // B transfer c: ring rows 64 w + 32 c + lane / 2, half (lane % 2) ^ (row / 4 % 2)
     const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = wrow(r) * (H / 2) + (uint32_t)((lane & 1) ^ ((r >> 2) & 1)) * 16u;
+    O.bdma[c] = wrow(r) * (H / 2) + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
   }
   O.sdma = wrow(64 * wave + lane) * (H / 16);
   floatx16 acc[2][4] = {};
@@ -323,13 +323,13 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)nrows * I * 2u);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u + (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
   O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
   O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = (uint32_t)(nt * kBN + r) * (I / 2) + (uint32_t)((lane & 1) ^ ((r >> 2) & 1)) * 16u;
+    O.bdma[c] = (uint32_t)(nt * kBN + r) * (I / 2) + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
   }
   O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * (I / 16);
   floatx16 acc[2][4] = {};

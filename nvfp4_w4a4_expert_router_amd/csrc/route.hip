@@ -108,8 +108,9 @@ __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ 
 }
 
 // LDS stage: 64 token rows and 3 x 128 expert rows of a K step (64 B = 4 chunks
-// of 16 B per row; chunk c of row r sits in slot c ^ (r / 2 % 4), so the MFMA
-// reads of 8 consecutive rows fall in 8 different bank groups).  Filled by
+// of 16 B per row; chunk c of row r sits in slot c ^ f(r), f(r) = bit 2 of r plus
+// twice (bit 1 xor bit 3), so the MFMA reads of 16 consecutive rows fall in 16
+// different 16-byte bank groups).  Filled by
 // buffer loads that write LDS directly, one step ahead.
 struct RouterRing {
   uint4 a[2][RM_T * 4];
@@ -134,7 +135,8 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * H * 2u);
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(Wp, 3u * E * H * 2u);
   // transfers: lane -> row (lane / 4) of a 16-row group, slot lane % 4
-  const uint32_t sw = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
+  auto swz_of = [](int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); };
+  const uint32_t sw = (uint32_t)(((lane & 3) ^ swz_of(lane >> 2)) * 16);
   const int ta = t0 + 16 * wave + (lane >> 2);
   const uint32_t aoff = (uint32_t)(ta < T ? ta : T - 1) * H * 2u + sw;  // rows past T repeat the last; dropped
   const uint32_t boff = (uint32_t)(e0 + (lane >> 2)) * H * 2u + sw;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
     run[j] = floatx16{};
   }
   const int hk = lane >> 5, r32 = lane & 31;
-  const int swz = (r32 >> 1) & 3;
+  const int swz = swz_of(r32);
   dma(0, 0);
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt 0
   __syncthreads();
