@@ -252,18 +252,20 @@ struct RoutingLds {
 __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, RoutingLds& R) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = q.T, E = q.E, k = q.k, P = T * k;
+  // the logits loads first; the token masks are cleared while they are in flight
+  double v[8];
+  int id[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = lane + kWave * j;
+    const bool ok = wave < T && e < E;
+    v[j] = ok ? q.logits[(int64_t)wave * E + e] : -INFINITY;
+    id[j] = ok ? e : 0x7FFFFFFF;
+  }
   for (int e = tid; e < E; e += 256) R.tmask[e] = 0u;
   __syncthreads();
   int my_e = 0;
   if (wave < T) {
-    double v[8];
-    int id[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane + kWave * j;
-      v[j] = e < E ? q.logits[(int64_t)wave * E + e] : -INFINITY;
-      id[j] = e < E ? e : 0x7FFFFFFF;
-    }
     double my_v = 0.0;
     wave_topk512(v, id, k, R.ts[wave], &my_v, &my_e);
     const float wk = topk_softmax_weight(my_v, k);
@@ -275,11 +277,13 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
   }
   __syncthreads();
   if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
+    unsigned int tm[8];
     int c[8], sc = 0, snz = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = lane * 8 + j;
-      c[j] = e < E ? __popc(R.tmask[e]) : 0;
+      tm[j] = e < E ? R.tmask[e] : 0u;
+      c[j] = __popc(tm[j]);
       sc += c[j];
       snz += c[j] > 0;
     }
@@ -291,15 +295,13 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
       if (e < E) {
         R.off[e] = rc;
         R.nzr[e] = rnz;
-        if (c[j] > 0) {  // slot entry: expert, first row, rows, tokens (one byte each, ascending)
-          unsigned int tm = R.tmask[e], toks = 0u;
-          for (int r = 0; r < c[j]; ++r) {
-            toks |= (unsigned)(__ffs(tm) - 1) << (8 * r);
-            tm &= tm - 1u;
-          }
-          q.slot_tab[rnz] = make_int4(e, rc, c[j], (int)toks);
-        }
       }
+      // slot entry: expert, first row, rows, tokens (one byte each, ascending);
+      // at most 4 tokens (bits of tm), peeled without a loop
+      const unsigned int t1 = tm[j] & (tm[j] - 1u), t2 = t1 & (t1 - 1u), t3 = t2 & (t2 - 1u);
+      auto low = [](unsigned int t) { return t ? (unsigned)(__ffs(t) - 1) : 0u; };  // bytes past the count: 0
+      const unsigned int toks = low(tm[j]) | low(t1) << 8 | low(t2) << 16 | low(t3) << 24;
+      if (c[j] > 0) q.slot_tab[rnz] = make_int4(e, rc, c[j], (int)toks);
       rc += c[j];
       rnz += c[j] > 0;
     }
