@@ -99,13 +99,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // are one 16-byte half-row (two whole 16-element blocks).  Each wave decodes the
 // B codes it needs after reading them from the ring.  One barrier per step.
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
+// live_rows: rows of the tile inside the expert's segment; a wave skips the
+// MFMAs (and the B decode) of its 32-row blocks that lie wholly past them.
 template <typename BRow>
-__device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, Ring& ring, BRow bj,
+__device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, int live_rows, Ring& ring, BRow bj,
                                          floatx16 (&acc)[2][4]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int wm = (wave >> 1) * 64;
   const int n = K / kBK;
   const int hk = lane >> 5;
+  const int nlive = live_rows <= wm ? 0 : live_rows <= wm + 32 ? 1 : 2;  // live 32-row blocks of this wave
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
   auto dma = [&](int t, int stage) {
@@ -121,6 +124,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&ring.s[stage][64 * wave], 4, O.sdma, k0 / 16, 0, 0);
   };
   auto compute = [&](int stage) {
+    if (nlive == 0) return;
     uint4 bq[4];
     half2_t sv[4];
 #pragma unroll
@@ -143,8 +147,8 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
         const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
         const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
         const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b, acc[0][j], 0, 0, 0);
+        if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], b, acc[1][j], 0, 0, 0);
       }
     }
   };
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   }
   O.sdma = wrow(64 * wave + lane) * (H / 16);
   floatx16 acc[2][4] = {};
-  tile_mma(O, 0, H, ring, bj, acc);
+  tile_mma(O, 0, H, seg_rows - m0, ring, bj, acc);
   // Epilogue.  Lane holds h column nt*128 + wn + 32 jg + (lane & 31) of rows
   // 8*(q/4) + 4*(lane/32) + q%4 (q = 0..15) of each 32-row block i; a 16-column A4
   // block of one row is one DPP row of 16 lanes.  Block amax by DPP max; lane r
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * (I / 16);
   floatx16 acc[2][4] = {};
   // K range [kc0, kc1) of I (the full sum: 0, I)
-  tile_mma(O, p.kc0, p.kc1 - p.kc0, ring, bj, acc);
+  tile_mma(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
   // output rows of the tile through a resource sized to the segment's rows in it
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
