@@ -14,7 +14,7 @@
 namespace moe {
 
 constexpr int kChunkTok = 256;  // tokens per workgroup (4 waves x 64)
-constexpr int kMaxE = 1024;
+constexpr int kMaxE = 1024;  // the scan's one thread per expert
 
 // Fill this wave's masks for a chunk: masks[wave][e] bit lane = token (chunk base
 // + 64*wave + lane) selected e.
@@ -42,39 +42,39 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
 }
 
 // One workgroup of 1024 threads: thread e walks the chunks in order (base of
-// expert e in chunk c = sum of earlier chunks' counts), then an exclusive scan
-// over experts gives expert_off; bases are shifted by it.
+// expert e in chunk c relative to the expert's segment = sum of earlier chunks'
+// counts; loads in batches of 16, all in flight together), then a scan over
+// experts (per wave, then over the 16 wave totals) gives expert_off.  The
+// scatter adds expert_off to the relative bases.
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ cnt /*in counts, out bases*/, int nchunk,
                                                     int E, int32_t* __restrict__ off) {
-  __shared__ int32_t tot[kMaxE];
-  const int e = threadIdx.x;
+  __shared__ int32_t wtot[16];
+  const int e = threadIdx.x, wave = e >> 6, lane = lane_id();
   int run = 0;
   if (e < E)
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = cnt[(int64_t)c * E + e];
-      cnt[(int64_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = c0 + i < nchunk ? cnt[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < nchunk) cnt[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
-  tot[e] = e < E ? run : 0;
+  const int incl = wave_incl_scan_i32(run);
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries
-  for (int d = 1; d < kMaxE; d <<= 1) {
-    const int add = e >= d ? tot[e - d] : 0;
-    __syncthreads();
-    tot[e] += add;
-    __syncthreads();
-  }
-  const int excl = e > 0 ? tot[e - 1] : 0;
-  if (e < E) {
-    off[e] = excl;
-    for (int c = 0; c < nchunk; ++c) cnt[(int64_t)c * E + e] += excl;
-  }
-  if (e == E - 1) off[E] = tot[e];
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  if (e < E) off[e] = before + incl - run;
+  if (e == E - 1) off[E] = before + incl;
 }
 
 __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int64_t T, int k, int E,
                                                       const int32_t* __restrict__ base /*[nchunk][E]*/,
-                                                      int32_t* __restrict__ r2p, int32_t* __restrict__ p2r) {
+                                                      const int32_t* __restrict__ off, int32_t* __restrict__ r2p,
+                                                      int32_t* __restrict__ p2r) {
   __shared__ unsigned long long masks[4][kMaxE];
   const int64_t t0 = (int64_t)blockIdx.x * kChunkTok;
   build_masks(idx, T, k, E, masks, t0);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict_
   for (int j = 0; j < k; ++j) {
     const int e = idx[t * k + j];
     if (e < 0 || e >= E) continue;
-    int r = base[(int64_t)blockIdx.x * E + e];
+    int r = off[e] + base[(int64_t)blockIdx.x * E + e];
     for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
     r += __popcll(masks[wave][e] & below);
     const int32_t p = (int32_t)(t * k + j);
@@ -162,7 +162,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* 
   int32_t* cnt = static_cast<int32_t*>(ws);
   if (nchunk > 0) hipLaunchKernelGGL(k_perm_count, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, cnt, nchunk, E, off);
-  if (nchunk > 0) hipLaunchKernelGGL(k_perm_scatter, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt, r2p, p2r);
+  if (nchunk > 0) hipLaunchKernelGGL(k_perm_scatter, dim3(nchunk), dim3(256), 0, s, idx, T, k, E, cnt, off, r2p, p2r);
   return hipGetLastError();
 }
 
