@@ -241,23 +241,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if ((l & 3) == 0) gu[rr][w + 4 * scatter_base<64>(l)] = acc[0];
   }
   __syncthreads();
-  // 5. SwiGLU + A4(h): 32 lanes per activation row (two 16-blocks)
+  // 5. SwiGLU + A4(h): 32 lanes per activation row (two 16-blocks, each a DPP
+  // row of 16 lanes); block maxima and code pairing by DPP, pairs of FP16 values
+  // stored by the even lanes
   for (int task = tid; task < nrows * 32; task += 256) {
     const int rr = task / 32, i = task % 32;
     const float g = G * gu[rr][i], u = G * gu[rr][32 + i];
     const float h = silu(g) * u;
-    float amax = fabsf(h);
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    const float amax = row16_absmax(h);
     const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
     const float sv = ue4m3_value(scode);
-    const uint32_t c = elem_code(h, sv * p.g_mid);
-    const uint32_t c_hi = __shfl_down(c, 1, 16);
+    const uint32_t c = elem_code_s(h, scode ? sv * p.g_mid : __builtin_inff());
+    const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
+    const half2_t hd = fp4x2<0>(c2) * half2_t{(half_t)sv, (half_t)sv};  // exact: <= 6 significant bits
     const int64_t orow = shared ? (int64_t)T * p.k + row0 + rr : (int64_t)row0 + rr;
     const int64_t col = (int64_t)cg * 32 + i;
-    p.hh[orow * I + col] = (half_t)(e2m1_value(c) * sv);
+    if ((i & 1) == 0) *reinterpret_cast<uint32_t*>(p.hh + orow * I + col) = __builtin_bit_cast(uint32_t, hd);
     if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-    if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
+    if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)c2;
     if (p.hs_dbg && (i & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
   }
 }

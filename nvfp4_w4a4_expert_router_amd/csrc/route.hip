@@ -209,9 +209,19 @@ __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ 
   if (e >= E) return;
   const int lane = lane_id();
   float s = 0.0f;
-  for (int h = lane; h < H; h += kWave) {
-    const float w = W[(int64_t)e * H + h];
-    s = fmaf(w, w, s);
+  if (H % 4 == 0) {  // 16-byte loads, contiguous across the wave
+    for (int h = 4 * lane; h < H; h += 4 * kWave) {
+      const float4 w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + h);
+      s = fmaf(w.x, w.x, s);
+      s = fmaf(w.y, w.y, s);
+      s = fmaf(w.z, w.z, s);
+      s = fmaf(w.w, w.w, s);
+    }
+  } else {
+    for (int h = lane; h < H; h += kWave) {
+      const float w = W[(int64_t)e * H + h];
+      s = fmaf(w, w, s);
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
