@@ -37,11 +37,13 @@ def sample_tokens(T, n, seed):
     return np.array(sorted(s), dtype=np.int32)
 
 
-@pytest.mark.parametrize("cfg,T", [(0, 8), (1, 1), (1, 4), (1, 257)])
+# expert FFN paths: decode kernels (T <= 4), weight streaming (5..31 tokens),
+# matrix cores (T >= 32; the tiny shape takes 4 and 2 K steps)
+@pytest.mark.parametrize("cfg,T", [(0, 8), (1, 1), (1, 4), (1, 20), (1, 257), (0, 33), (0, 300)])
 def test_layer_full(cfg, T):
     gh.log("case: config %d T=%d" % (cfg, T))
     L, DL = layer_for(cfg)
-    x = gen.make_tokens(cfg, T, step=0 if T != 257 else 7)
+    x = gen.make_tokens(cfg, T, step=0 if T not in (257, 300) else 7)
     g = gh.run_layer(DL, x, dump=("xq", "xs", "hq", "hs", "h"))
     rep = gh.check_layer(L, x, g, tokens=None if T <= 64 else sample_tokens(T, 48, T))
     gh.log("  ", rep.line())
