@@ -51,7 +51,7 @@ __device__ __forceinline__ uint4 opaque(uint4 v) {
 
 // Sum v[0..15] over aligned groups of kG lanes by recursive halving (all steps
 // resolved at compile time).  Afterwards lane l holds the group total of
-// indices base + i for i < max(1, 16 / kG), where base adds `half` for every
+// indices base + i for i < max(1, kN / kG), where base adds `half` for every
 // halving step whose mask bit the lane has.
 template <int kG, int kN>
 struct ReduceScatter {
@@ -266,11 +266,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // ---------------------------------------------------------------- down
 // W2 rows n, I/32 chunks per row = kLPR lanes per row, 64/kLPR rows per wave
 // instruction.  Thread (w, l): chunk l % kLPR of rows
-// n0 + (64/kLPR) * (w + 4 j) + l / kLPR, j < 16.
+// n0 + (64/kLPR) * (w + 4 j) + l / kLPR, j < kDownLoads.  Eight row loads per
+// thread (half a gate/up thread's) give twice the workgroups of sixteen, which
+// the few dozen slots of a decode step need to cover the chip.
+constexpr int kDownLoads = 8;
 template <int kLPR, bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_down_decode(FfnParams p) {
+  constexpr int kJ = kDownLoads;
   constexpr int kRPI = 64 / kLPR;       // rows per wave instruction
-  constexpr int kRowsWG = 64 * kRPI;    // 4 waves x 16 x kRPI
+  constexpr int kRowsWG = 4 * kJ * kRPI;
   const int H = p.H, I = p.I, T = p.T;
   const int n_nb = (H + kRowsWG - 1) / kRowsWG;
   const int nb = blockIdx.x % n_nb, slot = blockIdx.x / n_nb;
@@ -310,10 +314,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const auto rs = buffer_rsrc(bscales + (int64_t)e * H * srow, (uint32_t)H * srow);
   const uint32_t n_lane = (uint32_t)(base_n + kRPI * w);
   const uint32_t vq = n_lane * qrow + ch * 16u, vs = n_lane * srow + ch * 2u;
-  uint4 q[16];
-  uint32_t sc[16];
+  uint4 q[kJ];
+  uint32_t sc[kJ];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {  // rows past H read past the buffer: zeros
+  for (int j = 0; j < kJ; ++j) {  // rows past H read past the buffer: zeros
     q[j] = buffer_load16(rq, vq, (uint32_t)(4 * kRPI * j) * qrow);
     sc[j] = buffer_load2(rs, vs, (uint32_t)(4 * kRPI * j) * srow);
   }
@@ -327,15 +331,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     float acc[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kJ; ++j) {
       acc[j] = chunk32(opaque(q[j]), sc[j], a);
       __builtin_amdgcn_sched_barrier(0);
     }
-    reduce_scatter16<kLPR>(acc, l);
-    constexpr int kKeep = 16 / kLPR > 1 ? 16 / kLPR : 1;
-    const bool writer = kLPR <= 16 || (l & (kLPR / 16 - 1)) == 0;
+    ReduceScatter<kLPR, kJ>::run(acc, l);
+    constexpr int kKeep = kJ / kLPR > 1 ? kJ / kLPR : 1;
+    const bool writer = kLPR <= kJ || (l & (kLPR / kJ - 1)) == 0;
     if (writer) {
-      const int jb = scatter_base<kLPR>(l);
+      const int jb = ReduceScatter<kLPR, kJ>::base(l);
 #pragma unroll
       for (int i = 0; i < kKeep; ++i) {
         const int n = base_n + kRPI * (w + 4 * (jb + i));
@@ -385,7 +389,7 @@ static hipError_t launch_down_lpr(const FfnParams& p, int lpr, dim3 grid, hipStr
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = decode_slots(p);
   const int lpr = p.I / 32;
-  const int rows_wg = 64 * (64 / lpr);
+  const int rows_wg = 4 * kDownLoads * (64 / lpr);
   const dim3 grid((unsigned)(slots * ((p.H + rows_wg - 1) / rows_wg)));
   if (slots == 0) return record_idle(s, ev_before, ev_after);
   if (p.slot_tab) return launch_down_lpr<true>(p, lpr, grid, s, ev_before, ev_after);
