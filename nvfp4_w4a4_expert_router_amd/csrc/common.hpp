@@ -53,14 +53,36 @@ __device__ __forceinline__ float scale_threshold(int c, float g6) {
 // Block scale code = round-to-nearest-even of amax/(6g) on the UE4M3 grid,
 // saturating at 448 (code 126).  Decided by exact comparisons: the code is the
 // number of thresholds below amax, plus one on an exact tie whose upper
-// neighbour is the even code.
-__device__ __forceinline__ uint32_t scale_code(float amax, float g6) {
+// neighbour is the even code.  The thresholds are non-decreasing in c, so the
+// count is c exactly when t(c-1) < amax <= t(c).
+//
+// scale_code_search finds the count by binary search (7 threshold products);
+// scale_code guesses it from amax/(6g) rounded on the UE4M3 grid and keeps the
+// guess when the two bracketing thresholds confirm it.  The guess can only be
+// wrong for amax within a few FP32 ulps of a threshold (or not a number); those
+// lanes take the search.
+__device__ __forceinline__ uint32_t scale_code_search(float amax, float g6) {
   int pos = 0;
 #pragma unroll
   for (int step = 64; step >= 1; step >>= 1)
     if (pos + step <= 126 && scale_threshold(pos + step - 1, g6) < amax) pos += step;
   if (pos < 126 && scale_threshold(pos, g6) == amax && ((pos + 1) & 1) == 0) pos += 1;
   return (uint32_t)pos;
+}
+
+__device__ __forceinline__ uint32_t scale_code(float amax, float g6) {
+  const float y = amax * __builtin_amdgcn_rcpf(g6);
+  // normal range: exponent and three mantissa bits of y, rounded half up
+  // (bits >> 20 = 8 * biased exponent + mantissa; UE4M3's bias is 120 below FP32's)
+  const int cn = (int)((__float_as_uint(y) + 0x80000u) >> 20) - 960;
+  // subnormal range (y < 2^-6): y in units of 2^-9
+  const int cs = (int)(y * 512.0f + 0.5f);
+  int c = y < 0.015625f ? cs : cn;
+  c = c < 0 ? 0 : c > 126 ? 126 : c;
+  const float t_lo = c > 0 ? scale_threshold(c - 1, g6) : -1.0f;
+  const float t_hi = c < 126 ? scale_threshold(c, g6) : __builtin_inff();
+  if (!(t_lo < amax && amax <= t_hi)) return scale_code_search(amax, g6);
+  return (uint32_t)(c + (c < 126 && t_hi == amax && (c & 1) != 0 ? 1 : 0));
 }
 
 // Element code = round-to-nearest-even of |v|/s on the E2M1 grid, saturating
@@ -86,6 +108,24 @@ __device__ __forceinline__ uint32_t elem_code_s(float v, float s) {
   const bool c4 = a >= 1.75f * s;
   const bool c2 = a >= (c4 ? 3.5f : 0.75f) * s;
   const bool c1 = a > (c4 ? (c2 ? 5.0f : 2.5f) : (c2 ? 1.25f : 0.25f)) * s;
+  const uint32_t mag = (c4 ? 4u : 0u) + (c2 ? 2u : 0u) + (c1 ? 1u : 0u);
+  return mag | (__float_as_uint(v) >> 31 << 3);
+}
+
+// elem_code_s with the block's seven threshold products formed once, for a
+// block whose values are encoded many at a time (the same FP32 products, so
+// the same codes).
+struct E2M1Thresholds {
+  float t025, t075, t125, t175, t25, t35, t5;
+};
+__device__ __forceinline__ E2M1Thresholds e2m1_thresholds(float s) {
+  return {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+}
+__device__ __forceinline__ uint32_t elem_code_t(float v, const E2M1Thresholds& T) {
+  const float a = fabsf(v);
+  const bool c4 = a >= T.t175;
+  const bool c2 = a >= (c4 ? T.t35 : T.t075);
+  const bool c1 = a > (c4 ? (c2 ? T.t5 : T.t25) : (c2 ? T.t125 : T.t025));
   const uint32_t mag = (c4 ? 4u : 0u) + (c2 ? 2u : 0u) + (c1 ? 1u : 0u);
   return mag | (__float_as_uint(v) >> 31 << 3);
 }
@@ -161,6 +201,14 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
+// SwiGLU of raw sums: silu(G a) * (G b) for a common factor G > 0, as
+// (a b) / ((1 + 2^(-G log2(e) a)) / G^2), with c = -G log2(e) and inv_g2 = 1 / G^2
+// formed once per tile (the same few-ulp accuracy as silu).
+__device__ __forceinline__ float swiglu_scaled(float a, float b, float c, float inv_g2) {
+  const float e = __builtin_amdgcn_exp2f(c * a);
+  return (a * b) * __builtin_amdgcn_rcpf(fmaf(e, inv_g2, inv_g2));
+}
+
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resource over [base, base + bytes): 32-bit per-lane offsets, a
 // wave-uniform scalar offset, and reads past the end return zero.  Word 3 is
@@ -184,6 +232,22 @@ __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint3
 // are dropped (the offset is all in voff: the range check covers it).
 __device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buffer_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+
+// The values of lanes l % 32 and l % 32 + 32, in an order that depends only on
+// the direction of v_permlane32_swap (one half of the wave exchanged between
+// two registers; with the same value in both, one result holds the lower half's
+// value in every lane and the other the upper half's).  Callers use the pair
+// symmetrically or tag the values with their half.
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t* r0, uint32_t* r1) {
+  const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  *r0 = p[0];
+  *r1 = p[1];
 }
 
 // ---------------------------------------------------------------- wave helpers

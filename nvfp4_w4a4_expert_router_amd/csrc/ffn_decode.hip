@@ -154,13 +154,15 @@ constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use th
 // load) or from expert_off (one round trip and a wave scan).  The A4 codes of
 // x are read from the workspace and decoded to FP16 in LDS while the weight
 // burst is in flight.
+constexpr int kGuCols = 16;  // intermediate columns per workgroup (gate and up rows: 2 kGuCols)
 template <bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
+  constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
   __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
-  __shared__ float gu[kDecMaxT][64];
+  __shared__ float gu[kDecMaxT][2 * kGuCols];
   __shared__ int toks[kDecMaxT];
   const int H = p.H, I = p.I, T = p.T;
-  const int n_cg = I / 32;
+  const int n_cg = I / kGuCols;
   const int cg = blockIdx.x % n_cg, slot = blockIdx.x / n_cg;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
   const int sh_slot = slot - p.n_routed_slots;
@@ -204,14 +206,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const auto rq = buffer_rsrc(bcodes + (int64_t)e * 2 * I * qrow, 2u * I * qrow);
   const auto rs = buffer_rsrc(bscales + (int64_t)e * 2 * I * srow, 2u * I * srow);
   // lanes past the row's chunks read past the buffer: zeros
-  const uint32_t vq = l < nch ? (uint32_t)(cg * 32 + w) * qrow + l * 16u : 0x80000000u;
-  const uint32_t vs = l < nch ? (uint32_t)(cg * 32 + w) * srow + l * 2u : 0x80000000u;
-  uint4 q[16];
-  uint32_t sc[16];
+  const uint32_t vq = l < nch ? (uint32_t)(cg * kGuCols + w) * qrow + l * 16u : 0x80000000u;
+  const uint32_t vs = l < nch ? (uint32_t)(cg * kGuCols + w) * srow + l * 2u : 0x80000000u;
+  uint4 q[kJ];
+  uint32_t sc[kJ];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    // rows w + 4j: j < 8 gate column cg*32 + w + 4j, j >= 8 up column (same + I)
-    const uint32_t rowoff = j < 8 ? (uint32_t)(4 * j) : (uint32_t)I + 4u * (j - 8);
+  for (int j = 0; j < kJ; ++j) {
+    // j < kJ/2: gate column cg*kGuCols + w + 4j; j >= kJ/2: up column w + 4(j - kJ/2) (+ I)
+    const uint32_t rowoff = j < kJ / 2 ? (uint32_t)(4 * j) : (uint32_t)I + 4u * (j - kJ / 2);
     q[j] = buffer_load16(rq, vq, rowoff * qrow);
     sc[j] = buffer_load2(rs, vs, rowoff * srow);
   }
@@ -233,20 +235,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     float acc[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kJ; ++j) {
       acc[j] = chunk32(opaque(q[j]), sc[j], a);
       __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: bounded live registers
     }
-    reduce_scatter16<64>(acc, l);
-    if ((l & 3) == 0) gu[rr][w + 4 * scatter_base<64>(l)] = acc[0];
+    ReduceScatter<64, kJ>::run(acc, l);
+    // row w + 4j of the tile: gate column w + 4j, or up column w + 4j - kGuCols
+    if ((l & (64 / kJ - 1)) == 0) gu[rr][w + 4 * ReduceScatter<64, kJ>::base(l)] = acc[0];
   }
   __syncthreads();
-  // 5. SwiGLU + A4(h): 32 lanes per activation row (two 16-blocks, each a DPP
-  // row of 16 lanes); block maxima and code pairing by DPP, pairs of FP16 values
-  // stored by the even lanes
-  for (int task = tid; task < nrows * 32; task += 256) {
-    const int rr = task / 32, i = task % 32;
-    const float g = G * gu[rr][i], u = G * gu[rr][32 + i];
+  // 5. SwiGLU + A4(h): kGuCols lanes per activation row (each 16-element block
+  // a DPP row of 16 lanes); block maxima and code pairing by DPP, pairs of FP16
+  // values stored by the even lanes
+  for (int task = tid; task < nrows * kGuCols; task += 256) {
+    const int rr = task / kGuCols, i = task % kGuCols;
+    const float g = G * gu[rr][i], u = G * gu[rr][kGuCols + i];
     const float h = silu(g) * u;
     const float amax = row16_absmax(h);
     const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
     const half2_t hd = fp4x2<0>(c2) * half2_t{(half_t)sv, (half_t)sv};  // exact: <= 6 significant bits
     const int64_t orow = shared ? (int64_t)T * p.k + row0 + rr : (int64_t)row0 + rr;
-    const int64_t col = (int64_t)cg * 32 + i;
+    const int64_t col = (int64_t)cg * kGuCols + i;
     if ((i & 1) == 0) *reinterpret_cast<uint32_t*>(p.hh + orow * I + col) = __builtin_bit_cast(uint32_t, hd);
     if (p.h_dbg) p.h_dbg[orow * I + col] = h;
     if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)c2;
@@ -363,7 +366,7 @@ static int decode_slots(const FfnParams& p) {
 hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = decode_slots(p);
   if (slots == 0) return record_idle(s, ev_before, ev_after);
-  const dim3 grid((unsigned)(slots * (p.I / 32)));
+  const dim3 grid((unsigned)(slots * (p.I / kGuCols)));
   if (p.slot_tab) return launch_timed(k_gateup_decode<true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
   return launch_timed(k_gateup_decode<false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
 }

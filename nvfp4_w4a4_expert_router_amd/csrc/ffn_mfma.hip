@@ -91,6 +91,15 @@ struct Operands {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup b of the first n -> logical tile.  Workgroups are handed out round
+// robin over the chip's 8 XCDs (b % 8), each with its own L2; XCD x gets one
+// contiguous run of logical tiles, so the column tiles of a row tile (same A
+// rows) and the row tiles of an expert (same weights) meet in one L2.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
 // A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
 // registers) over K = [k_begin, k_begin + K).  Wave (wm, wn) owns 64 rows x 128
 // B rows as 2 x 4 MFMA tiles.  K is taken in a lane-contiguous order: in MFMA s
@@ -101,7 +110,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
 // live_rows: rows of the tile inside the expert's segment; a wave skips the
 // MFMAs (and the B decode) of its 32-row blocks that lie wholly past them.
-template <typename BRow>
+// kTransposed: the MFMAs take B as their first operand, so acc[i][j] holds the
+// transposed 32 x 32 block (lane l: row 32 i + l % 32 of the wave's rows, B rows
+// 8 (q / 4) + 4 (l / 32) + q % 4 of block j in its entries q = 0..15).
+template <bool kTransposed, typename BRow>
 __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, int live_rows, Ring& ring, BRow bj,
                                          floatx16 (&acc)[2][4]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
@@ -147,8 +159,13 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
         const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
         const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
         const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b, acc[0][j], 0, 0, 0);
-        if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], b, acc[1][j], 0, 0, 0);
+        if (kTransposed) {
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[0], acc[0][j], 0, 0, 0);
+          if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[1], acc[1][j], 0, 0, 0);
+        } else {
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b, acc[0][j], 0, 0, 0);
+          if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], b, acc[1][j], 0, 0, 0);
+        }
       }
     }
   };
@@ -192,9 +209,11 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = I / 128;
-  const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const int nseg = E + 1;
-  if (mt >= tile_start[nseg]) return;
+  const int n_tiles = tile_start[nseg] * n_nt;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int lt = xcd_tile((int)blockIdx.x, n_tiles);
+  const int mt = lt / n_nt, nt = lt % n_nt;
   const int seg = find_tile(tile_start, nseg, mt);
   const bool shared = seg == E;
   const int seg_row0 = shared ? 0 : p.off[seg];
@@ -227,69 +246,78 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   }
   O.sdma = wrow(64 * wave + lane) * (H / 16);
   floatx16 acc[2][4] = {};
-  tile_mma(O, 0, H, seg_rows - m0, ring, bj, acc);
-  // Epilogue.  Lane holds h column nt*128 + wn + 32 jg + (lane & 31) of rows
-  // 8*(q/4) + 4*(lane/32) + q%4 (q = 0..15) of each 32-row block i; a 16-column A4
-  // block of one row is one DPP row of 16 lanes.  Block amax by DPP max; lane r
-  // of each DPP row then owns row q = r: it computes that row's scale code once
-  // and broadcasts the scale back with row_newbcast.  Codes of lanes 2c, 2c+1 are
-  // paired, converted to FP16 and scaled together, and the even lane stores the
-  // pair.  Stores go through a buffer resource sized to the segment's rows in this
+  tile_mma<true>(O, 0, H, seg_rows - m0, ring, bj, acc);
+  // Epilogue.  acc[i][j] is transposed: lane l holds row m = wm + 32 i + l % 32
+  // and h columns c(q) = nt*128 + wn + 32 jg + 8 (q / 4) + 4 (l / 32) + q % 4, so
+  // the first 16-column A4 block of the 32 is entries q < 8 of lanes l and l ^ 32,
+  // the second entries q >= 8.  Each lane takes the maxima of its halves, the
+  // lane pair completes them, lane l < 32 computes the first block's scale code
+  // and lane l + 32 the second's, and the pair exchanges the codes.  Codes of
+  // adjacent columns (q, q + 1) are paired inside the lane, converted to FP16 and
+  // scaled together; four consecutive columns go out as one 8-byte store.
+  // Stores go through a buffer resource sized to the segment's rows in this
   // tile: rows past the segment are dropped by its range check.
-  const int rr = lane & 15;
   const float g6 = 6.0f * p.g_mid;
   const int64_t orow0 = (shared ? (int64_t)T * p.k : (int64_t)seg_row0) + m0;
   const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
   const __amdgpu_buffer_rsrc_t hh_r = buffer_rsrc(p.hh + orow0 * I, (uint32_t)nrows * I * 2u);
+  const int hi = lane >> 5;
+  const float c_exp = -G * 1.4426950408889634f, inv_g2 = 1.0f / (G * G);
   // (the debug dumps take a separate copy of the epilogue)
   auto epilogue = [&](auto dumps_c) {
     constexpr bool kDumps = decltype(dumps_c)::value != 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int m = wm + 32 * i + (lane & 31);  // tile row
 #pragma unroll
       for (int jg = 0; jg < 2; ++jg) {
-        const int col = nt * 128 + wn + 32 * jg + (lane & 31);
-        float hv[16], amx[16];
+        const int col0 = nt * 128 + wn + 32 * jg + 4 * hi;  // column of q = 0
+        float hv[16];
+        uint32_t p0 = 0u, p1 = 0u;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          hv[q] = silu(G * acc[i][jg][q]) * (G * acc[i][jg + 2][q]);
-          amx[q] = row16_absmax(hv[q]);
+          hv[q] = swiglu_scaled(acc[i][jg][q], acc[i][jg + 2][q], c_exp, inv_g2);
+          const uint32_t a = __float_as_uint(hv[q]) & 0x7FFFFFFFu;
+          if (q < 8) p0 = max(p0, a);
+          else p1 = max(p1, a);
         }
-        float my = amx[0];
+        uint32_t x0, y0, x1, y1;
+        lane_pair(p0, &x0, &y0);
+        lane_pair(p1, &x1, &y1);
+        const float amax = __uint_as_float(hi ? max(x1, y1) : max(x0, y0));
+        const uint32_t mine = scale_code(amax, g6) | ((uint32_t)hi << 8);
+        uint32_t ca, cb;
+        lane_pair(mine, &ca, &cb);
+        const uint32_t sc0 = ((ca >> 8) == 0u ? ca : cb) & 0xFFu, sc1 = ((ca >> 8) == 0u ? cb : ca) & 0xFFu;
+        const float u0 = ue4m3_value(sc0), u1 = ue4m3_value(sc1);  // 0 for code 0
+        const E2M1Thresholds T0 = e2m1_thresholds(sc0 ? u0 * p.g_mid : __builtin_inff());
+        const E2M1Thresholds T1 = e2m1_thresholds(sc1 ? u1 * p.g_mid : __builtin_inff());
+        const half_t uh0 = (half_t)u0, uh1 = (half_t)u1;  // exact: UE4M3 values
+        if (kDumps && p.hs_dbg && m < nrows)
+          p.hs_dbg[(orow0 + m) * (I / 16) + (nt * 128 + wn + 32 * jg) / 16 + hi] = (uint8_t)(hi ? sc1 : sc0);
 #pragma unroll
-        for (int q = 1; q < 16; ++q) my = rr == q ? amx[q] : my;
-        const uint32_t scode = scale_code(my, g6);
-        const float uv = ue4m3_value(scode);                        // 0 for code 0
-        const float sv = scode ? uv * p.g_mid : __builtin_inff();  // unit of the element thresholds
-        const int mrow = wm + 32 * i + 4 * (lane >> 5);             // tile row of q = 0
-        const uint32_t voff0 = (uint32_t)(mrow * I + col) * 2u;
-        if (kDumps && p.hs_dbg) {
-          const int m = mrow + 8 * (rr >> 2) + (rr & 3);
-          if (m < nrows) p.hs_dbg[(orow0 + m) * (I / 16) + (col - (lane & 15)) / 16] = (uint8_t)scode;
-        }
-        static_for<0, 16>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          constexpr int dm = 8 * (q >> 2) + (q & 3);
-          const float s = dpp_f32<0x150 + q>(sv);  // row_newbcast: lane q of the DPP row
-          const float u = dpp_f32<0x150 + q>(uv);
-          const uint32_t c = elem_code_s(hv[q], s);
-          const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
-          const half_t uh = (half_t)u;  // exact: a UE4M3 value
-          const half2_t hd = fp4x2<0>(c2) * half2_t{uh, uh};  // exact: <= 6 significant bits
-          if ((lane & 1) == 0) buffer_store4(__builtin_bit_cast(uint32_t, hd), hh_r, voff0 + (uint32_t)(dm * I * 2));
-          if (kDumps) {
-            const int m = mrow + dm;
-            if (m < nrows) {
-              const int64_t orow = orow0 + m;
-              if (p.hq_dbg) {
-                uint32_t t = c2 | (uint32_t)__builtin_amdgcn_mov_dpp((int)c2, 0x102, 0xF, 0xF, true) << 8;  // row_shl:2
-                t |= (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x104, 0xF, 0xF, true) << 16;               // row_shl:4
-                if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(p.hq_dbg + orow * (I / 2) + col / 2) = t;
-              }
-              if (p.h_dbg) p.h_dbg[orow * I + col] = hv[q];
-            }
+        for (int g = 0; g < 4; ++g) {  // columns col0 + 8 g .. + 3: entries 4 g .. 4 g + 3
+          const E2M1Thresholds& Tg = g < 2 ? T0 : T1;
+          const half_t uh = g < 2 ? uh0 : uh1;
+          uint32_t by[2];
+          half2_t hd[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int q = 4 * g + 2 * e;
+            by[e] = elem_code_t(hv[q], Tg) | elem_code_t(hv[q + 1], Tg) << 4;
+            hd[e] = fp4x2<0>(by[e]) * half2_t{uh, uh};  // exact: <= 6 significant bits
           }
-        });
+          const uint32_t voff = (uint32_t)(m * I + col0 + 8 * g) * 2u;
+          buffer_store8(u32x2{__builtin_bit_cast(uint32_t, hd[0]), __builtin_bit_cast(uint32_t, hd[1])}, hh_r, voff);
+          if (kDumps && m < nrows) {
+            const int64_t orow = orow0 + m;
+            const int c = col0 + 8 * g;
+            if (p.hq_dbg) *reinterpret_cast<uint16_t*>(p.hq_dbg + orow * (I / 2) + c / 2) = (uint16_t)(by[0] | by[1] << 8);
+            if (p.h_dbg)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) p.h_dbg[orow * I + c + e] = hv[4 * g + e];
+          }
+        }
       }
     }
   };
@@ -306,9 +334,11 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = H / kBN;
-  const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const int nseg = E + 1;
-  if (mt >= tile_start[nseg]) return;
+  const int n_tiles = tile_start[nseg] * n_nt;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int lt = xcd_tile((int)blockIdx.x, n_tiles);
+  const int mt = lt / n_nt, nt = lt % n_nt;
   const int seg = find_tile(tile_start, nseg, mt);
   const bool shared = seg == E;
   const int seg_row0 = shared ? 0 : p.off[seg];
@@ -338,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * (I / 16);
   floatx16 acc[2][4] = {};
   // K range [kc0, kc1) of I (the full sum: 0, I)
-  tile_mma(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
+  tile_mma<false>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
   // output rows of the tile through a resource sized to the segment's rows in it
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
