@@ -250,6 +250,15 @@ __device__ __forceinline__ void lane_pair(uint32_t v, uint32_t* r0, uint32_t* r1
   *r1 = p[1];
 }
 
+// Workgroup b of the first n -> logical tile.  Workgroups are handed out round
+// robin over the chip's 8 XCDs (b % 8), each with its own L2; XCD x gets one
+// contiguous run of logical tiles, so tiles that are neighbours in logical
+// order (sharing operands) run in the same L2.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 

@@ -91,14 +91,6 @@ struct Operands {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Workgroup b of the first n -> logical tile.  Workgroups are handed out round
-// robin over the chip's 8 XCDs (b % 8), each with its own L2; XCD x gets one
-// contiguous run of logical tiles, so the column tiles of a row tile (same A
-// rows) and the row tiles of an expert (same weights) meet in one L2.
-__device__ __forceinline__ int xcd_tile(int b, int n) {
-  const int x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
-  return x * q + (x < r ? x : r) + i;
-}
 
 // A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
 // registers) over K = [k_begin, k_begin + K).  Wave (wm, wn) owns 64 rows x 128
@@ -120,7 +112,8 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   const int wm = (wave >> 1) * 64;
   const int n = K / kBK;
   const int hk = lane >> 5;
-  const int nlive = live_rows <= wm ? 0 : live_rows <= wm + 32 ? 1 : 2;  // live 32-row blocks of this wave
+  // live 32-row blocks of this wave (wave-uniform: the MFMA loop branches on it once per step, not per MFMA)
+  const int nlive = __builtin_amdgcn_readfirstlane(live_rows <= wm ? 0 : live_rows <= wm + 32 ? 1 : 2);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
   auto dma = [&](int t, int stage) {
@@ -169,6 +162,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
       }
     }
   };
+
   // vmcnt(7) (expcnt, lgkmcnt untouched): the wave's 7 newest transfers (the step
   // issued last) may still be in flight; the one before is complete, and the
   // barrier then publishes it to the other waves

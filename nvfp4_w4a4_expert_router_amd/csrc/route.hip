@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
                                                             float* __restrict__ logits) {
   __shared__ RouterRing ring;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
+  // expert tile major within each XCD's run: one XCD keeps one expert tile's
+  // router rows (3 pieces x 128 rows x H) in its L2 while token tiles stream by
+  const int ntb = (int)gridDim.y;
+  const int lt = xcd_tile((int)(blockIdx.y * gridDim.x + blockIdx.x), (int)(gridDim.x * gridDim.y));
+  const int t0 = (lt % ntb) * RM_T, e0 = (lt / ntb) * RM_E;
   const int wt = wave >> 1, we = wave & 1;
   const int n = H / RM_K;
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * H * 2u);
