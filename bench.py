@@ -14,7 +14,8 @@ batch is timed the same way and reported in `detail`.
 Prefill workload (reported in `detail.prefill`): the same layer shape with
 Zipf(1.1)-skewed routing over one 15,360-token chunk; expert GEMM throughput is
 priced against the FP16 matrix-core peak the exact NVFP4 decode runs on, and
-against the FP8 peak.
+against the FP8 peak.  `detail.streamed_prefill`: a 55,296-token prompt through
+the same layer as four 13,824-token calls, the residual added in each combine.
 
 Inputs are seeded synthetic data, resident in HBM before any timed region.
 Prints one JSON line (stdout).  value = tokens per second through one MoE layer.
@@ -66,6 +67,8 @@ def parse():
     ap.add_argument("--graph-steps", type=int, default=16, help="steps per captured HIP graph (0 = no graph run)")
     ap.add_argument("--prefill-tokens", type=int, default=15360, help="prefill chunk (0 = skip the prefill leg)")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--stream-tokens", type=int, default=55296, help="streamed prompt length (0 = skip)")
+    ap.add_argument("--stream-chunks", type=int, default=4)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode legs (profiling the prefill only)")
     ap.add_argument("--skip-t1", action="store_true", help="skip the 1-token decode leg")
     ap.add_argument("--separate-calls", action="store_true",
@@ -358,6 +361,34 @@ def main():
             rec["ms_per_step"] = round(elapsed * 1e3 / n, 5)
             rec["config"] = {"workload": rec["detail"]["prefill"]["workload"], "tokens_per_step": Tp,
                              "parallelism": "single GPU"}
+        # streamed prompt: the same layer over a long prompt in equal chunks (each
+        # chunk one library call with the residual added in its combine)
+        if args.stream_tokens > 0:
+            Ts, nc = args.stream_tokens, args.stream_chunks
+            cs = Ts // nc
+            xs_ = up(gen.make_tokens(cfg_p, Ts, step=55).view(np.int16))
+            rs_ = up(gen.make_tokens(cfg_p, Ts, step=56).view(np.int16))
+            bufs = moe.Buffers(DLp, cs, dev)
+            outs = torch.empty((Ts, H), dtype=torch.int16, device=dev)
+
+            def prompt():
+                for c in range(nc):
+                    o = moe.moe_layer_forward(DLp, xs_[c * cs:(c + 1) * cs], bufs, residual=rs_[c * cs:(c + 1) * cs])
+                    outs[c * cs:(c + 1) * cs].copy_(o[:cs])
+
+            prompt()
+            torch.cuda.synchronize()
+            reps = 3
+            t_s = time.perf_counter()
+            for _ in range(reps):
+                prompt()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t_s
+            rec["detail"]["streamed_prefill"] = {
+                "workload": "a %d-token prompt as %d chunks of %d tokens, residual added, same layer" % (nc * cs, nc, cs),
+                "tok_s": round(nc * cs * reps / el, 1), "ms_per_prompt": round(el * 1e3 / reps, 4)}
+            log("streamed prefill: %d prompts in %.3f s" % (reps, el))
+            del bufs, xs_, rs_, outs
         del buf, DLp, xp
 
     # ---------------------------------------------------------------- oracle on the host
