@@ -306,7 +306,7 @@ def main():
         Tp, cfg_p = args.prefill_tokens, 3
         t0 = time.time()
         Lp = gen.make_layer(cfg_p)
-        DLp = device_layer(Lp)
+        DLp = device_layer(Lp).pack_kmajor()  # K-step-major weight copies for the matrix-core kernels
         xp = up(gen.make_tokens(cfg_p, Tp).view(np.int16))
         log("prefill layer and %d tokens generated (%.1f s)" % (Tp, time.time() - t0))
         buf = moe.Buffers(DLp, Tp, dev)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum {
   MOE_OK = 0,
@@ -75,12 +75,20 @@ typedef struct {
  *         has_shared == 0
  *   router_w : [E][H] FP32 router weights
  *   a_gscale_in, a_gscale_mid : global scales of the activation encodings of
- *         x and of h; powers of two (1.0 by default)                          */
+ *         x and of h; powers of two (1.0 by default)
+ *   w13k, w2k, sh13k, sh2k : optional K-step-major copies (moe_pack_kmajor) of
+ *         the codes and scales of w13, w2, sh13, sh2 (their gscale is not
+ *         read).  Where a copy's codes pointer is non-null, the matrix-core
+ *         kernels (prompt chunks) read the copy, whose K steps are contiguous
+ *         runs; otherwise they read the row-major bank.  Results are identical
+ *         either way; the decode and weight-streaming kernels always read the
+ *         row-major banks.  Zero-initialise the struct to leave them unset.   */
 typedef struct {
   int32_t H, I, E, k, has_shared;
   const float* router_w;
   moe_nvfp4_bank w13, w2, sh13, sh2;
   float a_gscale_in, a_gscale_mid;
+  moe_nvfp4_bank w13k, w2k, sh13k, sh2k;
 } moe_layer;
 
 /* Optional dumps of intermediate values (all nullable, device pointers).
@@ -223,6 +231,23 @@ int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* 
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
                      uint8_t* scales, hipStream_t stream);
+
+/* K-step-major copy of one NVFP4 bank (the format of moe_nvfp4_bank: the
+ * pages' 16-element E2M1 blocks with UE4M3 scales, Richland article, "What
+ * shipped"), for the matrix-core kernels.  With S = K/64 steps of 64 elements:
+ *   codes_out  [n_exp][S][N][32] : bytes 32s .. 32s+31 of row n (its elements
+ *                                  64s .. 64s+63, same nibble order)
+ *   scales_out [n_exp][S][N][4]  : scales 4s .. 4s+3 of row n
+ * so that one K step of consecutive rows is one contiguous run of memory.
+ *   codes, scales : the row-major bank (device, 16- and 4-byte aligned)
+ *   codes_out [n_exp*N*K/2], scales_out [n_exp*N*K/16] : device, caller-owned,
+ *                   16- and 4-byte aligned, not overlapping the inputs
+ * A pure permutation of bytes; run once per layer, before the copies are
+ * named in a moe_layer.
+ * Errors: MOE_EINVAL (null or misaligned pointer), MOE_ESHAPE (n_exp < 1,
+ * N < 1, K < 64 or K % 64 != 0).                                             */
+int moe_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int32_t n_exp, int32_t N, int32_t K,
+                    uint8_t* codes_out, uint8_t* scales_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

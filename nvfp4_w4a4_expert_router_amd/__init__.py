@@ -36,7 +36,8 @@ class Bank(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("has_shared", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("w13", Bank), ("w2", Bank),
-                ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float)]
+                ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float),
+                ("w13k", Bank), ("w2k", Bank), ("sh13k", Bank), ("sh2k", Bank)]
 
 
 FFN_KERNELS = 3  # A4(x), gate/up + SwiGLU + A4(h), down
@@ -67,8 +68,10 @@ def _load():
     L.moe_rms_norm.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_double, vp, vp]
     L.moe_expert_ffn_krange.argtypes = [pl, vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, sz, vp]
     L.moe_combine_f32.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp]
+    i32 = ctypes.c_int32
+    L.moe_pack_kmajor.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
-              "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32"):
+              "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32", "moe_pack_kmajor"):
         getattr(L, f).restype = ci
     return L
 
@@ -76,7 +79,7 @@ def _load():
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm", "moe_expert_ffn_krange",
-           "moe_combine_f32")
+           "moe_combine_f32", "moe_pack_kmajor")
 
 
 def strerror(code: int) -> str:
@@ -103,6 +106,7 @@ class MoELayer:
 
     router_w [E][H] float32; banks are dicts of uint8 codes / uint8 scales / float32
     gscale tensors in the layouts of include/moe_nvfp4.h.  Tensors are kept alive here.
+    pack_kmajor() adds the K-step-major copies that the matrix-core kernels read.
     """
 
     def __init__(self, H, I, E, k, router_w, w13, w2, sh13=None, sh2=None, a_gscale_in=1.0, a_gscale_mid=1.0):
@@ -116,6 +120,20 @@ class MoELayer:
         self.desc = LayerDesc(H, I, E, k, self.has_shared, _ptr(router_w), bank(w13), bank(w2), bank(sh13), bank(sh2),
                               a_gscale_in, a_gscale_mid)
         self.a_gscale_in, self.a_gscale_mid = a_gscale_in, a_gscale_mid
+
+    def pack_kmajor(self, stream=None):
+        """Write K-step-major copies of every bank (moe_pack_kmajor) and name them in
+        the descriptor; returns self.  Needs H and I to be multiples of 64."""
+        banks = [("w13k", self.w13, self.E, 2 * self.I, self.H), ("w2k", self.w2, self.E, self.H, self.I)]
+        if self.has_shared:
+            banks += [("sh13k", self.sh13, 1, 2 * self.I, self.H), ("sh2k", self.sh2, 1, self.H, self.I)]
+        self.kmajor = {}
+        for name, b, n_exp, N, K in banks:
+            c, s = torch.empty_like(b["codes"]), torch.empty_like(b["scales"])
+            moe_pack_kmajor(b["codes"], b["scales"], n_exp, N, K, c, s, stream=stream)
+            self.kmajor[name] = (c, s)
+            setattr(self.desc, name, Bank(_ptr(c), _ptr(s), None))
+        return self
 
     def workspace_bytes(self, T_max: int) -> int:
         return int(lib.moe_workspace_bytes(ctypes.byref(self.desc), T_max))
@@ -170,6 +188,12 @@ def moe_combine(layer: MoELayer, y_rows, y_shared, pair2row, topk_w, out, residu
     T = out.shape[0] if T is None else T
     _check(lib.moe_combine(ctypes.byref(layer.desc), T, _ptr(y_rows), _ptr(y_shared), _ptr(pair2row), _ptr(topk_w),
                            _ptr(residual), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_pack_kmajor(codes, scales, n_exp, N, K, codes_out, scales_out, stream=None):
+    """K-step-major copy of one NVFP4 bank (include/moe_nvfp4.h)."""
+    _check(lib.moe_pack_kmajor(_ptr(codes), _ptr(scales), n_exp, N, K, _ptr(codes_out), _ptr(scales_out),
+                               _stream(stream)), "moe_pack_kmajor")
 
 
 def moe_quantize_act(x, codes, scales, gscale=1.0, stream=None):

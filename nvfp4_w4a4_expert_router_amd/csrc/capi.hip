@@ -40,6 +40,14 @@ int check_shape(const moe_layer* L) {
   return MOE_OK;
 }
 
+// an optional K-step-major copy: absent (null codes) or codes and scales
+// aligned, with K a whole number of 64-element steps
+int check_kmajor(const moe_nvfp4_bank& b, int K) {
+  if (!b.codes) return MOE_OK;
+  if (!aligned16(b.codes) || !b.scales || reinterpret_cast<uintptr_t>(b.scales) % 4) return MOE_EINVAL;
+  return K % 64 ? MOE_ESHAPE : MOE_OK;
+}
+
 int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
   int rc = check_shape(L);
   if (rc) return rc;
@@ -47,6 +55,8 @@ int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
   if (need_experts) {
     if ((rc = check_bank(L->w13)) || (rc = check_bank(L->w2))) return rc;
     if (L->has_shared && ((rc = check_bank(L->sh13)) || (rc = check_bank(L->sh2)))) return rc;
+    if ((rc = check_kmajor(L->w13k, L->H)) || (rc = check_kmajor(L->w2k, L->I))) return rc;
+    if (L->has_shared && ((rc = check_kmajor(L->sh13k, L->H)) || (rc = check_kmajor(L->sh2k, L->I)))) return rc;
     if (!pow2_scale(L->a_gscale_in) || !pow2_scale(L->a_gscale_mid)) return MOE_EINVAL;
   }
   return MOE_OK;
@@ -226,6 +236,10 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   p.w2 = L->w2;
   p.sh13 = L->sh13;
   p.sh2 = L->sh2;
+  p.w13k = L->w13k;
+  p.w2k = L->w2k;
+  p.sh13k = L->has_shared ? L->sh13k : moe_nvfp4_bank{};
+  p.sh2k = L->has_shared ? L->sh2k : moe_nvfp4_bank{};
   p.g_in = L->a_gscale_in;
   p.g_mid = L->a_gscale_mid;
   p.hh = reinterpret_cast<half_t*>(base + lay.hh);
@@ -357,6 +371,10 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.w2 = L->w2;
   p.sh13 = L->sh13;
   p.sh2 = L->sh2;
+  p.w13k = L->w13k;
+  p.w2k = L->w2k;
+  p.sh13k = L->has_shared ? L->sh13k : moe_nvfp4_bank{};
+  p.sh2k = L->has_shared ? L->sh2k : moe_nvfp4_bank{};
   p.g_in = L->a_gscale_in;
   p.g_mid = L->a_gscale_mid;
   p.hh = reinterpret_cast<half_t*>(fbase + lay.hh);
@@ -376,6 +394,14 @@ int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* 
   if (T == 0) return MOE_OK;
   if (!ptr_ok(x) || !ptr_ok(out)) return MOE_EINVAL;
   return launch_rc(launch_rms_norm(x, T, H, eps, out, stream));
+}
+
+int moe_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int32_t n_exp, int32_t N, int32_t K,
+                    uint8_t* codes_out, uint8_t* scales_out, hipStream_t stream) {
+  if (n_exp < 1 || N < 1 || K < 64 || K % 64) return MOE_ESHAPE;
+  if (!ptr_ok(codes) || !ptr_ok(codes_out) || !scales || !scales_out) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(scales_out) % 4) return MOE_EINVAL;
+  return launch_rc(launch_pack_kmajor(codes, scales, n_exp, N, K, codes_out, scales_out, stream));
 }
 
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,

@@ -489,6 +489,7 @@ struct FfnParams {
   const uint16_t* x;  // [T][H] BF16 hidden states
   const half_t* xh;   // [T][H] dequantized A4(x) without a_gscale_in (generic kernels)
   moe_nvfp4_bank w13, w2, sh13, sh2;
+  moe_nvfp4_bank w13k, w2k, sh13k, sh2k;  // K-step-major copies (codes null: absent)
   float g_in, g_mid;
   half_t* hh;  // [R][I] dequantized A4(h) without a_gscale_mid; R = T*k (+ T)
   float* h_dbg;
@@ -572,6 +573,8 @@ hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_b
 bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k);
 size_t ffn_mfma_ws_bytes(int E);
 hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int n_exp, int N, int K, uint8_t* codes_out,
+                              uint8_t* scales_out, hipStream_t s);
 // weight-streaming kernels (H % 256 == 0, I / 32 a power of two <= 64)
 bool ffn_stream_supported(int H, int I);
 hipError_t launch_gateup_stream(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);

@@ -81,13 +81,21 @@ struct Ring {
 };
 
 // One operand set: buffer resources and per-lane byte offsets (a K step at element
-// k0 adds 2 k0 for A, k0 / 2 for B codes and k0 / 16 for B scales as wave-uniform
+// k0 adds 2 k0 for A, bmul k0 / 2 for B codes and bmul k0 / 16 for B scales as wave-uniform
 // offsets).  adma[c] / bdma[c]: the row (and swizzled chunk) this lane moves in
 // the wave's c-th A / B transfer; sdma: the B row whose scales this lane moves.
 struct Operands {
   __amdgpu_buffer_rsrc_t a, bq, bs;
   uint32_t adma[4], bdma[2], sdma;
+  uint32_t bmul;  // B bytes per K step: 32 bmul of codes, 4 bmul of scales
 };
+
+// B rows (one expert's N x K NVFP4 matrix) are read either from the row-major
+// bank (a row's K step: 32 code bytes at row K/2 + 32 s, bmul = 1) or from its
+// K-step-major copy (32 bytes at (s N + row) 32, bmul = N), where the 32 rows
+// of one wave transfer are one contiguous 1 KB run instead of 32 separate
+// lines; the expert's block has the same size and offset in both.
+
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -125,8 +133,9 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bq, (lds_ptr_t)&ring.b[stage][(64 * wave + 32 * c) * 2], 16, O.bdma[c],
-                                               k0 / 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&ring.s[stage][64 * wave], 4, O.sdma, k0 / 16, 0, 0);
+                                               k0 / 2 * O.bmul, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&ring.s[stage][64 * wave], 4, O.sdma,
+                                             k0 / 16 * O.bmul, 0, 0);
   };
   auto compute = [&](int stage) {
     if (nlive == 0) return;
@@ -213,8 +222,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   const int seg_row0 = shared ? 0 : p.off[seg];
   const int seg_rows = shared ? T : p.off[seg + 1] - p.off[seg];
   const int m0 = (mt - tile_start[seg]) * kBM;
-  const uint8_t* codes = shared ? p.sh13.codes : p.w13.codes + (int64_t)seg * 2 * I * (H / 2);
-  const uint8_t* scales = shared ? p.sh13.scales : p.w13.scales + (int64_t)seg * 2 * I * (H / 16);
+  const moe_nvfp4_bank& bank = shared ? (p.sh13k.codes ? p.sh13k : p.sh13) : (p.w13k.codes ? p.w13k : p.w13);
+  const bool km = shared ? p.sh13k.codes != nullptr : p.w13k.codes != nullptr;
+  const int64_t erow = shared ? 0 : (int64_t)seg * 2 * I;  // the expert's first row in the bank
+  const uint8_t* codes = bank.codes + erow * (H / 2);
+  const uint8_t* scales = bank.scales + erow * (H / 16);
+  const uint32_t qrow = km ? 32u : (uint32_t)(H / 2), srow = km ? 4u : (uint32_t)(H / 16);
   const float G = (shared ? p.sh13.gscale[0] : p.w13.gscale[seg]) * p.g_in;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -236,9 +249,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   for (int c = 0; c < 2; ++c) {
     // B transfer c: ring rows 64 w + 32 c + lane / 2, half (lane % 2) ^ (row / 4 % 2)
     const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = wrow(r) * (H / 2) + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
+    O.bdma[c] = wrow(r) * qrow + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
   }
-  O.sdma = wrow(64 * wave + lane) * (H / 16);
+  O.sdma = wrow(64 * wave + lane) * srow;
+  O.bmul = km ? 2u * I : 1u;
   floatx16 acc[2][4] = {};
   tile_mma<true>(O, 0, H, seg_rows - m0, ring, bj, acc);
   // Epilogue.  acc[i][j] is transposed: lane l holds row m = wm + 32 i + l % 32
@@ -338,8 +352,12 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   const int seg_row0 = shared ? 0 : p.off[seg];
   const int seg_rows = shared ? T : p.off[seg + 1] - p.off[seg];
   const int m0 = (mt - tile_start[seg]) * kBM;
-  const uint8_t* codes = shared ? p.sh2.codes : p.w2.codes + (int64_t)seg * H * (I / 2);
-  const uint8_t* scales = shared ? p.sh2.scales : p.w2.scales + (int64_t)seg * H * (I / 16);
+  const moe_nvfp4_bank& bank = shared ? (p.sh2k.codes ? p.sh2k : p.sh2) : (p.w2k.codes ? p.w2k : p.w2);
+  const bool km = shared ? p.sh2k.codes != nullptr : p.w2k.codes != nullptr;
+  const int64_t erow = shared ? 0 : (int64_t)seg * H;  // the expert's first row in the bank
+  const uint8_t* codes = bank.codes + erow * (I / 2);
+  const uint8_t* scales = bank.scales + erow * (I / 16);
+  const uint32_t qrow = km ? 32u : (uint32_t)(I / 2), srow = km ? 4u : (uint32_t)(I / 16);
   const float G = (shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
@@ -357,9 +375,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = (uint32_t)(nt * kBN + r) * (I / 2) + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
+    O.bdma[c] = (uint32_t)(nt * kBN + r) * qrow + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
   }
-  O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * (I / 16);
+  O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * srow;
+  O.bmul = km ? (uint32_t)H : 1u;
   floatx16 acc[2][4] = {};
   // K range [kc0, kc1) of I (the full sum: 0, I)
   tile_mma<false>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
@@ -391,6 +410,39 @@ bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k) {
 }
 
 size_t ffn_mfma_ws_bytes(int E) { return (size_t)(E + 2) * sizeof(int32_t); }
+
+// K-step-major copy of a bank: thread i moves 16 code bytes (half of one row's
+// K step) or, for i < n_exp S N, one row's 4 scale bytes of a step; both
+// written in output order (contiguous), read as 16- and 4-byte pieces.
+__global__ __launch_bounds__(256) void k_pack_kmajor(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t n_rows_steps, int N,
+                                                     int K, uint8_t* __restrict__ codes_out,
+                                                     uint8_t* __restrict__ scales_out) {
+  const int S = K / 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n_rows_steps; i += (int64_t)gridDim.x * 256) {
+    const int64_t q = i >> 1;  // (e, s, n) in output order
+    const int half = (int)(i & 1);
+    const int n = (int)(q % N);
+    const int64_t es = q / N;
+    const int st = (int)(es % S);
+    const int64_t e = es / S;
+    const int64_t row = e * N + n;
+    *reinterpret_cast<uint4*>(codes_out + i * 16) =
+        *reinterpret_cast<const uint4*>(codes + row * (K / 2) + st * 32 + half * 16);
+    if (half == 0)
+      *reinterpret_cast<uint32_t*>(scales_out + q * 4) =
+          *reinterpret_cast<const uint32_t*>(scales + row * (K / 16) + st * 4);
+  }
+}
+
+hipError_t launch_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int n_exp, int N, int K, uint8_t* codes_out,
+                              uint8_t* scales_out, hipStream_t s) {
+  const int64_t n = (int64_t)n_exp * (K / 64) * N;
+  const int64_t blocks = (2 * n + 255) / 256;
+  hipLaunchKernelGGL(k_pack_kmajor, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, codes, scales,
+                     n, N, K, codes_out, scales_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev) {
   const int64_t P = (int64_t)p.T * p.k;

@@ -29,11 +29,16 @@ def bank_to_dev(b):
     return {"codes": to_dev(b["codes"]), "scales": to_dev(b["scales"]), "gscale": to_dev(b["gscale"])}
 
 
-def device_layer(L, router_w=None) -> moe.MoELayer:
+def device_layer(L, router_w=None, kmajor=True) -> moe.MoELayer:
+    """The layer on the device; kmajor: also the K-step-major weight copies that the
+    matrix-core kernels read (the product configuration)."""
     sh = L.shape
     rw = L.router_w if router_w is None else router_w
-    return moe.MoELayer(sh.H, sh.I, sh.E, sh.k, to_dev(rw), bank_to_dev(L.w13), bank_to_dev(L.w2),
-                        bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid)
+    DL = moe.MoELayer(sh.H, sh.I, sh.E, sh.k, to_dev(rw), bank_to_dev(L.w13), bank_to_dev(L.w2),
+                      bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid)
+    if kmajor and sh.H % 64 == 0 and sh.I % 64 == 0:
+        DL.pack_kmajor()
+    return DL
 
 
 def run_layer(DL: moe.MoELayer, x: np.ndarray, residual=None, dump=("xq", "xs", "hq", "hs"), logits_in=None):

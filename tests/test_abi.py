@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.lib.moe_abi_version() == 1
+    assert moe.lib.moe_abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert moe.strerror(code) and moe.strerror(code) != "unknown error"
     assert moe.strerror(-99) == "unknown error"
@@ -112,6 +112,26 @@ def test_workspace_too_small():
     assert rc == moe.MOE_EWORKSPACE
     rc = moe.lib.moe_permute(ctypes.byref(L), FAKE, 100000, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert rc == moe.MOE_EWORKSPACE
+
+
+def test_kmajor_copies_validated():
+    L = layer()
+    L.w13k = moe.Bank(FAKE + 8, FAKE, None)  # misaligned codes
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+    L = layer()
+    L.w2k = moe.Bank(FAKE, None, None)  # codes without scales
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+    L = layer(I=544)  # I not a whole number of 64-element steps
+    L.w2k = moe.Bank(FAKE, FAKE, None)
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_ESHAPE
+    pack = moe.lib.moe_pack_kmajor
+    assert pack(FAKE, FAKE, 1, 64, 96, FAKE, FAKE, None) == moe.MOE_ESHAPE
+    assert pack(FAKE, FAKE, 0, 64, 128, FAKE, FAKE, None) == moe.MOE_ESHAPE
+    assert pack(FAKE, FAKE, 1, 64, 128, FAKE + 4, FAKE, None) == moe.MOE_EINVAL
+    assert pack(FAKE, FAKE + 2, 1, 64, 128, FAKE, FAKE, None) == moe.MOE_EINVAL
 
 
 def test_workspace_monotone_in_T():

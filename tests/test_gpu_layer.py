@@ -296,3 +296,49 @@ def test_rms_norm_matches_oracle():
         moe.moe_rms_norm(gh.to_dev(x.view(np.int16)), out)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.rms_norm(x)), (T, H)
+
+
+def test_pack_kmajor_layout():
+    """moe_pack_kmajor is the byte permutation its header states (checked on the
+    host copy of the tiny layer's banks)."""
+    L, _ = layer_for(0)
+    for bank in (L.w13, L.w2):
+        codes, scales = bank["codes"], bank["scales"]
+        n_exp, N, K = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+        c_out = torch.empty(codes.size, dtype=torch.uint8, device=gh.DEV)
+        s_out = torch.empty(scales.size, dtype=torch.uint8, device=gh.DEV)
+        moe.moe_pack_kmajor(gh.to_dev(codes), gh.to_dev(scales), n_exp, N, K, c_out, s_out)
+        torch.cuda.synchronize()
+        S = K // 64
+        want_c = codes.reshape(n_exp, N, S, 32).transpose(0, 2, 1, 3).reshape(-1)
+        want_s = scales.reshape(n_exp, N, S, 4).transpose(0, 2, 1, 3).reshape(-1)
+        assert np.array_equal(c_out.cpu().numpy(), want_c)
+        assert np.array_equal(s_out.cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("cfg,T", [(0, 300), (2, 4096)])
+def test_kmajor_copies_give_identical_results(cfg, T):
+    """The matrix-core kernels read the row-major banks or their K-step-major copies
+    with the same arithmetic: every output is bit-identical, and so is the split-K
+    partial of the down projection."""
+    gh.log("case: config %d T=%d, row-major vs K-step-major weights" % (cfg, T))
+    L, DLk = layer_for(cfg)
+    assert DLk.desc.w13k.codes is not None
+    DLr = gh.device_layer(L, kmajor=False)
+    x = gen.make_tokens(cfg, T, step=11)
+    a = gh.run_layer(DLr, x, dump=("hq", "hs"))
+    b = gh.run_layer(DLk, x, dump=("hq", "hs"))
+    for key in ("y_rows", "y_shared", "out", "hq", "hs"):
+        assert np.array_equal(a[key], b[key]), key
+    half = L.shape.I // 32
+    xd = gh.to_dev(x.view(np.int16))
+    outs = []
+    for DL in (DLr, DLk):
+        buf = moe.Buffers(DL, T, gh.DEV)
+        moe.moe_route(DL, xd, buf.topk_idx, buf.topk_w, buf.ws, T=T)
+        moe.moe_permute(DL, buf.topk_idx, buf.expert_off, buf.row2pair, buf.pair2row, buf.ws, T=T)
+        moe.moe_expert_ffn_krange(DL, xd, buf.expert_off, buf.row2pair, half, 2 * half, buf.y_rows, buf.y_shared,
+                                  buf.ws, T=T)
+        torch.cuda.synchronize()
+        outs.append((buf.y_rows.cpu().numpy(), buf.y_shared.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
