@@ -8,6 +8,13 @@
 
 namespace moe {
 
+// 16-byte load marked non-temporal: the rows are read once, so they need not
+// displace other lines in the caches
+__device__ __forceinline__ float4 load_once(const float* p) {
+  const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const float* __restrict__ y_rows,
                                                  const float* __restrict__ y_shared, const int32_t* __restrict__ p2r,
                                                  const float* __restrict__ w, const uint16_t* __restrict__ residual,
@@ -32,7 +39,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
   float4 y[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (j < k) y[j] = *reinterpret_cast<const float4*>(y_rows + r[j] * H + c4);
+    if (j < k) y[j] = load_once(y_rows + r[j] * H + c4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
@@ -44,7 +51,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
     }
   }
   if (y_shared) {
-    const float4 y = *reinterpret_cast<const float4*>(y_shared + t * H + c4);
+    const float4 y = load_once(y_shared + t * H + c4);
     acc.x += y.x;
     acc.y += y.y;
     acc.z += y.z;
