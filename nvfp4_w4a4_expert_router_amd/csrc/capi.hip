@@ -89,7 +89,7 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   w.hs = o;
   o = align_up(o + (size_t)R * (L->I / 16));
   w.tiles = o;
-  o = align_up(o + ffn_mfma_ws_bytes(L->E));
+  o = align_up(o + ffn_mfma_ws_bytes(L->E, T, L->k, L->has_shared));
   w.end = o;
   return w;
 }

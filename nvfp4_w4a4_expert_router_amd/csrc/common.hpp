@@ -571,7 +571,7 @@ hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEve
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 // matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
 bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k);
-size_t ffn_mfma_ws_bytes(int E);
+size_t ffn_mfma_ws_bytes(int E, int64_t T, int k, int has_shared);
 hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int n_exp, int N, int K, uint8_t* codes_out,
                               uint8_t* scales_out, hipStream_t s);

@@ -154,7 +154,7 @@ constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use th
 // load) or from expert_off (one round trip and a wave scan).  The A4 codes of
 // x are read from the workspace and decoded to FP16 in LDS while the weight
 // burst is in flight.
-constexpr int kGuCols = 16;  // intermediate columns per workgroup (gate and up rows: 2 kGuCols)
+constexpr int kGuCols = 32;  // intermediate columns per workgroup (gate and up rows: 2 kGuCols)
 template <bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
   constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up

@@ -35,26 +35,27 @@ constexpr int kBM = 128, kBN = 256, kBK = 64;  // tile rows, tile B rows (column
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 
-// row tile -> (expert slot, first row in the segment); slot E = shared expert
-__device__ __forceinline__ int find_tile(const int32_t* __restrict__ tile_start, int nseg, int mt) {
-  int lo = 0, hi = nseg;  // last seg with tile_start[seg] <= mt
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= mt) lo = mid; else hi = mid;
-  }
-  return lo;
-}
+// The tile table follows tile_start ([E + 2] int32) in the workspace, 16-byte aligned.
+__host__ __device__ inline int tile_tab_offset(int E) { return (E + 2 + 3) / 4 * 4; }
 
 }  // namespace
 
 // tile_start[s] = number of 128-row tiles of segments < s; segments 0..E-1 are the
 // routed experts, segment E the shared expert (T rows), tile_start[E+1] = total.
+// tile_tab[mt] = (segment, first row of the tile in the segment, the segment's
+// first row in the permuted order, the segment's rows) for every row tile mt <
+// total, so that a GEMM workgroup finds its tile in one load instead of a
+// binary search of dependent loads.
 __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ off, int E, int T, int has_shared,
-                                                   int32_t* __restrict__ tile_start) {
+                                                   int32_t* __restrict__ tile_start, int4* __restrict__ tile_tab) {
   __shared__ int part[1024];
+  __shared__ int row0[1024], rows[1024];
   const int tid = threadIdx.x;
-  const int n = tid < E ? (off[tid + 1] - off[tid] + kBM - 1) / kBM : (tid == E && has_shared ? (T + kBM - 1) / kBM : 0);
-  part[tid] = n;
+  const int r0 = tid < E ? off[tid] : 0;
+  const int nr = tid < E ? off[tid + 1] - r0 : (tid == E && has_shared ? T : 0);
+  part[tid] = (nr + kBM - 1) / kBM;
+  row0[tid] = r0;
+  rows[tid] = nr;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
     const int add = tid >= d ? part[tid - d] : 0;
@@ -63,6 +64,16 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
     __syncthreads();
   }
   if (tid <= E + 1) tile_start[tid] = tid > 0 ? part[tid - 1] : 0;
+  const int total = part[E];
+  for (int mt = tid; mt < total; mt += 1024) {
+    int lo = 0, hi = E;  // first segment whose inclusive tile count exceeds mt
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (part[mid] > mt) hi = mid; else lo = mid + 1;
+    }
+    const int first = lo > 0 ? part[lo - 1] : 0;
+    tile_tab[mt] = make_int4(lo, (mt - first) * kBM, row0[lo], rows[lo]);
+  }
 }
 
 // LDS ring of kStages K steps.  Each stage holds the tile's A rows (128 rows x 64
@@ -208,7 +219,8 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 // pairs (j, j + 2) meet in the same lane.  Dequantized A4(h) of every row goes
 // to hh (permuted rows, then shared rows); the down GEMM reads it back as its A
 // operand.  Codes and scales are written only to the debug dumps.
-__global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+__global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                        const int4* __restrict__ tile_tab) {
   __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = I / 128;
@@ -217,11 +229,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   if ((int)blockIdx.x >= n_tiles) return;
   const int lt = xcd_tile((int)blockIdx.x, n_tiles);
   const int mt = lt / n_nt, nt = lt % n_nt;
-  const int seg = find_tile(tile_start, nseg, mt);
+  const int4 te = tile_tab[mt];
+  const int seg = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+  const int seg_row0 = __builtin_amdgcn_readfirstlane(te.z), seg_rows = __builtin_amdgcn_readfirstlane(te.w);
   const bool shared = seg == E;
-  const int seg_row0 = shared ? 0 : p.off[seg];
-  const int seg_rows = shared ? T : p.off[seg + 1] - p.off[seg];
-  const int m0 = (mt - tile_start[seg]) * kBM;
   const moe_nvfp4_bank& bank = shared ? (p.sh13k.codes ? p.sh13k : p.sh13) : (p.w13k.codes ? p.w13k : p.w13);
   const bool km = shared ? p.sh13k.codes != nullptr : p.w13k.codes != nullptr;
   const int64_t erow = shared ? 0 : (int64_t)seg * 2 * I;  // the expert's first row in the bank
@@ -338,7 +349,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
 // ---------------------------------------------------------------- G2
 // Tile: 128 rows x 256 output columns; wave (wm, wn) holds columns nt*256 + wn ..
 // + 127 as blocks j = 0..3.
-__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start) {
+__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                      const int4* __restrict__ tile_tab) {
   __shared__ Ring ring;
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = H / kBN;
@@ -347,11 +359,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   if ((int)blockIdx.x >= n_tiles) return;
   const int lt = xcd_tile((int)blockIdx.x, n_tiles);
   const int mt = lt / n_nt, nt = lt % n_nt;
-  const int seg = find_tile(tile_start, nseg, mt);
+  const int4 te = tile_tab[mt];
+  const int seg = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+  const int seg_row0 = __builtin_amdgcn_readfirstlane(te.z), seg_rows = __builtin_amdgcn_readfirstlane(te.w);
   const bool shared = seg == E;
-  const int seg_row0 = shared ? 0 : p.off[seg];
-  const int seg_rows = shared ? T : p.off[seg + 1] - p.off[seg];
-  const int m0 = (mt - tile_start[seg]) * kBM;
   const moe_nvfp4_bank& bank = shared ? (p.sh2k.codes ? p.sh2k : p.sh2) : (p.w2k.codes ? p.w2k : p.w2);
   const bool km = shared ? p.sh2k.codes != nullptr : p.w2k.codes != nullptr;
   const int64_t erow = shared ? 0 : (int64_t)seg * H;  // the expert's first row in the bank
@@ -409,7 +420,14 @@ bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k) {
          (int64_t)I * H < lim;
 }
 
-size_t ffn_mfma_ws_bytes(int E) { return (size_t)(E + 2) * sizeof(int32_t); }
+static int64_t mfma_max_tiles(int64_t T, int k, int E, int has_shared) {
+  const int64_t P = T * k;
+  return (P + kBM - 1) / kBM + (P < E ? P : E) + (has_shared ? (T + kBM - 1) / kBM : 0);
+}
+
+size_t ffn_mfma_ws_bytes(int E, int64_t T, int k, int has_shared) {
+  return (size_t)tile_tab_offset(E) * sizeof(int32_t) + (size_t)mfma_max_tiles(T, k, E, has_shared) * sizeof(int4);
+}
 
 // K-step-major copy of a bank: thread i moves 16 code bytes (half of one row's
 // K step) or, for i < n_exp S N, one row's 4 scale bytes of a step; both
@@ -445,16 +463,16 @@ hipError_t launch_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int n
 }
 
 hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev) {
-  const int64_t P = (int64_t)p.T * p.k;
-  const int64_t max_tiles = (P + kBM - 1) / kBM + (P < p.E ? P : p.E) + (p.has_shared ? (p.T + kBM - 1) / kBM : 0);
-  hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, p.off, p.E, p.T, p.has_shared, tile_start);
+  const int64_t max_tiles = mfma_max_tiles(p.T, p.k, p.E, p.has_shared);
+  int4* tile_tab = reinterpret_cast<int4*>(tile_start + tile_tab_offset(p.E));
+  hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, p.off, p.E, p.T, p.has_shared, tile_start, tile_tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_timed(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 128))), dim3(256), 0, s, ev ? ev[2] : nullptr,
-                   ev ? ev[3] : nullptr, p, (const int32_t*)tile_start);
+                   ev ? ev[3] : nullptr, p, (const int32_t*)tile_start, (const int4*)tile_tab);
   if (e != hipSuccess) return e;
   return launch_timed(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, ev ? ev[4] : nullptr,
-                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start);
+                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start, (const int4*)tile_tab);
 }
 
 }  // namespace moe
