@@ -5,8 +5,10 @@
 // the kernels are bound by streaming packed NVFP4 bytes from HBM, and with
 // only ~40 experts per call the time is mostly memory latency.  Two choices
 // follow from that:
-//   * each thread holds 16 x 16 B of weight codes plus their scales in
-//     registers, so one round of resident workgroups covers the whole call;
+//   * each gate/up thread holds 16 x 16 B of weight codes plus their scales in
+//     registers (a down-projection thread 8, which doubles the workgroups of
+//     the smaller W2 burst), so one round of resident workgroups covers the
+//     whole call;
 //   * loads are issued in dependency order with nothing else in between:
 //     HIP's vmcnt waits are in order, so a load issued after the weight burst
 //     could not be consumed before the whole burst had arrived.
