@@ -14,16 +14,17 @@
 //
 // Work decomposition: the rows of each expert segment (permuted-row order) are
 // cut into 128-row tiles; a work item is (row tile, column tile).  A small
-// kernel turns expert_off into the prefix of tile counts; each workgroup
-// binary-searches its row tile.  Work items of one column tile sit 8 apart in
-// the grid, so with round-robin workgroup placement they share an XCD and its
-// L2 for the expert's weight slice.
+// kernel turns expert_off into the prefix of tile counts and a table of row
+// tiles; each workgroup reads its row tile from the table.  Workgroups are
+// dealt round robin to the 8 XCDs and each XCD takes one contiguous run of
+// work items, so the column tiles of a row tile and the row tiles of an expert
+// share one L2.
 //
-// G1 (gate/up): 128 rows x (64 gate + 64 up) columns, K = H in steps of 64;
-// wave w computes rows 64*(w/2).. and h columns 32*(w%2).. for both gate and
-// up, so SwiGLU pairs meet in the same lane; the epilogue forms h, encodes its
-// 16-column blocks (amax across the 16 lanes of a DPP row) and stores the
-// dequantized FP16 h.  G2 (down): 128 rows x 128 output columns, K = I.
+// G1 (gate/up): 128 rows x (128 gate + 128 up) columns, K = H in steps of 64;
+// wave w computes all 128 rows and h columns 32 w .. 32 w + 31 for both gate
+// and up, so SwiGLU pairs meet in the same lane; the epilogue forms h, encodes
+// its 16-column blocks and stores the dequantized FP16 h.  G2 (down): 128 rows
+// x 256 output columns, K = I; wave w computes columns 64 w .. 64 w + 63.
 #include "common.hpp"
 
 namespace moe {
@@ -112,27 +113,27 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 
 // A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
-// registers) over K = [k_begin, k_begin + K).  Wave (wm, wn) owns 64 rows x 128
-// B rows as 2 x 4 MFMA tiles.  K is taken in a lane-contiguous order: in MFMA s
+// registers) over K = [k_begin, k_begin + K).  Every wave owns all 128 rows of
+// the tile and 64 B rows as 4 x 2 MFMA tiles, so each B element a wave decodes
+// feeds four MFMAs (the decode is the main loop's largest VALU cost).  K is taken in a lane-contiguous order: in MFMA s
 // (0..3) of a step, lanes 0..31 supply elements 8s..8s+7 and lanes 32..63
 // elements 32+8s..32+8s+7, for A and B alike, so a lane's B codes for the step
 // are one 16-byte half-row (two whole 16-element blocks).  Each wave decodes the
 // B codes it needs after reading them from the ring.  One barrier per step.
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
-// live_rows: rows of the tile inside the expert's segment; a wave skips the
-// MFMAs (and the B decode) of its 32-row blocks that lie wholly past them.
+// live_rows: rows of the tile inside the expert's segment; the waves skip the
+// MFMAs of 32-row blocks that lie wholly past them.
 // kTransposed: the MFMAs take B as their first operand, so acc[i][j] holds the
-// transposed 32 x 32 block (lane l: row 32 i + l % 32 of the wave's rows, B rows
+// transposed 32 x 32 block (lane l: tile row 32 i + l % 32, B rows
 // 8 (q / 4) + 4 (l / 32) + q % 4 of block j in its entries q = 0..15).
 template <bool kTransposed, typename BRow>
 __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, int live_rows, Ring& ring, BRow bj,
-                                         floatx16 (&acc)[2][4]) {
+                                         floatx16 (&acc)[4][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int wm = (wave >> 1) * 64;
   const int n = K / kBK;
   const int hk = lane >> 5;
-  // live 32-row blocks of this wave (wave-uniform: the MFMA loop branches on it once per step, not per MFMA)
-  const int nlive = __builtin_amdgcn_readfirstlane(live_rows <= wm ? 0 : live_rows <= wm + 32 ? 1 : 2);
+  // live 32-row blocks of the tile (wave-uniform)
+  const int nlive = __builtin_amdgcn_readfirstlane(live_rows <= 0 ? 0 : live_rows >= 96 ? 4 : (live_rows + 31) / 32);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
   auto dma = [&](int t, int stage) {
@@ -150,34 +151,36 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   };
   auto compute = [&](int stage) {
     if (nlive == 0) return;
-    uint4 bq[4];
-    half2_t sv[4];
+    uint4 bq[2];
+    half2_t sv[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int r = bj(j) + (lane & 31);
       bq[j] = ring.b[stage][r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
       sv[j] = ue4m3x2_to_half2(ring.s[stage][r] >> (16 * hk));
     }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      half8_t a[2];
+      half8_t a[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm + 32 * i + (lane & 31);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * i + (lane & 31);
         a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const half2_t S = half2_t{sv[j][s4 >> 1], sv[j][s4 >> 1]};
         const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
         const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
         const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-        if (kTransposed) {
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[0], acc[0][j], 0, 0, 0);
-          if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[1], acc[1][j], 0, 0, 0);
-        } else {
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], b, acc[0][j], 0, 0, 0);
-          if (nlive > 1) acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], b, acc[1][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i == 0 || nlive > i) {
+            if (kTransposed)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
+          }
         }
       }
     }
@@ -214,9 +217,9 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 }
 
 // ---------------------------------------------------------------- G1
-// Tile: 128 rows x (128 gate + 128 up) columns; wave (wm, wn) holds h columns
-// nt*128 + wn .. + 63 as gate blocks j = 0, 1 and up blocks j = 2, 3, so SwiGLU
-// pairs (j, j + 2) meet in the same lane.  Dequantized A4(h) of every row goes
+// Tile: 128 rows x (128 gate + 128 up) columns; wave w holds h columns
+// nt*128 + 32 w .. + 31 of all 128 rows as gate block j = 0 and up block j = 1,
+// so SwiGLU pairs meet in the same lane.  Dequantized A4(h) of every row goes
 // to hh (permuted rows, then shared rows); the down GEMM reads it back as its A
 // operand.  Codes and scales are written only to the debug dumps.
 __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
@@ -241,10 +244,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   const uint32_t qrow = km ? 32u : (uint32_t)(H / 2), srow = km ? 4u : (uint32_t)(H / 16);
   const float G = (shared ? p.sh13.gscale[0] : p.w13.gscale[seg]) * p.g_in;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wn = 32 * wave;
   // ring B row r: gate column nt*128 + r (r < 128), up column I + nt*128 + r - 128
   auto wrow = [&](int r) { return (uint32_t)(r < 128 ? nt * 128 + r : I + nt * 128 + (r - 128)); };
-  auto bj = [&](int j) { return j < 2 ? wn + 32 * j : 128 + wn + 32 * (j - 2); };
+  auto bj = [&](int j) { return j == 0 ? wn : 128 + wn; };
   Operands O;
   O.a = buffer_rsrc(p.xh, (uint32_t)T * H * 2u);
 #pragma unroll
@@ -264,10 +267,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   }
   O.sdma = wrow(64 * wave + lane) * srow;
   O.bmul = km ? 2u * I : 1u;
-  floatx16 acc[2][4] = {};
+  floatx16 acc[4][2] = {};
   tile_mma<true>(O, 0, H, seg_rows - m0, ring, bj, acc);
-  // Epilogue.  acc[i][j] is transposed: lane l holds row m = wm + 32 i + l % 32
-  // and h columns c(q) = nt*128 + wn + 32 jg + 8 (q / 4) + 4 (l / 32) + q % 4, so
+  // Epilogue.  acc[i][j] is transposed: lane l holds row m = 32 i + l % 32
+  // and h columns c(q) = nt*128 + wn + 8 (q / 4) + 4 (l / 32) + q % 4, so
   // the first 16-column A4 block of the 32 is entries q < 8 of lanes l and l ^ 32,
   // the second entries q >= 8.  Each lane takes the maxima of its halves, the
   // lane pair completes them, lane l < 32 computes the first block's scale code
@@ -286,16 +289,15 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   auto epilogue = [&](auto dumps_c) {
     constexpr bool kDumps = decltype(dumps_c)::value != 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = wm + 32 * i + (lane & 31);  // tile row
-#pragma unroll
-      for (int jg = 0; jg < 2; ++jg) {
-        const int col0 = nt * 128 + wn + 32 * jg + 4 * hi;  // column of q = 0
+    for (int i = 0; i < 4; ++i) {
+      const int m = 32 * i + (lane & 31);  // tile row
+      {
+        const int col0 = nt * 128 + wn + 4 * hi;  // column of q = 0
         float hv[16];
         uint32_t p0 = 0u, p1 = 0u;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          hv[q] = swiglu_scaled(acc[i][jg][q], acc[i][jg + 2][q], c_exp, inv_g2);
+          hv[q] = swiglu_scaled(acc[i][0][q], acc[i][1][q], c_exp, inv_g2);
           const uint32_t a = __float_as_uint(hv[q]) & 0x7FFFFFFFu;
           if (q < 8) p0 = max(p0, a);
           else p1 = max(p1, a);
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
         const E2M1Thresholds T1 = e2m1_thresholds(sc1 ? u1 * p.g_mid : __builtin_inff());
         const half_t uh0 = (half_t)u0, uh1 = (half_t)u1;  // exact: UE4M3 values
         if (kDumps && p.hs_dbg && m < nrows)
-          p.hs_dbg[(orow0 + m) * (I / 16) + (nt * 128 + wn + 32 * jg) / 16 + hi] = (uint8_t)(hi ? sc1 : sc0);
+          p.hs_dbg[(orow0 + m) * (I / 16) + (nt * 128 + wn) / 16 + hi] = (uint8_t)(hi ? sc1 : sc0);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {  // columns col0 + 8 g .. + 3: entries 4 g .. 4 g + 3
           const E2M1Thresholds& Tg = g < 2 ? T0 : T1;
@@ -347,8 +349,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
 }
 
 // ---------------------------------------------------------------- G2
-// Tile: 128 rows x 256 output columns; wave (wm, wn) holds columns nt*256 + wn ..
-// + 127 as blocks j = 0..3.
+// Tile: 128 rows x 256 output columns; wave w holds columns nt*256 + 64 w ..
+// + 63 of all 128 rows as blocks j = 0, 1.
 __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
                                                       const int4* __restrict__ tile_tab) {
   __shared__ Ring ring;
@@ -371,8 +373,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   const uint32_t qrow = km ? 32u : (uint32_t)(I / 2), srow = km ? 4u : (uint32_t)(I / 16);
   const float G = (shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
-  auto bj = [&](int j) { return wn + 32 * j; };
+  auto bj = [&](int j) { return 64 * wave + 32 * j; };
   // A rows: the tile's rows of hh; rows past the segment read zeros (range check)
   const int64_t row0 = (shared ? (int64_t)T * p.k : (int64_t)seg_row0) + m0;
   const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
@@ -390,17 +391,17 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   }
   O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * srow;
   O.bmul = km ? (uint32_t)H : 1u;
-  floatx16 acc[2][4] = {};
+  floatx16 acc[4][2] = {};
   // K range [kc0, kc1) of I (the full sum: 0, I)
   tile_mma<false>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
   // output rows of the tile through a resource sized to the segment's rows in it
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
-  const uint32_t voff0 = (uint32_t)((wm + 4 * (lane >> 5)) * H) * 4u;
+  const uint32_t voff0 = (uint32_t)(4 * (lane >> 5) * H) * 4u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = nt * kBN + bj(j) + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
