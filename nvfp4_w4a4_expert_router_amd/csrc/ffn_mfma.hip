@@ -121,8 +121,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // are one 16-byte half-row (two whole 16-element blocks).  Each wave decodes the
 // B codes it needs after reading them from the ring.  One barrier per step.
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
-// live_rows: rows of the tile inside the expert's segment; the waves skip the
-// MFMAs of 32-row blocks that lie wholly past them.
+// live_rows: rows of the tile inside the expert's segment; a tile with none
+// skips the step (the MFMAs run on whole 128-row tiles: a branch per MFMA
+// costs more than the padding rows).
 // kTransposed: the MFMAs take B as their first operand, so acc[i][j] holds the
 // transposed 32 x 32 block (lane l: tile row 32 i + l % 32, B rows
 // 8 (q / 4) + 4 (l / 32) + q % 4 of block j in its entries q = 0..15).
@@ -132,8 +133,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int n = K / kBK;
   const int hk = lane >> 5;
-  // live 32-row blocks of the tile (wave-uniform)
-  const int nlive = __builtin_amdgcn_readfirstlane(live_rows <= 0 ? 0 : live_rows >= 96 ? 4 : (live_rows + 31) / 32);
+  const int nlive = __builtin_amdgcn_readfirstlane(live_rows > 0 ? 1 : 0);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
   auto dma = [&](int t, int stage) {
@@ -174,13 +174,11 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
         const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
         const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i == 0 || nlive > i) {
-            if (kTransposed)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
-          }
+        for (int i = 0; i < 4; ++i) {  // blocks past live_rows compute rows that are never stored
+          if (kTransposed)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
         }
       }
     }
