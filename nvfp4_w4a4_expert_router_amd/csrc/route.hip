@@ -340,54 +340,78 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   __shared__ double part[2][kGemvMaxT][2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = q.T, H = q.H, E = q.E;
-  // 1. A4 codes of x (fused): the T*H/16 blocks over the grid's threads
-  if (kFused) {
-    const int64_t nb = (int64_t)T * (H / 16);
-    for (int64_t b = (int64_t)blockIdx.x * 256 + tid; b < nb; b += (int64_t)gridDim.x * 256) {
-      const uint4* src = reinterpret_cast<const uint4*>(q.x + b * 16);
-      const uint4 a0 = src[0], a1 = src[1];
-      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = __uint_as_float(wv[i] << 16);
-        v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
-      }
-      uint2 pk;
-      const uint32_t sc = encode_a4_block16(v, q.g_in, 6.0f * q.g_in, &pk);
-      reinterpret_cast<uint2*>(q.xq)[b] = pk;
-      q.xs[b] = (uint8_t)sc;
-    }
+  // 1. loads in dependency order: this thread's A4 block of x (fused: block
+  // tid * grid + workgroup, so every workgroup encodes a few), then the first
+  // router and x chunks; the encoding runs while the router rows are in flight
+  const int64_t nb = kFused ? (int64_t)T * (H / 16) : 0;
+  const int64_t b = (int64_t)tid * gridDim.x + blockIdx.x;
+  const bool enc = b < nb;
+  uint4 ab[2] = {};
+  if (enc) {
+    const uint4* src = reinterpret_cast<const uint4*>(q.x + b * 16);
+    ab[0] = src[0];
+    ab[1] = src[1];
   }
-  // 2. logits of expert e
+  // logits of expert e: lane L of the expert's wave pair owns elements h0 .. h0 + 15
   const int e = 2 * blockIdx.x + (wave >> 1);
   const int L = kWave * (wave & 1) + lane;
   double acc[kGemvMaxT][2] = {};
-  if (e < E) {
-    for (int h0 = 16 * L; h0 < H; h0 += 2048) {
-      float4 wv[4];
+  float4 wv[4];
+  uint4 xv[kGemvMaxT][2];
+  auto load = [&](int h0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const float4*>(q.W + (int64_t)e * H + h0 + 4 * i);
-      uint4 xv[kGemvMaxT][2];
+    for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const float4*>(q.W + (int64_t)e * H + h0 + 4 * i);
 #pragma unroll
-      for (int t = 0; t < kGemvMaxT; ++t)
-        if (t < T)
+    for (int t = 0; t < kGemvMaxT; ++t)
+      if (t < T)
 #pragma unroll
-          for (int i = 0; i < 2; ++i) xv[t][i] = *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + h0 + 8 * i);
-      const float wf[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
-                            wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
+        for (int i = 0; i < 2; ++i) xv[t][i] = *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + h0 + 8 * i);
+  };
+  auto fma_chunk = [&]() {
+    const float wf[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                          wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
 #pragma unroll
-      for (int t = 0; t < kGemvMaxT; ++t) {
-        if (t < T) {
-          const uint32_t xw[8] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
-                                  xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w};
+    for (int t = 0; t < kGemvMaxT; ++t) {
+      if (t < T) {
+        const uint32_t xw[8] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
+                                xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            acc[t][0] = fma((double)__uint_as_float(xw[i] << 16), (double)wf[2 * i], acc[t][0]);
-            acc[t][1] = fma((double)__uint_as_float(xw[i] & 0xFFFF0000u), (double)wf[2 * i + 1], acc[t][1]);
-          }
+        for (int i = 0; i < 8; ++i) {
+          acc[t][0] = fma((double)__uint_as_float(xw[i] << 16), (double)wf[2 * i], acc[t][0]);
+          acc[t][1] = fma((double)__uint_as_float(xw[i] & 0xFFFF0000u), (double)wf[2 * i + 1], acc[t][1]);
         }
       }
+    }
+  };
+  const bool has = e < E && 16 * L < H;
+  if (has) load(16 * L);
+  // 2. A4 codes of x (fused): blocks b, b + 256 * grid, ... (the first one loaded above)
+  if (kFused && enc) {
+    for (int64_t bb = b; bb < nb; bb += (int64_t)256 * gridDim.x) {
+      if (bb != b) {
+        const uint4* src = reinterpret_cast<const uint4*>(q.x + bb * 16);
+        ab[0] = src[0];
+        ab[1] = src[1];
+      }
+      const uint32_t wb[8] = {ab[0].x, ab[0].y, ab[0].z, ab[0].w, ab[1].x, ab[1].y, ab[1].z, ab[1].w};
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(wb[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wb[i] & 0xFFFF0000u);
+      }
+      uint2 pk;
+      const uint32_t sc = encode_a4_block16(v, q.g_in, 6.0f * q.g_in, &pk);
+      reinterpret_cast<uint2*>(q.xq)[bb] = pk;
+      q.xs[bb] = (uint8_t)sc;
+    }
+  }
+  // 3. the FP64 sums
+  if (has) {
+    fma_chunk();
+    for (int h0 = 16 * L + 2048; h0 < H; h0 += 2048) {
+      load(h0);
+      fma_chunk();
     }
   }
 #pragma unroll
