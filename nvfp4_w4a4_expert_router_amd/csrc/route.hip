@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
 // and group sums the running sum: depth 96 + 8 + H/256.  The terms' absolute
 // sum is at most (1 + 2^-7 + 2^-14) sum_h |x_h W_eh|; the radius takes unit
 // roundoff 2^-23 (any rounding of the MFMA's FP32 adds, not only to nearest).
-constexpr int RM_T = 64, RM_E = 128, RM_K = 32;
+constexpr int RM_T = 256, RM_E = 128, RM_K = 32, RM_S = 3;  // tokens, experts, K step, ring stages
 
 // W [E][H] FP32 -> Wp [3][E][H] BF16 pieces (truncation; exact split)
 __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ W, int64_t n,
@@ -107,24 +107,25 @@ __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ 
   Wp[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-// LDS stage: 64 token rows and 3 x 128 expert rows of a K step (64 B = 4 chunks
+// LDS stage: 256 token rows and 3 x 128 expert rows of a K step (64 B = 4 chunks
 // of 16 B per row; chunk c of row r sits in slot c ^ f(r), f(r) = bit 2 of r plus
 // twice (bit 1 xor bit 3), so the MFMA reads of 16 consecutive rows fall in 16
-// different 16-byte bank groups).  Filled by
-// buffer loads that write LDS directly, one step ahead.
+// different 16-byte bank groups).  A ring of 3 stages (120 KB, one workgroup per
+// CU) filled by buffer loads that write LDS directly, two steps ahead.
 struct RouterRing {
-  uint4 a[2][RM_T * 4];
-  uint4 b[2][3][RM_E * 4];
+  uint4 a[RM_S][RM_T * 4];
+  uint4 b[RM_S][3][RM_E * 4];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 
-// logits[t][e] for a 64-token x 128-expert tile; 4 waves, wave (wt, we) owns
-// tokens 32 wt.. x experts 64 we.. as 2 MFMA tiles.  K order inside a step is
+// logits[t][e] for a 256-token x 128-expert tile; 8 waves, wave w owns tokens
+// 32 w.. x all 128 experts as 4 MFMA tiles (each B fragment read from LDS feeds
+// one MFMA per wave, each A fragment four).  K order inside a step is
 // lane-contiguous (lanes 0..31 supply elements 8s.., lanes 32..63 16+8s.. in
 // MFMA s), the same for both operands.
-__global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ Wp, int T, int H, int E,
                                                             float* __restrict__ logits) {
   __shared__ RouterRing ring;
@@ -134,73 +135,85 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const uint16_t* __re
   const int ntb = (int)gridDim.y;
   const int lt = xcd_tile((int)(blockIdx.y * gridDim.x + blockIdx.x), (int)(gridDim.x * gridDim.y));
   const int t0 = (lt % ntb) * RM_T, e0 = (lt / ntb) * RM_E;
-  const int wt = wave >> 1, we = wave & 1;
   const int n = H / RM_K;
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * H * 2u);
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(Wp, 3u * E * H * 2u);
   // transfers: lane -> row (lane / 4) of a 16-row group, slot lane % 4
   auto swz_of = [](int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); };
   const uint32_t sw = (uint32_t)(((lane & 3) ^ swz_of(lane >> 2)) * 16);
-  const int ta = t0 + 16 * wave + (lane >> 2);
-  const uint32_t aoff = (uint32_t)(ta < T ? ta : T - 1) * H * 2u + sw;  // rows past T repeat the last; dropped
+  uint32_t aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ta = t0 + 32 * wave + 16 * i + (lane >> 2);
+    aoff[i] = (uint32_t)(ta < T ? ta : T - 1) * H * 2u + sw;  // rows past T repeat the last; dropped
+  }
   const uint32_t boff = (uint32_t)(e0 + (lane >> 2)) * H * 2u + sw;
+  // two A and three B transfers per wave and step (steps past the last repeat it)
   auto dma = [&](int t, int st) {
     const uint32_t k0 = (uint32_t)((t < n ? t : n - 1) * RM_K);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&ring.a[st][16 * wave * 4], 16, aoff, k0 * 2, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int q = 6 * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&ring.a[st][(32 * wave + 16 * i) * 4], 16, aoff[i],
+                                               k0 * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int q = 3 * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&ring.b[st][pc][16 * c * 4], 16, boff,
                                                k0 * 2 + (uint32_t)(pc * E + 16 * c) * H * 2u, 0, 0);
     }
   };
-  floatx16 fresh[2], grp[2], run[2];
+  floatx16 fresh[4], grp[4], run[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 4; ++j) {
     grp[j] = floatx16{};
     run[j] = floatx16{};
   }
   const int hk = lane >> 5, r32 = lane & 31;
   const int swz = swz_of(r32);
+  // vmcnt(5): the newest step's transfers may be in flight, the one before is
+  // complete (the barrier then publishes it)
   dma(0, 0);
-  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt 0
+  dma(1, 1);
+  __builtin_amdgcn_s_waitcnt(0xF75);
   __syncthreads();
+  int st = 0;  // t % 3
   for (int t = 0; t < n; ++t) {
-    const int st = t & 1;
-    dma(t + 1, st ^ 1);  // stage st ^ 1 was last read in step t - 1, before the barrier
+    dma(t + 2, st == 0 ? 2 : st - 1);  // stage (t + 2) % 3, last read in step t - 1, before the barrier
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fresh[j] = floatx16{};
+    for (int j = 0; j < 4; ++j) fresh[j] = floatx16{};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int slot = (2 * hk + s2) ^ swz;
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring.a[st][(32 * wt + r32) * 4 + slot]);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring.a[st][(32 * wave + r32) * 4 + slot]);
 #pragma unroll
       for (int pc = 2; pc >= 0; --pc)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ring.b[st][pc][(64 * we + 32 * j + r32) * 4 + slot]);
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ring.b[st][pc][(32 * j + r32) * 4 + slot]);
           fresh[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, fresh[j], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) grp[j] += fresh[j];
+    for (int j = 0; j < 4; ++j) grp[j] += fresh[j];
     if ((t & 7) == 7 || t == n - 1) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
         run[j] += grp[j];
         grp[j] = floatx16{};
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xF70);  // this wave's transfers for step t + 1 are complete
+    __builtin_amdgcn_s_waitcnt(0xF75);  // this wave's transfers for step t + 1 are complete
     __syncthreads();
+    st = st == 2 ? 0 : st + 1;
   }
-  // lane holds experts 64 we + 32 j + lane % 32 of tokens 8 (q / 4) + 4 (lane / 32) + q % 4
+  __builtin_amdgcn_s_waitcnt(0xF70);  // no transfer into LDS outlives the loop
+  // lane holds experts 32 j + lane % 32 of tokens 32 w + 8 (q / 4) + 4 (lane / 32) + q % 4
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = e0 + 64 * we + 32 * j + r32;
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 32 * j + r32;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int tt = t0 + 32 * wt + 8 * (q >> 2) + 4 * hk + (q & 3);
+      const int tt = t0 + 32 * wave + 8 * (q >> 2) + 4 * hk + (q & 3);
       if (tt < T) logits[(int64_t)tt * E + e] = run[j][q];
     }
   }
@@ -843,7 +856,7 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
       const int64_t nw = (int64_t)E * H;
       hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
       const dim3 grid((unsigned)(E / RM_E), (unsigned)((T + RM_T - 1) / RM_T));
-      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(256), 0, s, x, (const uint16_t*)wp, (int)T, H, E, lg);
+      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(512), 0, s, x, (const uint16_t*)wp, (int)T, H, E, lg);
       // u = 2^-23 (twice the FP32 unit roundoff), and the pieces' 1 + 2^-7 + 2^-14
       p.gamma = 2.0f * gamma_for_depth(3 * 2 * 16 + 8 + (H / RM_K + 7) / 8) * (1.0f + 0x1p-6f);
     } else {
