@@ -82,9 +82,10 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
 // c ^ (r % 8) ^ (r / 8 % 2), so that the MFMA reads of 16 consecutive rows hit 16
 // different 16-byte bank groups), the step's 32 B of codes of each of the 256 B
 // rows (two 16-byte halves; half h of row r sits in slot h ^ (r / 4 % 2) ^
-// (r / 8 % 2), for the same reason) and the step's four UE4M3 scales of each B row.  All of it arrives by buffer loads that write LDS
-// directly (64 lanes x 16 B per transfer: 8 A rows or 32 B rows; 64 lanes x 4 B:
-// 64 scale words), so the ring costs no registers and is filled 2 steps ahead.
+// (r / 8 % 2), for the same reason) and the step's four UE4M3 scales of each B
+// row.  All of it arrives by buffer loads that write LDS directly (64 lanes x
+// 16 B per transfer: 8 A rows or 32 B rows; 64 lanes x 4 B: 64 scale words), so
+// the ring costs no registers and is filled 2 steps ahead.
 constexpr int kStages = 3;
 struct Ring {
   uint4 a[kStages][kBM * 8];
@@ -92,9 +93,9 @@ struct Ring {
   uint32_t s[kStages][kBN];
 };
 
-// One operand set: buffer resources and per-lane byte offsets (a K step at element
-// k0 adds 2 k0 for A, bmul k0 / 2 for B codes and bmul k0 / 16 for B scales as wave-uniform
-// offsets).  adma[c] / bdma[c]: the row (and swizzled chunk) this lane moves in
+// One operand set: buffer resources and per-lane byte offsets (a K step at
+// element k0 adds 2 k0 for A, bmul k0 / 2 for B codes and bmul k0 / 16 for B
+// scales as wave-uniform offsets).  adma[c] / bdma[c]: the row (and swizzled chunk) this lane moves in
 // the wave's c-th A / B transfer; sdma: the B row whose scales this lane moves.
 struct Operands {
   __amdgpu_buffer_rsrc_t a, bq, bs;
@@ -108,17 +109,16 @@ struct Operands {
 // of one wave transfer are one contiguous 1 KB run instead of 32 separate
 // lines; the expert's block has the same size and offset in both.
 
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 
 // A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
 // registers) over K = [k_begin, k_begin + K).  Every wave owns all 128 rows of
 // the tile and 64 B rows as 4 x 2 MFMA tiles, so each B element a wave decodes
-// feeds four MFMAs (the decode is the main loop's largest VALU cost).  K is taken in a lane-contiguous order: in MFMA s
-// (0..3) of a step, lanes 0..31 supply elements 8s..8s+7 and lanes 32..63
-// elements 32+8s..32+8s+7, for A and B alike, so a lane's B codes for the step
-// are one 16-byte half-row (two whole 16-element blocks).  Each wave decodes the
+// feeds four MFMAs (the decode is the main loop's largest VALU cost).  K is
+// taken in a lane-contiguous order: in MFMA s (0..3) of a step, lanes 0..31
+// supply elements 8s..8s+7 and lanes 32..63 elements 32+8s..32+8s+7, for A and
+// B alike, so a lane's B codes for the step are one 16-byte half-row (two whole
+// 16-element blocks).  Each wave decodes the
 // B codes it needs after reading them from the ring.  One barrier per step.
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
 // live_rows: rows of the tile inside the expert's segment; a tile with none
@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
           if (kDumps && m < nrows) {
             const int64_t orow = orow0 + m;
             const int c = col0 + 8 * g;
-            if (p.hq_dbg) *reinterpret_cast<uint16_t*>(p.hq_dbg + orow * (I / 2) + c / 2) = (uint16_t)(by[0] | by[1] << 8);
+            if (p.hq_dbg)
+              *reinterpret_cast<uint16_t*>(p.hq_dbg + orow * (I / 2) + c / 2) = (uint16_t)(by[0] | by[1] << 8);
             if (p.h_dbg)
 #pragma unroll
               for (int e = 0; e < 4; ++e) p.h_dbg[orow * I + c + e] = hv[4 * g + e];
@@ -379,7 +380,8 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)nrows * I * 2u);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u + (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
+    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u +
+                (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
   O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
   O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
 #pragma unroll

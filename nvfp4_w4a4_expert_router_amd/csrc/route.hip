@@ -770,7 +770,8 @@ __global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
     for (int c = 0; c < 4; ++c) e4[c] = (int)ts[wave].key[c0 + c < nc ? c0 + c : c0];
     double d4[4];
     dot64x4(xr, p.W, H, e4, lane, d4);
-    if (lane < 4 && c0 + lane < nc) ts[wave].val[c0 + lane] = lane == 0 ? d4[0] : lane == 1 ? d4[1] : lane == 2 ? d4[2] : d4[3];
+    if (lane < 4 && c0 + lane < nc)
+      ts[wave].val[c0 + lane] = lane == 0 ? d4[0] : lane == 1 ? d4[1] : lane == 2 ? d4[2] : d4[3];
   }
   wave_sync_lds();
   // final top k among the candidates (lane owns candidates lane + 64 q)
