@@ -234,6 +234,13 @@ __device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
 }
 
+// The same with the non-temporal cache policy (bit 1 of the policy operand on
+// this chip family: `nt`): for output written once and read much later, so it
+// does not displace operands that are being reused in L2.
+__device__ __forceinline__ void buffer_store4_nt(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 2);
+}
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void buffer_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);

@@ -395,6 +395,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   // K range [kc0, kc1) of I (the full sum: 0, I)
   tile_mma<false>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
   // output rows of the tile through a resource sized to the segment's rows in it
+  // (non-temporal: the combine reads them after every tile is done)
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
   const uint32_t voff0 = (uint32_t)(4 * (lane >> 5) * H) * 4u;
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int dm = 32 * i + 8 * (q >> 2) + (q & 3);
-        buffer_store4(__float_as_uint(G * acc[i][j][q]), y_r, voff0 + (uint32_t)(dm * H * 4) + (uint32_t)(n * 4));
+        buffer_store4_nt(__float_as_uint(G * acc[i][j][q]), y_r, voff0 + (uint32_t)(dm * H * 4) + (uint32_t)(n * 4));
       }
     }
 }
