@@ -270,7 +270,8 @@ struct RoutingLds {
   unsigned int tmask[kRdMaxE];  // tokens that chose expert e (bit t)
   int off[kRdMaxE + 1];
   int nzr[kRdMaxE];  // experts with pairs and a smaller id (slot of the expert)
-  int n_slots;
+  int4 slot[kRdMaxT * 32];  // slot table, written out after the last barrier
+  int wsum[4], wnz[4];      // per-wave totals of the scan
 };
 
 // The routing of all T tokens in one workgroup (wave t takes token t).  Rows
@@ -291,58 +292,65 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
   }
   for (int e = tid; e < E; e += 256) R.tmask[e] = 0u;
   __syncthreads();
+  // global outputs are written after the last barrier: a barrier here also
+  // waits for this wave's outstanding stores
   int my_e = 0;
+  float my_w = 0.0f;
   if (wave < T) {
     double my_v = 0.0;
     wave_topk512(v, id, k, R.ts[wave], &my_v, &my_e);
-    const float wk = topk_softmax_weight(my_v, k);
-    if (lane < k) {
-      atomicOr(&R.tmask[my_e], 1u << wave);
-      q.idx[wave * k + lane] = my_e;
-      q.w[wave * k + lane] = wk;
-    }
+    my_w = topk_softmax_weight(my_v, k);
+    if (lane < k) atomicOr(&R.tmask[my_e], 1u << wave);
   }
   __syncthreads();
-  if (wave == 0) {  // scan: lane l owns experts [8l, 8l + 8)
-    unsigned int tm[8];
-    int c[8], sc = 0, snz = 0;
+  // scan over the experts, thread tid owning experts 2 tid and 2 tid + 1 (E <=
+  // 512): pair counts and nonzero counts, wave scans, then the wave totals
+  unsigned int tm[2];
+  int c[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane * 8 + j;
-      tm[j] = e < E ? R.tmask[e] : 0u;
-      c[j] = __popc(tm[j]);
-      sc += c[j];
-      snz += c[j] > 0;
-    }
-    const int ic = wave_incl_scan_i32(sc), inz = wave_incl_scan_i32(snz);
-    int rc = ic - sc, rnz = inz - snz;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane * 8 + j;
-      if (e < E) {
-        R.off[e] = rc;
-        R.nzr[e] = rnz;
-      }
-      // slot entry: expert, first row, rows, tokens (one byte each, ascending);
-      // at most 4 tokens (bits of tm), peeled without a loop
-      const unsigned int t1 = tm[j] & (tm[j] - 1u), t2 = t1 & (t1 - 1u), t3 = t2 & (t2 - 1u);
-      auto low = [](unsigned int t) { return t ? (unsigned)(__ffs(t) - 1) : 0u; };  // bytes past the count: 0
-      const unsigned int toks = low(tm[j]) | low(t1) << 8 | low(t2) << 16 | low(t3) << 24;
-      if (c[j] > 0) q.slot_tab[rnz] = make_int4(e, rc, c[j], (int)toks);
-      rc += c[j];
-      rnz += c[j] > 0;
-    }
-    if (lane == 63) {
-      R.off[E] = ic;
-      R.n_slots = inz;
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int e = 2 * tid + j;
+    tm[j] = e < E ? R.tmask[e] : 0u;
+    c[j] = __popc(tm[j]);
   }
+  const int sc = c[0] + c[1], snz = (c[0] > 0) + (c[1] > 0);
+  const int ic = wave_incl_scan_i32(sc), inz = wave_incl_scan_i32(snz);
+  if (lane == kWave - 1) {
+    R.wsum[wave] = ic;
+    R.wnz[wave] = inz;
+  }
+  __syncthreads();
+  int rc = ic - sc, rnz = inz - snz;
+  for (int w = 0; w < wave; ++w) {
+    rc += R.wsum[w];
+    rnz += R.wnz[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = 2 * tid + j;
+    if (e < E) {
+      R.off[e] = rc;
+      R.nzr[e] = rnz;
+    }
+    // slot entry: expert, first row, rows, tokens (one byte each, ascending);
+    // at most 4 tokens (bits of tm), peeled without a loop
+    const unsigned int t1 = tm[j] & (tm[j] - 1u), t2 = t1 & (t1 - 1u), t3 = t2 & (t2 - 1u);
+    auto low = [](unsigned int t) { return t ? (unsigned)(__ffs(t) - 1) : 0u; };  // bytes past the count: 0
+    const unsigned int toks = low(tm[j]) | low(t1) << 8 | low(t2) << 16 | low(t3) << 24;
+    if (c[j] > 0) R.slot[rnz] = make_int4(e, rc, c[j], (int)toks);
+    rc += c[j];
+    rnz += c[j] > 0;
+  }
+  if (tid == 255) R.off[E] = rc;  // the last thread's running count is the total
   __syncthreads();
   for (int e = tid; e <= E; e += 256) q.off[e] = R.off[e];
-  for (int s = R.n_slots + tid; s < P; s += 256) q.slot_tab[s] = make_int4(-1, 0, 0, 0);
+  const int n_slots = R.wnz[0] + R.wnz[1] + R.wnz[2] + R.wnz[3];
+  for (int s = tid; s < P; s += 256) q.slot_tab[s] = s < n_slots ? R.slot[s] : make_int4(-1, 0, 0, 0);
   if (wave < T && lane < k) {
     const int pi = wave * k + lane;
     const int row = R.off[my_e] + __popc(R.tmask[my_e] & ((1u << wave) - 1u));
+    q.idx[pi] = my_e;
+    q.w[pi] = my_w;
     q.p2r[pi] = row;
     q.r2p[row] = pi;
   }
