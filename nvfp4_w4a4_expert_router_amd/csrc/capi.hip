@@ -115,9 +115,11 @@ const char* moe_strerror(int code) {
 
 // FP64 logits and the slot table of the fused decode path sit before the
 // expert-FFN workspace
+// fused decode path: FP64 logits, slot table, token-major copy of the routed output rows
 size_t fused_logits_ws(const moe_layer* L, int64_t T) {
   const int64_t t = T < 4 ? T : 4;
-  return align_up((size_t)t * L->E * sizeof(double)) + align_up((size_t)t * L->k * sizeof(int4));
+  return align_up((size_t)t * L->E * sizeof(double)) + align_up((size_t)t * L->k * sizeof(int4)) +
+         align_up((size_t)t * L->k * L->H * sizeof(float));
 }
 
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
@@ -383,9 +385,13 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.shared_split = 1;
   p.kc0 = 0;
   p.kc1 = L->I;
+  // the down kernel also writes the routed rows in token-major order, so the
+  // combine reads them without the dependent pair2row load (same values)
+  p.y_tok = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +
+                                     align_up((size_t)T * L->k * sizeof(int4)));
   if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
   if ((rc = launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr)))) return rc;
-  return launch_rc(launch_combine(T, L->H, L->k, y_rows, p.y_shared, pair2row, topk_w, residual, out, stream));
+  return launch_rc(launch_combine(T, L->H, L->k, p.y_tok, p.y_shared, nullptr, topk_w, residual, out, stream));
 }
 
 int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* out, hipStream_t stream) {

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
-      r[j] = p2r[t * k + j];
+      r[j] = p2r ? p2r[t * k + j] : t * k + j;  // no map: the rows are in token-major order
       wj[j] = w[t * k + j];
     }
   }

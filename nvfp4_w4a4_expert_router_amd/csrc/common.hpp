@@ -497,6 +497,7 @@ struct FfnParams {
   const half_t* xh;   // [T][H] dequantized A4(x) without a_gscale_in (generic kernels)
   moe_nvfp4_bank w13, w2, sh13, sh2;
   moe_nvfp4_bank w13k, w2k, sh13k, sh2k;  // K-step-major copies (codes null: absent)
+  float* y_tok;  // decode: optional copy of the routed output rows in token-major (pair) order
   float g_in, g_mid;
   half_t* hh;  // [R][I] dequantized A4(h) without a_gscale_mid; R = T*k (+ T)
   float* h_dbg;

@@ -328,6 +328,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
   const float G = gsc * p.g_mid;
   float* dst0 = shared ? p.y_shared + (int64_t)row0 * H : p.y_rows + (int64_t)row0 * H;
+  // pair ids of the slot's rows for the token-major copy (loaded with the burst in flight)
+  int pair[kDecMaxT] = {};
+  const bool tok_copy = p.y_tok != nullptr && !shared;
+  if (tok_copy)
+#pragma unroll
+    for (int rr = 0; rr < kDecMaxT; ++rr)
+      if (rr < nrows) pair[rr] = p.row2pair[row0 + rr];
   for (int rr = 0; rr < nrows; ++rr) {
     if (rr > 0) {
       const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + (hrow0 + rr) * I + ch * 32);
@@ -348,7 +355,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
       for (int i = 0; i < kKeep; ++i) {
         const int n = base_n + kRPI * (w + 4 * (jb + i));
-        if (n < H) dst0[(int64_t)rr * H + n] = G * acc[i];
+        if (n < H) {
+          dst0[(int64_t)rr * H + n] = G * acc[i];
+          if (tok_copy) {
+            int pr = pair[0];
+#pragma unroll
+            for (int r2 = 1; r2 < kDecMaxT; ++r2) pr = rr == r2 ? pair[r2] : pr;
+            p.y_tok[(int64_t)pr * H + n] = G * acc[i];
+          }
+        }
       }
     }
   }
