@@ -242,6 +242,7 @@ __device__ __forceinline__ void buffer_store4_nt(uint32_t v, __amdgpu_buffer_rsr
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;  // LDS destination of buffer-to-LDS loads
 __device__ __forceinline__ void buffer_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }

@@ -161,6 +161,7 @@ template <bool kTable>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
   constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
   __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
+  __shared__ __align__(16) uint8_t sct[4][kJ][128];      // each wave's rows' block scales (H/16 bytes)
   __shared__ float gu[kDecMaxT][2 * kGuCols];
   __shared__ int toks[kDecMaxT];
   const int H = p.H, I = p.I, T = p.T;
@@ -207,22 +208,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const uint32_t qrow = (uint32_t)H / 2, srow = (uint32_t)H / 16;
   const auto rq = buffer_rsrc(bcodes + (int64_t)e * 2 * I * qrow, 2u * I * qrow);
   const auto rs = buffer_rsrc(bscales + (int64_t)e * 2 * I * srow, 2u * I * srow);
+  // j < kJ/2: gate column cg*kGuCols + w + 4j; j >= kJ/2: up column w + 4(j - kJ/2) (+ I)
+  auto rowoff = [&](int j) { return j < kJ / 2 ? (uint32_t)(4 * j) : (uint32_t)I + 4u * (j - kJ / 2); };
+  // the scales of the wave's kJ rows go to LDS first, by transfers of 8 rows
+  // (8 lanes x 16 B per row; bytes past a row's H/16 are never read): 2-byte
+  // loads per lane and row would cost a load instruction each
+#pragma unroll
+  for (int c = 0; c < kJ / 8; ++c) {
+    const int j = 8 * c + (l >> 3);
+    const uint32_t voff = ((uint32_t)(cg * kGuCols + w) + rowoff(j)) * srow + (uint32_t)(l & 7) * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&sct[w][8 * c][0], 16, voff, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the code burst is issued after the scale transfers
   // lanes past the row's chunks read past the buffer: zeros
   const uint32_t vq = l < nch ? (uint32_t)(cg * kGuCols + w) * qrow + l * 16u : 0x80000000u;
-  const uint32_t vs = l < nch ? (uint32_t)(cg * kGuCols + w) * srow + l * 2u : 0x80000000u;
   uint4 q[kJ];
-  uint32_t sc[kJ];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    // j < kJ/2: gate column cg*kGuCols + w + 4j; j >= kJ/2: up column w + 4(j - kJ/2) (+ I)
-    const uint32_t rowoff = j < kJ / 2 ? (uint32_t)(4 * j) : (uint32_t)I + 4u * (j - kJ / 2);
-    q[j] = buffer_load16(rq, vq, rowoff * qrow);
-    sc[j] = buffer_load2(rs, vs, rowoff * srow);
-  }
+  for (int j = 0; j < kJ; ++j) q[j] = buffer_load16(rq, vq, rowoff(j) * qrow);
+  __builtin_amdgcn_sched_barrier(0);
   const float G = gsc * p.g_in;
   // 3. A4(x) to FP16 in LDS while the weights are in flight
   if (xmine) decode32_fp16(xq4, xs2, xs + (size_t)xt * H + xc * 32);
   if (tid < nrows) toks[tid] = shared ? row0 + tid : kTable ? (int)(((unsigned)ent.w >> (8 * tid)) & 0xFFu) : tok;
+  // the scale transfers are complete once at most the kJ code loads are in flight
+  static_assert(kJ == 16, "vmcnt immediate below");
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16, expcnt 7, lgkmcnt 15
+  uint32_t sc[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) sc[j] = *reinterpret_cast<const uint16_t*>(&sct[w][j][2 * l]);
   __syncthreads();
   // 4. dot products, one activation row at a time
   for (int rr = 0; rr < nrows; ++rr) {

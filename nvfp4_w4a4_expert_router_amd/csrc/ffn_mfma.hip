@@ -109,8 +109,6 @@ struct Operands {
 // of one wave transfer are one contiguous 1 KB run instead of 32 separate
 // lines; the expert's block has the same size and offset in both.
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // A (FP16 activation rows) x B (weight rows, NVFP4 codes decoded to FP16 in
 // registers) over K = [k_begin, k_begin + K).  Every wave owns all 128 rows of
 // the tile and 64 B rows as 4 x 2 MFMA tiles, so each B element a wave decodes

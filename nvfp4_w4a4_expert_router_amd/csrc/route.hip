@@ -117,7 +117,6 @@ struct RouterRing {
   uint4 b[RM_S][3][RM_E * 4];
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 
 // logits[t][e] for a 256-token x 128-expert tile; 8 waves, wave w owns tokens
