@@ -330,15 +330,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const uint32_t qrow = (uint32_t)I / 2, srow = (uint32_t)I / 16;
   const auto rq = buffer_rsrc(bcodes + (int64_t)e * H * qrow, (uint32_t)H * qrow);
   const auto rs = buffer_rsrc(bscales + (int64_t)e * H * srow, (uint32_t)H * srow);
+  // the scales of the wave's rows first: load j covers kRPI consecutive rows,
+  // whose scales are one 128-byte run (kRPI rows x 2 kLPR bytes); the kJ runs
+  // go to LDS by one transfer (8 lanes x 16 B per run), and lane l's two bytes
+  // of run j sit at byte 2 l (l = row in the run x kLPR + chunk)
+  static_assert(kJ * 8 == kWave, "one 16-byte piece per lane");
+  __shared__ __align__(16) uint8_t sct[4][kJ][128];
+  {
+    const uint32_t run0 = (uint32_t)(nb * kRowsWG + kRPI * (w + 4 * (l >> 3)));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&sct[w][0][0], 16, run0 * srow + (uint32_t)(l & 7) * 16u,
+                                             0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the code burst is issued after the scale transfer
   const uint32_t n_lane = (uint32_t)(base_n + kRPI * w);
-  const uint32_t vq = n_lane * qrow + ch * 16u, vs = n_lane * srow + ch * 2u;
+  const uint32_t vq = n_lane * qrow + ch * 16u;
   uint4 q[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)  // rows past H read past the buffer: zeros
+    q[j] = buffer_load16(rq, vq, (uint32_t)(4 * kRPI * j) * qrow);
+  __builtin_amdgcn_sched_barrier(0);
+  // the scale transfer is complete once at most the kJ code loads are in flight
+  static_assert(kJ == 8, "vmcnt immediate below");
+  __builtin_amdgcn_s_waitcnt(0xF78);  // vmcnt 8, expcnt 7, lgkmcnt 15
   uint32_t sc[kJ];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) {  // rows past H read past the buffer: zeros
-    q[j] = buffer_load16(rq, vq, (uint32_t)(4 * kRPI * j) * qrow);
-    sc[j] = buffer_load2(rs, vs, (uint32_t)(4 * kRPI * j) * srow);
-  }
+  for (int j = 0; j < kJ; ++j) sc[j] = *reinterpret_cast<const uint16_t*>(&sct[w][j][2 * l]);
   const float G = gsc * p.g_mid;
   float* dst0 = shared ? p.y_shared + (int64_t)row0 * H : p.y_rows + (int64_t)row0 * H;
   // pair ids of the slot's rows for the token-major copy (loaded with the burst in flight)
