@@ -1,6 +1,7 @@
 """Reduced-precision prompt routers on the matrix cores, measured against exact
-routing (capy-flash README v0.7.7, "Benchmarks": the prompt router on tensor cores
-sums in another order and can pick another expert where two are tied).
+routing (capy-flash README v0.5.4, "Measured": moving the prompt router onto the
+matrix units changes the order of its sums, so a near tie between two experts can
+resolve the other way).
 
 On the 15,360-token chunk (Zipf-skewed router), three routers pick the top 10 of
 512 experts per token:
