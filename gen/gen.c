@@ -6,8 +6,8 @@
  * products, combine).  It only draws random numbers and turns FP64 weight
  * draws into a packed NVFP4 checkpoint, the form in which the layer receives
  * its expert weights (capy-flash README, "Model weights": the NVFP4 experts
- * are used as published, not re-quantized; the layer itself never encodes a
- * weight).
+ * come from NVIDIA's checkpoint unchanged, with no second quantization pass;
+ * the layer itself never encodes a weight).
  *
  * Random numbers: SplitMix64 (Steele, Lea and Flood, 2014) used as a
  * counter-based generator.  Output i of stream `key` is the SplitMix64

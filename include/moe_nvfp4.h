@@ -7,7 +7,8 @@
  *     shared expert (capy-flash README v0.5.4, synthetic test-artifact script:
  *     "512 NVFP4 experts top-10 + shared"; Richland article, "What shipped");
  *   - expert weights in NVFP4: E2M1 codes, UE4M3 block scales, an FP32
- *     per-expert scale, used as published (Richland article, "What shipped");
+ *     per-expert scale, taken from the checkpoint unchanged (Richland
+ *     article, "What shipped");
  *   - activations quantized the same way (W4A4) wherever an expert runs
  *     (capy-flash README v0.5.4, "What it does" and "Serve");
  *   - FP32 accumulation of partials (Richland article, "Why it matters");

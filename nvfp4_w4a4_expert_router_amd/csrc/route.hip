@@ -2,7 +2,8 @@
 // selected logits (512 experts, top-10 routed: capy-flash README v0.5.4,
 // synthetic test-artifact script; Richland article, "What shipped").
 //
-// A sum in another order can pick the other of two nearly tied experts
+// Changing the summation order of a logit can swap which of two almost equal
+// experts makes the top k
 // (capy-flash README v0.5.4, "Measured", footnote on the tensor-core router).
 // To make the decision independent of the summation order, the selection is
 // taken on FP64 logits, computed only where they matter:

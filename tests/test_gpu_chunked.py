@@ -8,7 +8,7 @@ rows.  Every chunk of at least 32 tokens takes the same kernels (matrix-core
 router with exact FP64 refinement, matrix-core expert GEMMs), whose sums for one
 output do not depend on where its row sits in a tile, so the chunked outputs must
 equal the single call's bit for bit.  (Chunks under 32 tokens take the weight-
-streaming or decode kernels, which sum in another order; they are not compared
+streaming or decode kernels, which order their sums differently; they are not compared
 here.)  The single call is checked against the oracle on sampled tokens.
 """
 import time
