@@ -132,7 +132,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   const int n = K / kBK;
   const int hk = lane >> 5;
   const int nlive = __builtin_amdgcn_readfirstlane(live_rows > 0 ? 1 : 0);
-  auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // repeats the last step
+  auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // n = 1: the prologue repeats step 0
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
   auto dma = [&](int t, int stage) {
     const uint32_t k0 = kof(t);
@@ -192,14 +192,19 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
   // step t: transfers for step t + 2 into stage (t + 2) % 3 (last read in step
-  // t - 1, before the previous barrier), then the MFMAs of step t
+  // t - 1, before the previous barrier), then the MFMAs of step t.  The last
+  // two steps issue no transfers and wait for all of theirs instead.
   auto phase = [&](auto pc, int t) {
     constexpr int P = decltype(pc)::value;  // t % 3
-    dma(t + 2, (P + 2) % kStages);
+    const bool more = t + 2 < n;  // uniform
+    if (more) dma(t + 2, (P + 2) % kStages);
     __builtin_amdgcn_sched_barrier(0);
     compute(P);
     __builtin_amdgcn_sched_barrier(0);
-    wait_ring();
+    if (more)
+      wait_ring();
+    else
+      __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt 0, expcnt 7, lgkmcnt 15
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
