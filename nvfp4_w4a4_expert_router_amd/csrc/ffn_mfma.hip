@@ -120,12 +120,19 @@ struct Operands {
 // B codes it needs after reading them from the ring.  One barrier per step.
 // bj(j): the ring's B row index of the wave's column block j (lane % 32 added).
 // live_rows: rows of the tile inside the expert's segment; a tile with none
-// skips the step (the MFMAs run on whole 128-row tiles: a branch per MFMA
-// costs more than the padding rows).
+// skips the step.  kRB: 32-row blocks computed (the caller instantiates one
+// variant per block count, so a segment's last tile runs only the blocks that
+// hold its rows without a branch per MFMA; blocks past kRB keep their zeros).
 // kTransposed: the MFMAs take B as their first operand, so acc[i][j] holds the
 // transposed 32 x 32 block (lane l: tile row 32 i + l % 32, B rows
 // 8 (q / 4) + 4 (l / 32) + q % 4 of block j in its entries q = 0..15).
-template <bool kTransposed, typename BRow>
+// 32-row blocks holding a tile's live rows (1..4; 4 when the segment continues
+// past the tile)
+__device__ __forceinline__ int tile_blocks(int live_rows) {
+  return live_rows >= kBM ? 4 : live_rows <= 32 ? 1 : (live_rows + 31) / 32;
+}
+
+template <bool kTransposed, int kRB, typename BRow>
 __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, int live_rows, Ring& ring, BRow bj,
                                          floatx16 (&acc)[4][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
@@ -161,7 +168,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
     for (int s4 = 0; s4 < 4; ++s4) {
       half8_t a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kRB; ++i) {
         const int row = 32 * i + (lane & 31);
         a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
       }
@@ -172,7 +179,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
         const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
         const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // blocks past live_rows compute rows that are never stored
+        for (int i = 0; i < kRB; ++i) {  // rows past live_rows in a block are computed, never stored
           if (kTransposed)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
           else
@@ -269,7 +276,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   O.sdma = wrow(64 * wave + lane) * srow;
   O.bmul = km ? 2u * I : 1u;
   floatx16 acc[4][2] = {};
-  tile_mma<true>(O, 0, H, seg_rows - m0, ring, bj, acc);
+  switch (tile_blocks(seg_rows - m0)) {
+    case 1: tile_mma<true, 1>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
+    case 2: tile_mma<true, 2>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
+    case 3: tile_mma<true, 3>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
+    default: tile_mma<true, 4>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
+  }
   // Epilogue.  acc[i][j] is transposed: lane l holds row m = 32 i + l % 32
   // and h columns c(q) = nt*128 + wn + 8 (q / 4) + 4 (l / 32) + q % 4, so
   // the first 16-column A4 block of the 32 is entries q < 8 of lanes l and l ^ 32,
@@ -396,7 +408,12 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   O.bmul = km ? (uint32_t)H : 1u;
   floatx16 acc[4][2] = {};
   // K range [kc0, kc1) of I (the full sum: 0, I)
-  tile_mma<false>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc);
+  switch (tile_blocks(nrows)) {
+    case 1: tile_mma<false, 1>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
+    case 2: tile_mma<false, 2>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
+    case 3: tile_mma<false, 3>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
+    default: tile_mma<false, 4>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
+  }
   // output rows of the tile through a resource sized to the segment's rows in it
   // (non-temporal: the combine reads them after every tile is done)
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
