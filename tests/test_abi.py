@@ -173,3 +173,20 @@ def test_krange_validation():
         assert moe.lib.moe_expert_ffn_krange(*args(kb0, kb1)) == moe.MOE_ESHAPE, (kb0, kb1)
     assert moe.lib.moe_combine_f32(ctypes.byref(L), -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ESHAPE
     assert moe.lib.moe_combine_f32(ctypes.byref(L), 4, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+
+
+def test_package_refuses_to_load_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the binding next to no built library raises
+    ImportError on import (checked in a fresh interpreter)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "nvfp4_w4a4_expert_router_amd", "__init__.py")
+    pkg = tmp_path / "nvfp4_w4a4_expert_router_amd"
+    pkg.mkdir()
+    shutil.copy(src, pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import nvfp4_w4a4_expert_router_amd\nexcept ImportError as e:\n    print('refused:', e)\n"
+            "else:\n    print('loaded')\n") % str(tmp_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert "refused:" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
