@@ -122,7 +122,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this layer is built and measured on a single MI355X "
-              "(expert parallelism across GPUs is a design note, not part of this build); use --gpus 1.",
+              "(expert parallelism across GPUs is designed but not implemented); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
