@@ -342,3 +342,23 @@ def test_kmajor_copies_give_identical_results(cfg, T):
         torch.cuda.synchronize()
         outs.append((buf.y_rows.cpu().numpy(), buf.y_shared.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("first", [0, 502])
+def test_layer_all_tokens_on_ten_experts(first):
+    """Routing forced through logits_in: every token picks experts first..first+9
+    (weights of logits 8, 7, ..., -1), so each of the ten segments holds all 4,096
+    rows (32 row tiles of one expert) next to the shared expert's; first = 502
+    puts the last expert id, 511, in play.  Sampled tokens against the oracle."""
+    cfg, T = 2, 4096
+    gh.log("case: config %d T=%d, all tokens on experts %d..%d" % (cfg, T, first, first + 9))
+    L, DL = layer_for(cfg)
+    E, k = L.shape.E, L.shape.k
+    lg = np.full((T, E), -100.0, np.float32)
+    lg[:, first:first + k] = np.arange(8, 8 - k, -1, dtype=np.float32)
+    x = gen.make_tokens(cfg, T, step=88)
+    g = gh.run_layer(DL, x, logits_in=lg)
+    counts = np.diff(g["off"])
+    assert np.all(counts[first:first + k] == T) and counts.sum() == T * k
+    rep = gh.check_layer(L, x, g, tokens=sample_tokens(T, 32, first), logits64=lg.astype(np.float64))
+    gh.log("  ", rep.line())
