@@ -362,3 +362,24 @@ def test_layer_all_tokens_on_ten_experts(first):
     assert np.all(counts[first:first + k] == T) and counts.sum() == T * k
     rep = gh.check_layer(L, x, g, tokens=sample_tokens(T, 32, first), logits64=lg.astype(np.float64))
     gh.log("  ", rep.line())
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_decode_identical_tokens_share_every_expert(T):
+    """T identical tokens at decode: every selected expert serves all T rows (the
+    multi-row paths of the slot table and of the decode kernels).  The fused call
+    equals the four separate calls bit for bit, every token's output is the same,
+    and the separate calls are checked against the oracle."""
+    gh.log("case: config 1, %d identical tokens" % T)
+    L, DL = layer_for(1)
+    x = np.repeat(gen.make_tokens(1, 1, step=91), T, axis=0)
+    ref = gh.run_layer(DL, x)
+    assert np.all(np.diff(ref["off"])[np.diff(ref["off"]) > 0] == T)
+    buf = moe.Buffers(DL, T, gh.DEV)
+    moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
+    torch.cuda.synchronize()
+    out = buf.out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(out, ref["out"]) and np.array_equal(buf.topk_idx.cpu().numpy(), ref["idx"])
+    assert all(np.array_equal(out[t], out[0]) for t in range(T))
+    rep = gh.check_layer(L, x, ref)
+    gh.log("  ", rep.line())
