@@ -383,3 +383,23 @@ def test_decode_identical_tokens_share_every_expert(T):
     assert all(np.array_equal(out[t], out[0]) for t in range(T))
     rep = gh.check_layer(L, x, ref)
     gh.log("  ", rep.line())
+
+
+@pytest.mark.parametrize("T", [4, 20, 300])
+def test_layer_activation_global_scales(T):
+    """Power-of-two activation global scales (x encoded under 2^-2, h under 2^3)
+    on the decode (fused call), weight-streaming and matrix-core paths, against
+    the oracle under the same scales."""
+    import dataclasses
+    gh.log("case: config 1 T=%d, a_gscale_in 0.25, a_gscale_mid 8" % T)
+    L = dataclasses.replace(gen.make_layer(1), a_gscale_in=0.25, a_gscale_mid=8.0)
+    DL = gh.device_layer(L)
+    x = gen.make_tokens(1, T, step=93)
+    g = gh.run_layer(DL, x)
+    rep = gh.check_layer(L, x, g, tokens=None if T <= 64 else sample_tokens(T, 32, T))
+    gh.log("  ", rep.line())
+    if T <= 4:
+        buf = moe.Buffers(DL, T, gh.DEV)
+        moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), g["out"])
