@@ -26,6 +26,8 @@ def to_dev(a):
 
 
 def bank_to_dev(b):
+    if b is None:  # no shared expert
+        return None
     return {"codes": to_dev(b["codes"]), "scales": to_dev(b["scales"]), "gscale": to_dev(b["gscale"])}
 
 
@@ -96,12 +98,15 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     rows = g["p2r"][(tok[:, None] * sh.k + np.arange(sh.k)[None, :]).reshape(-1)]
     srows = T * sh.k + tok
     r_o = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
-    s_o = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
-                             L.a_gscale_mid)
+    shared = L.sh13 is not None
+    if shared:
+        s_o = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
+                                 L.a_gscale_mid)
     hq_r, hs_r = checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid,
                                        rep, "h")
-    hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
-                                       L.a_gscale_mid, rep, "hsh")
+    if shared:
+        hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
+                                           L.a_gscale_mid, rep, "hsh")
     if "h" in g:
         hr = g["h"][rows].astype(np.float64)
         d = np.abs(hr - r_o["h"]) / (np.abs(r_o["h"]).max() + 1e-30)
@@ -110,12 +115,15 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     # their other side (identical to the oracle's codes when nothing flipped)
     r_t = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid,
                              hq_in=hq_r, hs_in=hs_r)
-    s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
-                             L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s)
+    y_sh = None
+    if shared:
+        s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
+                                 L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s)
+        y_sh = s_t["y"]
+        checker.check_fp32_rows(g["y_shared"][tok], y_sh, rep, "y_shared")
     checker.check_fp32_rows(g["y_rows"][rows], r_t["y"], rep, "y_rows")
-    checker.check_fp32_rows(g["y_shared"][tok], s_t["y"], rep, "y_shared")
     resid = None if residual is None else residual[tok]
-    o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_ad[tok], s_t["y"], resid)
+    o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_ad[tok], y_sh, resid)
     checker.check_output(g["out"][tok], o64, o16, rep)
     rep["oracle_s"] = round(time.time() - t0, 2)
     rep["checked_tokens"] = n

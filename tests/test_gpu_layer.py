@@ -403,3 +403,23 @@ def test_layer_activation_global_scales(T):
         moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
         torch.cuda.synchronize()
         assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), g["out"])
+
+
+@pytest.mark.parametrize("T", [4, 20, 300])
+def test_layer_without_shared_expert(T):
+    """No shared expert (has_shared = 0, y_shared null): the decode (fused call and
+    separate calls), weight-streaming and matrix-core paths against the oracle."""
+    import dataclasses
+    gh.log("case: config 1 T=%d without the shared expert" % T)
+    L = dataclasses.replace(gen.make_layer(1), sh13=None, sh2=None)
+    DL = gh.device_layer(L)
+    assert DL.has_shared == 0
+    x = gen.make_tokens(1, T, step=95)
+    g = gh.run_layer(DL, x)
+    rep = gh.check_layer(L, x, g, tokens=None if T <= 64 else sample_tokens(T, 32, T))
+    gh.log("  ", rep.line())
+    if T <= 4:
+        buf = moe.Buffers(DL, T, gh.DEV)
+        moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), g["out"])
