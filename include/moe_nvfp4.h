@@ -50,7 +50,10 @@ enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,     /* null required pointer, misaligned pointer, bad dtype   */
   MOE_ESHAPE = -2,     /* H or I not a multiple of 32, k outside [1, min(E,32)],
-                          E outside [1, 1024], T < 0, H > 16384, I > 4096       */
+                          E outside [1, 1024], H > 16384, I > 4096, or a token
+                          count T outside 0 <= T, T*H*2 < 2^31, T*(k+1) < 2^31
+                          (32-bit row offsets and int32 pair ids; at H = 2048:
+                          T < 524,288)                                         */
   MOE_EWORKSPACE = -3, /* workspace smaller than moe_workspace_bytes()          */
   MOE_ELAUNCH = -4     /* a kernel launch failed (hipGetLastError)              */
 };
@@ -120,7 +123,8 @@ const char* moe_strerror(int code);
 
 /* Bytes of workspace that moe_route, moe_permute, moe_expert_ffn and
  * moe_layer_forward need for up to T_max tokens of layer L (one workspace may
- * serve all of them, not concurrently).  Returns 0 if L or T_max is invalid.
+ * serve all of them, not concurrently).  Returns 0 if L or T_max is invalid
+ * (including a T_max beyond the token bound of MOE_ESHAPE).
  * Host call.  The workspace is scratch: nothing is kept between calls.       */
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max);
 

@@ -40,6 +40,14 @@ int check_shape(const moe_layer* L) {
   return MOE_OK;
 }
 
+// Token counts: the router's and the matrix-core kernels' buffer resources
+// address a call's [T][H] BF16 rows with 32-bit offsets, and pair ids and
+// permuted rows are int32, so T * H * 2 and T * (k + 1) stay below 2^31.
+inline bool tokens_ok(const moe_layer* L, int64_t T) {
+  const int64_t lim = (int64_t)1 << 31;
+  return T >= 0 && T < lim / (2 * (int64_t)L->H) && T < lim / ((int64_t)L->k + 1);
+}
+
 // an optional K-step-major copy: absent (null codes) or codes and scales
 // aligned, with K a whole number of 64-element steps
 int check_kmajor(const moe_nvfp4_bank& b, int K) {
@@ -106,7 +114,9 @@ const char* moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument (null or misaligned pointer, bad dtype or scale)";
-    case MOE_ESHAPE: return "unsupported shape (H, I multiples of 32; 1 <= k <= min(E, 32); E <= 1024; T >= 0)";
+    case MOE_ESHAPE:
+      return "unsupported shape (H, I multiples of 32; 1 <= k <= min(E, 32); E <= 1024; 0 <= T, T*H*2 < 2^31, "
+             "T*(k+1) < 2^31)";
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_ELAUNCH: return "kernel launch failed";
     default: return "unknown error";
@@ -123,7 +133,7 @@ size_t fused_logits_ws(const moe_layer* L, int64_t T) {
 }
 
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
-  if (check_shape(L) != MOE_OK || T_max < 0) return 0;
+  if (check_shape(L) != MOE_OK || !tokens_ok(L, T_max)) return 0;
   size_t need = route_ws(L, T_max);
   if (permute_ws(L, T_max) > need) need = permute_ws(L, T_max);
   if (ffn_ws(L, T_max).end > need) need = ffn_ws(L, T_max).end;
@@ -135,7 +145,7 @@ int moe_route(const moe_layer* L, const uint16_t* x, int64_t T, const float* log
               float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ptr_ok(topk_idx) || !ptr_ok(topk_w)) return MOE_EINVAL;
   if (!logits_in) {
@@ -153,7 +163,7 @@ int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t*
                 int32_t* pair2row, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   if (!ptr_ok(expert_off)) return MOE_EINVAL;
   if (T > 0 && (!ptr_ok(topk_idx) || !ptr_ok(row2pair) || !ptr_ok(pair2row) || !ptr_ok(ws))) return MOE_EINVAL;
   if (T > 0 && ws_bytes < permute_ws(L, T)) return MOE_EWORKSPACE;
@@ -179,7 +189,7 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
                       const moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_layer(L, false, true);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   const bool partial = kb0 != 0 || kb1 != L->I / 16;
   if (partial && (kb0 < 0 || kb1 > L->I / 16 || kb0 >= kb1 || kb0 % 2 || kb1 % 2)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
@@ -287,7 +297,7 @@ int moe_combine_f32(const moe_layer* L, int64_t T, const float* y_rows, const fl
                     const int32_t* pair2row, const float* topk_w, float* out, hipStream_t stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ptr_ok(y_rows) || !ptr_ok(pair2row) || !ptr_ok(topk_w) || !ptr_ok(out)) return MOE_EINVAL;
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
@@ -299,7 +309,7 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
                 const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ptr_ok(y_rows) || !ptr_ok(pair2row) || !ptr_ok(topk_w) || !ptr_ok(out) || !opt_ok(residual))
     return MOE_EINVAL;
@@ -314,7 +324,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
                       size_t ws_bytes, hipStream_t stream) {
   int rc = check_layer(L, true, true);
   if (rc) return rc;
-  if (T < 0) return MOE_ESHAPE;
+  if (!tokens_ok(L, T)) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ptr_ok(x) || !ptr_ok(topk_idx) || !ptr_ok(topk_w) || !ptr_ok(expert_off) || !ptr_ok(row2pair) ||
       !ptr_ok(pair2row) || !ptr_ok(y_rows) || !ptr_ok(out) || !ptr_ok(ws) || !opt_ok(residual))

@@ -46,10 +46,10 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
-      acc.x += wj[j] * y[j].x;
-      acc.y += wj[j] * y[j].y;
-      acc.z += wj[j] * y[j].z;
-      acc.w += wj[j] * y[j].w;
+      acc.x = fmaf(wj[j], y[j].x, acc.x);
+      acc.y = fmaf(wj[j], y[j].y, acc.y);
+      acc.z = fmaf(wj[j], y[j].z, acc.z);
+      acc.w = fmaf(wj[j], y[j].w, acc.w);
     }
   }
   if (y_shared) {
@@ -72,7 +72,9 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int H, int k, const 
 }
 
 // The un-rounded FP32 layer output without residual (a K-split partial when
-// the rows are partials): out[t] = sum_j w[t][j] y[pair2row[t*k+j]] + y_shared[t].
+// the rows are partials): out[t] = sum_j w[t][j] y[pair2row[t*k+j]] + y_shared[t],
+// with the same fused multiply-adds in the same order as k_combine, so that
+// k_combine's output is the BF16 rounding of this sum (plus the residual).
 __global__ __launch_bounds__(256) void k_combine_f32(int64_t T, int H, int k, const float* __restrict__ y_rows,
                                                      const float* __restrict__ y_shared,
                                                      const int32_t* __restrict__ p2r, const float* __restrict__ w,
@@ -86,10 +88,10 @@ __global__ __launch_bounds__(256) void k_combine_f32(int64_t T, int H, int k, co
   for (int j = 0; j < k; ++j) {
     const float wj = w[t * k + j];
     const float4 y = *reinterpret_cast<const float4*>(y_rows + (int64_t)p2r[t * k + j] * H + c4);
-    acc.x += wj * y.x;
-    acc.y += wj * y.y;
-    acc.z += wj * y.z;
-    acc.w += wj * y.w;
+    acc.x = fmaf(wj, y.x, acc.x);
+    acc.y = fmaf(wj, y.y, acc.y);
+    acc.z = fmaf(wj, y.z, acc.z);
+    acc.w = fmaf(wj, y.w, acc.w);
   }
   if (y_shared) {
     const float4 y = *reinterpret_cast<const float4*>(y_shared + t * H + c4);

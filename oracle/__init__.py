@@ -48,7 +48,6 @@ def lib():
         L.orc_scale_code.argtypes, L.orc_scale_code.restype = [dbl, dbl], ci
         L.orc_elem_code.argtypes, L.orc_elem_code.restype = [dbl, dbl], ci
         L.orc_quant_rows.argtypes = [vp, i64, i64, dbl, vp, vp]
-        L.orc_dequant_rows.argtypes = [vp, vp, i64, i64, dbl, vp]
         L.orc_bf16_to_f64.argtypes = [vp, i64, vp]
         L.orc_round_bf16.argtypes, L.orc_round_bf16.restype = [dbl], ctypes.c_uint16
         L.orc_round_f16_sat.argtypes, L.orc_round_f16_sat.restype = [dbl], dbl
@@ -96,14 +95,6 @@ def quantize(v: np.ndarray, g: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
     scales = np.empty((rows, cols // 16), np.uint8)
     lib().orc_quant_rows(_p(v), rows, cols, g, _p(codes), _p(scales))
     return codes, scales
-
-
-def dequantize(codes: np.ndarray, scales: np.ndarray, g: float = 1.0) -> np.ndarray:
-    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
-    rows, cols = codes.shape[0], codes.shape[1] * 2
-    out = np.empty((rows, cols), np.float64)
-    lib().orc_dequant_rows(_p(codes), _p(scales), rows, cols, g, _p(out))
-    return out
 
 
 def bf16_to_f64(x: np.ndarray) -> np.ndarray:
@@ -207,13 +198,12 @@ def rms_norm(x_bf16, eps=1e-6):
 
 
 # ---------------------------------------------------------------- whole layer
-def layer(L, x_bf16, tokens=None, idx=None, w=None, residual=None, kb=None, h_adopt=None, want_gu=False):
+def layer(L, x_bf16, tokens=None, residual=None, kb=None, want_gu=False):
     """Reference forward of one MoE layer on the tokens listed (default: all).
 
-    L: gen.Layer-like object (router_w, w13, w2, sh13, sh2, shape, a_gscale_in/mid).
-    idx/w: routing to use instead of the oracle's own (teacher forcing after an
-    accepted near-tie), full [T][k].  h_adopt: optional callable(rows_info) ->
-    (hq, hs) replacing the oracle's h codes for routed and shared rows.
+    L: gen.Layer-like object (router_w, w13, w2, sh13, sh2, shape, a_gscale_in/mid);
+    sh13 None: a layer without the shared expert.
+    residual: [T][H] BF16 added before the rounding.  kb = (b0, b1): the down projections over I-blocks [b0, b1) only.
     Returns a dict of every intermediate.
     """
     sh = L.shape
@@ -221,13 +211,10 @@ def layer(L, x_bf16, tokens=None, idx=None, w=None, residual=None, kb=None, h_ad
     T = x_bf16.shape[0]
     tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
     res = {}
-    if idx is None:
-        lg = router_logits(x_bf16[tok], L.router_w)
-        i_s, w_s = topk_softmax(lg, sh.k)
-        res["logits"] = lg
-        idx_t, w_t = i_s, w_s.astype(np.float32)
-    else:
-        idx_t, w_t = _c(idx, np.int32)[tok], _c(w, np.float32)[tok]
+    lg = router_logits(x_bf16[tok], L.router_w)
+    idx_t, w_s = topk_softmax(lg, sh.k)
+    w_t = w_s.astype(np.float32)  # the combine takes the FP32 router weights
+    res["logits"] = lg
     res["idx"], res["w"] = idx_t, w_t
     xf = bf16_to_f64(x_bf16[tok])
     xq, xs = quantize(xf, L.a_gscale_in)
@@ -235,16 +222,15 @@ def layer(L, x_bf16, tokens=None, idx=None, w=None, residual=None, kb=None, h_ad
     n = tok.shape[0]
     a_row = np.repeat(np.arange(n, dtype=np.int32), sh.k)
     a_exp = idx_t.reshape(-1).astype(np.int32)
-    hq_in = hs_in = hq_sh_in = hs_sh_in = None
-    if h_adopt is not None:
-        hq_in, hs_in, hq_sh_in, hs_sh_in = h_adopt(tok, idx_t)
-    r = expert_rows(a_row, a_exp, xq, xs, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid, kb, hq_in, hs_in,
-                    want_gu)
-    s = expert_rows(np.arange(n, dtype=np.int32), np.zeros(n, np.int32), xq, xs, L.sh13, L.sh2, sh.H, sh.I,
-                    L.a_gscale_in, L.a_gscale_mid, kb, hq_sh_in, hs_sh_in, want_gu)
+    r = expert_rows(a_row, a_exp, xq, xs, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid, kb,
+                    want_gu=want_gu)
+    s = None
+    if L.sh13 is not None:  # the shared expert runs on every token (weight 1)
+        s = expert_rows(np.arange(n, dtype=np.int32), np.zeros(n, np.int32), xq, xs, L.sh13, L.sh2, sh.H, sh.I,
+                        L.a_gscale_in, L.a_gscale_mid, kb, want_gu=want_gu)
     res["routed"], res["shared"] = r, s
     resid = None if residual is None else _c(residual, np.uint16)[tok]
-    o64, o16 = combine(r["y"].reshape(n, sh.k, sh.H), w_t, s["y"], resid)
+    o64, o16 = combine(r["y"].reshape(n, sh.k, sh.H), w_t, None if s is None else s["y"], resid)
     res["out_f64"], res["out_bf16"] = o64, o16
     res["tokens"] = tok
     return res

@@ -113,17 +113,6 @@ void orc_quant_rows(const double* v, int64_t rows, int64_t cols, double g, uint8
   }
 }
 
-/* Dequantize [rows][cols] NVFP4 (codes, scales) times a global scale g.    */
-void orc_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, double g, double* out) {
-#pragma omp parallel for schedule(static)
-  for (int64_t r = 0; r < rows; ++r)
-    for (int64_t c = 0; c < cols; ++c) {
-      uint8_t byte = codes[r * (cols / 2) + c / 2];
-      int code = (c & 1) ? (byte >> 4) : (byte & 15);
-      out[r * cols + c] = orc_e2m1(code) * orc_ue4m3(scales[r * (cols / 16) + c / 16]) * g;
-    }
-}
-
 static double bf16_value(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;

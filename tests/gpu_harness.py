@@ -67,10 +67,14 @@ def run_layer(DL: moe.MoELayer, x: np.ndarray, residual=None, dump=("xq", "xs", 
     moe.moe_permute(DL, buf.topk_idx, buf.expert_off, buf.row2pair, buf.pair2row, buf.ws, T=T)
     moe.moe_expert_ffn(DL, xd, buf.expert_off, buf.row2pair, buf.y_rows, buf.y_shared, buf.ws, debug=dbg, T=T)
     moe.moe_combine(DL, buf.y_rows, buf.y_shared, buf.pair2row, buf.topk_w, buf.out, residual=res, T=T)
+    # the FP32 sum before the rounding (without the residual, which the checker adds in FP32)
+    out32 = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    moe.moe_combine_f32(DL, buf.y_rows, buf.y_shared, buf.pair2row, buf.topk_w, out32, T=T)
     torch.cuda.synchronize()
     out = {"idx": buf.topk_idx.cpu().numpy(), "w": buf.topk_w.cpu().numpy(), "off": buf.expert_off.cpu().numpy(),
            "r2p": buf.row2pair.cpu().numpy(), "p2r": buf.pair2row.cpu().numpy(),
-           "y_rows": buf.y_rows.cpu().numpy(), "out": buf.out.cpu().numpy().view(np.uint16)}
+           "y_rows": buf.y_rows.cpu().numpy(), "out": buf.out.cpu().numpy().view(np.uint16),
+           "out_f32": out32.cpu().numpy()}
     if buf.y_shared is not None:
         out["y_shared"] = buf.y_shared.cpu().numpy()
     for key, t in dbg.items():
@@ -124,7 +128,72 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     checker.check_fp32_rows(g["y_rows"][rows], r_t["y"], rep, "y_rows")
     resid = None if residual is None else residual[tok]
     o64, o16 = oracle.combine(r_t["y"].reshape(n, sh.k, sh.H), w_ad[tok], y_sh, resid)
-    checker.check_output(g["out"][tok], o64, o16, rep)
+    v32 = None
+    if "out_f32" in g:  # the kernel's FP32 sum before rounding; the residual is its last FP32 addition
+        v32 = g["out_f32"][tok].astype(np.float32)
+        if resid is not None:
+            v32 = v32 + checker.bf16_bits_to_f64(resid).astype(np.float32)
+    checker.check_output(g["out"][tok], o64, o16, rep, v32=v32)
     rep["oracle_s"] = round(time.time() - t0, 2)
     rep["checked_tokens"] = n
+    return rep
+
+
+def run_krange(DL: moe.MoELayer, x: np.ndarray, kb0: int, kb1: int):
+    """route -> permute -> moe_expert_ffn_krange over the I-blocks [kb0, kb1) ->
+    moe_combine_f32; returns numpy copies of the partial rows and output."""
+    T = x.shape[0]
+    xd = to_dev(x.view(np.int16))
+    buf = moe.Buffers(DL, T, DEV)
+    moe.moe_route(DL, xd, buf.topk_idx, buf.topk_w, buf.ws, T=T)
+    moe.moe_permute(DL, buf.topk_idx, buf.expert_off, buf.row2pair, buf.pair2row, buf.ws, T=T)
+    moe.moe_expert_ffn_krange(DL, xd, buf.expert_off, buf.row2pair, kb0, kb1, buf.y_rows, buf.y_shared, buf.ws, T=T)
+    o32 = torch.empty((T, DL.H), dtype=torch.float32, device=DEV)
+    moe.moe_combine_f32(DL, buf.y_rows, buf.y_shared, buf.pair2row, buf.topk_w, o32, T=T)
+    torch.cuda.synchronize()
+    out = {"idx": buf.topk_idx.cpu().numpy(), "p2r": buf.pair2row.cpu().numpy(), "y_rows": buf.y_rows.cpu().numpy(),
+           "out_f32": o32.cpu().numpy()}
+    if buf.y_shared is not None:
+        out["y_shared"] = buf.y_shared.cpu().numpy()
+    return out
+
+
+def check_krange(L, x, g, part, kb0, kb1, rep=None):
+    """A K-split partial (from run_krange) against the oracle's partial over the same
+    I-blocks, on the h codes the full call g (run_layer with hq/hs dumps) produced,
+    accepted by the checker (identical to the oracle's when nothing flipped)."""
+    rep = checker.Report() if rep is None else rep
+    sh = L.shape
+    T = x.shape[0]
+    assert np.array_equal(part["idx"], g["idx"]) and np.array_equal(part["p2r"], g["p2r"])
+    logits64 = oracle.router_logits(x, L.router_w)
+    idx_ad, w_ad = checker.check_topk(g["idx"], g["w"], logits64, sh.k, rep)
+    xq, xs = oracle.quantize(oracle.bf16_to_f64(x), L.a_gscale_in)
+    tok = np.arange(T, dtype=np.int32)
+    a_row = np.repeat(tok, sh.k).astype(np.int32)
+    a_exp = idx_ad.reshape(-1).astype(np.int32)
+    rows = g["p2r"]
+    args = (xq, xs, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
+    r_o = oracle.expert_rows(a_row, a_exp, *args)
+    hq, hs = checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid,
+                                   rep, "h")
+    r_t = oracle.expert_rows(a_row, a_exp, *args, kb=(kb0, kb1), hq_in=hq, hs_in=hs)
+    checker.check_fp32_rows(part["y_rows"][rows], r_t["y"], rep, "y_rows_part")
+    y_sh = None
+    if L.sh13 is not None:
+        sargs = (xq, xs, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
+        s_o = oracle.expert_rows(tok, np.zeros(T, np.int32), *sargs)
+        srows = T * sh.k + tok
+        hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
+                                           L.a_gscale_mid, rep, "hsh")
+        y_sh = oracle.expert_rows(tok, np.zeros(T, np.int32), *sargs, kb=(kb0, kb1), hq_in=hq_s, hs_in=hs_s)["y"]
+        checker.check_fp32_rows(part["y_shared"], y_sh, rep, "y_shared_part")
+    o64, _ = oracle.combine(r_t["y"].reshape(T, sh.k, sh.H), w_ad, y_sh)
+    rms = float(np.sqrt(np.mean(o64 ** 2)))
+    d = np.abs(part["out_f32"].astype(np.float64) - o64)
+    rep["part_fp32_maxabs_over_rms"] = float(d.max() / rms)
+    assert d.max() <= 1e-2 * rms, "partial output: max-abs %.3g > 1e-2 * RMS" % d.max()
+    rel = float(np.linalg.norm(part["out_f32"] - o64) / np.linalg.norm(o64))
+    rep["part_rel_l2"] = rel
+    assert rel <= 2e-3
     return rep

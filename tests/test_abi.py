@@ -100,6 +100,31 @@ def test_negative_T_and_zero_T():
     assert moe.lib.moe_quantize_act(None, 0, 0, 64, 1.0, None, None, None) == moe.MOE_OK
 
 
+def test_token_bound():
+    """T * H * 2 and T * (k + 1) must stay below 2^31 (32-bit row offsets of the
+    router's and the matrix-core kernels' buffer resources, int32 pair ids): the
+    first count past the bound is refused by every layer entry point, the last
+    one below it is not refused for its shape."""
+    L = layer()  # H 2048, k 10: the bound is 2^31 / 4096 = 524,288 tokens
+    big = (1 << 31) // (2 * L.H)
+    assert big == 524288
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(L), big) == 0
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(L), big - 1) > 0
+    assert route(L, T=big) == moe.MOE_ESHAPE
+    assert route(L, T=big - 1, wsb=0) == moe.MOE_EWORKSPACE
+    assert moe.lib.moe_permute(ctypes.byref(L), FAKE, big, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_expert_ffn(ctypes.byref(L), FAKE, big, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                  None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_combine(ctypes.byref(L), big, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_combine_f32(ctypes.byref(L), big, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_layer_forward(ctypes.byref(L), FAKE, big, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None, FAKE, 1 << 40, None) == moe.MOE_ESHAPE
+    # the smallest hidden size: 2^31 / 64 tokens
+    Ls = layer(H=32, I=32, E=64, k=32)
+    assert route(Ls, T=(1 << 31) // 64) == moe.MOE_ESHAPE
+    assert route(Ls, T=(1 << 31) // 64 - 1, wsb=0) == moe.MOE_EWORKSPACE
+
+
 def test_workspace_too_small():
     L = layer()
     need = moe.lib.moe_workspace_bytes(ctypes.byref(L), 4)

@@ -420,6 +420,139 @@ def test_layer_equivariance_and_duplicates():
     assert np.array_equal(rp["out_bf16"], r["out_bf16"][perm])
 
 
+# ---------------------------------------------------------------- the whole layer, composed independently
+def _exact_dot_int_blocks(qa, sa, qw, sw, b0, b1):
+    """_exact_dot_int over the 16-element blocks [b0, b1) only."""
+    a = E2M1_X2[_unpack(qa)]
+    w = E2M1_X2[_unpack(qw)]
+    K = a.shape[-1]
+    inner = (a.reshape(-1, K // 16, 16)[:, None, b0:b1] * w.reshape(-1, K // 16, 16)[None, :, b0:b1]).sum(-1)
+    scale = _ue4m3_x512(sa)[:, None, b0:b1] * _ue4m3_x512(sw)[None, :, b0:b1]
+    return (inner * scale).sum(-1)
+
+
+def _bf16_bits(v):
+    return (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rne_bf16_exact(q):
+    """Round an exact rational to the nearest BF16 (ties to even) by integer
+    arithmetic; returns (bits, distance to the nearest rounding midpoint)."""
+    if q == 0:
+        return 0, Fraction(1)
+    a = abs(q)
+    e = int(np.floor(np.log2(float(a))))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** max(e - 7, -133)  # 8 significant bits
+    n = a / quantum
+    m = n.numerator // n.denominator
+    frac = n - m
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    val = float(m * quantum) * (1 if q > 0 else -1)
+    return int(_bf16_bits(val)), abs(frac - Fraction(1, 2)) * quantum
+
+
+def _layer_exact(L, x, residual=None, kb=None):
+    """The layer of one call composed without oracle.layer or oracle.expert_rows:
+    exact-rational router logits, top k by a stable sort, softmax by scipy,
+    A4 codes by the (separately pinned) encoder, gate/up and down products as exact
+    integers, h = fl32(silu(g) u) with scipy's expit, and the combine as an exact
+    rational (routed rows times their FP32 weights, the shared row with weight 1,
+    the residual).  Returns (idx, w32, exact outputs as Fractions, per-element
+    scale of the summed terms)."""
+    from scipy.special import expit, softmax
+    sh = L.shape
+    H, I, k = sh.H, sh.I, sh.k
+    T = x.shape[0]
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    lg = [[sum(Fraction(float(xf[t, h])) * Fraction(float(L.router_w[e, h])) for h in range(H)) for e in range(sh.E)]
+          for t in range(T)]
+    idx = np.array([sorted(range(sh.E), key=lambda e: (-lg[t][e], e))[:k] for t in range(T)], np.int32)
+    w32 = np.array([softmax([float(lg[t][e]) for e in idx[t]]) for t in range(T)]).astype(np.float32)
+    xq, xs = oracle.quantize(xf, 1.0)
+    b0, b1 = kb if kb is not None else (0, I // 16)
+    den = 4 * 512 * 512
+
+    def ffn(bank13, bank2, e, t):
+        N = _exact_dot_int(xq[t:t + 1], xs[t:t + 1], bank13["codes"][e], bank13["scales"][e])[0]
+        gu = np.array([float(Fraction(int(n), den) * Fraction(float(bank13["gscale"][e]))) for n in N])
+        g, u = gu[:I], gu[I:]
+        h = (g * expit(g) * u).astype(np.float32).astype(np.float64)[None]
+        hq, hs = oracle.quantize(h, 1.0)
+        Ny = _exact_dot_int_blocks(hq, hs, bank2["codes"][e], bank2["scales"][e], b0, b1)[0]
+        return [Fraction(int(n), den) * Fraction(float(bank2["gscale"][e])) for n in Ny]
+
+    out, mag = [], []
+    for t in range(T):
+        rows = [ffn(L.w13, L.w2, int(idx[t, j]), t) for j in range(k)]
+        terms = [[Fraction(float(w32[t, j])) * rows[j][n] for n in range(H)] for j in range(k)]
+        if L.sh13 is not None:
+            terms.append(ffn(L.sh13, L.sh2, 0, t))
+        if residual is not None:
+            terms.append([Fraction(float(v)) for v in (residual[t].astype(np.uint32) << 16).view(np.float32)])
+        out.append([sum(tt[n] for tt in terms) for n in range(H)])
+        mag.append([float(sum(abs(tt[n]) for tt in terms)) for n in range(H)])
+    return idx, w32, out, np.array(mag)
+
+
+def _assert_layer_matches_exact(r, idx, w32, out, mag):
+    assert np.array_equal(r["idx"], idx)
+    assert np.allclose(r["w"], w32, rtol=2.0 ** -22, atol=0)
+    ex = np.array([[float(v) for v in row] for row in out])
+    tol = 2.0 ** -30 * mag + 1e-300  # the oracle's FP64 rounding of h, y and the sums
+    assert np.all(np.abs(r["out_f64"] - ex) <= tol)
+    checked = 0
+    for t in range(ex.shape[0]):
+        for n in range(ex.shape[1]):
+            bits, dmid = _rne_bf16_exact(out[t][n])
+            if dmid > tol[t, n]:  # not within the oracle's rounding of a BF16 midpoint
+                assert int(r["out_bf16"][t, n]) == bits, (t, n)
+                checked += 1
+    assert checked >= 0.99 * ex.size
+    return ex
+
+
+def test_layer_composition_exact_c0():
+    """oracle.layer against the independent composition, with the residual and a
+    K-split of the down projections; and a dropped shared row, residual or K range
+    would be caught (each changes the output far beyond the tolerance)."""
+    L = gen.make_layer(0)
+    T, H, I = 6, L.shape.H, L.shape.I
+    x = gen.make_tokens(0, T, step=21)
+    res = gen.make_tokens(0, T, step=22)
+    kb = (0, I // 32)
+    r = oracle.layer(L, x, residual=res, kb=kb)
+    idx, w32, out, mag = _layer_exact(L, x, residual=res, kb=kb)
+    ex = _assert_layer_matches_exact(r, idx, w32, out, mag)
+    rms = np.sqrt(np.mean(ex ** 2))
+    for what in ("shared", "residual", "kb"):
+        L2 = gen.Layer(**{**L.__dict__, "sh13": None, "sh2": None}) if what == "shared" else L
+        _, _, out2, _ = _layer_exact(L2, x, residual=None if what == "residual" else res,
+                                     kb=None if what == "kb" else kb)
+        alt = np.array([[float(v) for v in row] for row in out2])
+        assert np.mean(np.abs(alt - ex) > 1e-3 * rms) > 0.5, what
+
+
+def test_layer_without_shared_and_token_subset_c0():
+    """A layer without the shared expert (its term is absent, not zero-weighted by
+    accident), and the tokens= subset of a call equals the call on those tokens."""
+    L = gen.make_layer(0)
+    L0 = gen.Layer(**{**L.__dict__, "sh13": None, "sh2": None})
+    x = gen.make_tokens(0, 8, step=23)
+    r = oracle.layer(L0, x)
+    assert r["shared"] is None
+    idx, w32, out, mag = _layer_exact(L0, x)
+    _assert_layer_matches_exact(r, idx, w32, out, mag)
+    sub = np.array([6, 1, 3], np.int32)
+    rs = oracle.layer(L0, x, tokens=sub)
+    assert np.array_equal(rs["out_bf16"], r["out_bf16"][sub]) and np.array_equal(rs["out_f64"], r["out_f64"][sub])
+    assert np.array_equal(rs["idx"], r["idx"][sub])
+
+
 # ---------------------------------------------------------------- the pages' printed sizes
 def test_packed_size_matches_host_bank():
     facts = {r[0]: float(r[1]) for r in _read_table("page_facts.txt")}
