@@ -216,6 +216,24 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
                       float* y_rows, float* y_shared, uint16_t* out, const moe_debug* dbg, void* ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a device array inside
+ * the library of moe_noalloc_scratch_bytes() bytes (64 MiB), one per GPU the
+ * library runs on, held until the process ends; this call allocates nothing.
+ * Arguments, outputs and results are those of moe_layer_forward (same
+ * kernels).  MOE_EWORKSPACE when moe_workspace_bytes(L, T) exceeds the array
+ * (at hidden 2048, 512 experts, top 10 + shared, intermediate 512: more than
+ * 3,391 tokens); the size is checked before anything else touches the GPU.  The array of the current device is used (the stream
+ * must belong to it).  Every call on a GPU shares that GPU's array and leaves
+ * its contents behind (no call needs it cleared); calls that overlap in time
+ * on one GPU race.                                                            */
+size_t moe_noalloc_scratch_bytes(void);
+int moe_layer_forward_noalloc(const moe_layer* L, const uint16_t* x, int64_t T, const uint16_t* residual,
+                              int32_t* topk_idx, float* topk_w, int32_t* expert_off, int32_t* row2pair,
+                              int32_t* pair2row, float* y_rows, float* y_shared, uint16_t* out,
+                              const moe_debug* dbg, hipStream_t stream);
+
 /* Parameter-free RMS norm of BF16 rows, the composition that chains layers
  * into a stack (the pages run 48 MoE layers, Richland article, "What
  * shipped"; the block structure around them is not printed):

@@ -68,10 +68,14 @@ def _load():
     L.moe_rms_norm.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_double, vp, vp]
     L.moe_expert_ffn_krange.argtypes = [pl, vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, sz, vp]
     L.moe_combine_f32.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp]
+    L.moe_noalloc_scratch_bytes.restype = sz
+    L.moe_layer_forward_noalloc.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug),
+                                            vp]
     i32 = ctypes.c_int32
     L.moe_pack_kmajor.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
-              "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32", "moe_pack_kmajor"):
+              "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32", "moe_pack_kmajor",
+              "moe_layer_forward_noalloc"):
         getattr(L, f).restype = ci
     return L
 
@@ -79,7 +83,7 @@ def _load():
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm", "moe_expert_ffn_krange",
-           "moe_combine_f32", "moe_pack_kmajor")
+           "moe_combine_f32", "moe_pack_kmajor", "moe_noalloc_scratch_bytes", "moe_layer_forward_noalloc")
 
 
 def strerror(code: int) -> str:
@@ -255,6 +259,21 @@ def moe_layer_forward(layer: MoELayer, x, buf: Buffers, residual=None, T=None, d
                                  _ptr(buf.expert_off), _ptr(buf.row2pair), _ptr(buf.pair2row), _ptr(buf.y_rows),
                                  _ptr(buf.y_shared), _ptr(buf.out), None if dbg is None else ctypes.byref(dbg),
                                  _ptr(buf.ws), buf.ws.numel(), _stream(stream)), "moe_layer_forward")
+    return buf.out
+
+
+def moe_layer_forward_noalloc(layer: MoELayer, x, buf: Buffers, residual=None, T=None, debug=None, topk=None,
+                              stream=None):
+    """moe_layer_forward with the library's own device scratch array as workspace
+    (buf.ws is not used; nothing is allocated); returns buf.out."""
+    T = x.shape[0] if T is None else T
+    idx, w = (buf.topk_idx, buf.topk_w) if topk is None else topk
+    dbg = _debug(debug)
+    _check(lib.moe_layer_forward_noalloc(ctypes.byref(layer.desc), _ptr(x), T, _ptr(residual), _ptr(idx), _ptr(w),
+                                         _ptr(buf.expert_off), _ptr(buf.row2pair), _ptr(buf.pair2row),
+                                         _ptr(buf.y_rows), _ptr(buf.y_shared), _ptr(buf.out),
+                                         None if dbg is None else ctypes.byref(dbg), _stream(stream)),
+           "moe_layer_forward_noalloc")
     return buf.out
 
 

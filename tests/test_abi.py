@@ -125,6 +125,21 @@ def test_token_bound():
     assert route(Ls, T=(1 << 31) // 64 - 1, wsb=0) == moe.MOE_EWORKSPACE
 
 
+def test_noalloc_refuses_beyond_its_array():
+    """The allocation-free layer call checks its size before touching the GPU: a
+    token count whose workspace exceeds the library's 64 MiB array is refused."""
+    L = layer()
+    lim = moe.lib.moe_noalloc_scratch_bytes()
+    assert lim == 64 << 20
+    T = 1
+    while moe.lib.moe_workspace_bytes(ctypes.byref(L), T) <= lim:
+        T += 256
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert moe.lib.moe_layer_forward_noalloc(ctypes.byref(L), FAKE, T, None, *args) == moe.MOE_EWORKSPACE
+    assert moe.lib.moe_layer_forward_noalloc(ctypes.byref(L), FAKE, -1, None, *args) == moe.MOE_ESHAPE
+    assert moe.lib.moe_layer_forward_noalloc(None, FAKE, 4, None, *args) == moe.MOE_EINVAL
+
+
 def test_workspace_too_small():
     L = layer()
     need = moe.lib.moe_workspace_bytes(ctypes.byref(L), 4)
