@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libgen.so")
 
 BASE_SEED = 1234
-TENSOR_HIDDEN, TENSOR_ROUTER, TENSOR_W13, TENSOR_W2, TENSOR_SH13, TENSOR_SH2 = range(6)
+TENSOR_HIDDEN, TENSOR_ROUTER, TENSOR_W13, TENSOR_W2, TENSOR_SH13, TENSOR_SH2, TENSOR_SHGATE = range(7)
 
 
 def build(force: bool = True) -> str:
@@ -178,10 +178,14 @@ class Layer:
     sh2: dict
     a_gscale_in: float = 1.0
     a_gscale_mid: float = 1.0
+    shared_gate_w: np.ndarray | None = None  # [H] f32, optional gate of the shared expert
+    act_bits: int = 4  # activation encoding: 4 (W4A4) or 8 (the W4A8 variant)
 
 
-def make_layer(cfg: int, layer: int = 0, seed: int = BASE_SEED, shape: Shape | None = None) -> Layer:
-    """One MoE layer's weights (router FP32, routed and shared NVFP4 banks)."""
+def make_layer(cfg: int, layer: int = 0, seed: int = BASE_SEED, shape: Shape | None = None,
+               shared_gate: bool = False) -> Layer:
+    """One MoE layer's weights (router FP32, routed and shared NVFP4 banks, and with
+    shared_gate an N(0, 0.02^2) FP32 gate vector for the shared expert)."""
     sh = shape or SHAPES[cfg]
     sk = lambda t: stream_key(seed, cfg, layer, t)
     return Layer(
@@ -191,6 +195,7 @@ def make_layer(cfg: int, layer: int = 0, seed: int = BASE_SEED, shape: Shape | N
         w2=nvfp4_bank(sk(TENSOR_W2), sh.E, sh.H, sh.I),
         sh13=nvfp4_bank(sk(TENSOR_SH13), 1, 2 * sh.I, sh.H),
         sh2=nvfp4_bank(sk(TENSOR_SH2), 1, sh.H, sh.I),
+        shared_gate_w=normal_f32_rows(sk(TENSOR_SHGATE), np.array([ROUTER_SIGMA]), sh.H)[0] if shared_gate else None,
     )
 
 

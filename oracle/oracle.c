@@ -310,6 +310,139 @@ void orc_combine(int64_t n, int k, int64_t H, const double* y, const float* w, c
 }
 
 /* ------------------------------------------------------------------ */
+/* A8: the 8-bit activation encoding of the W4A8 variant.  The pages name the
+ * older W4A8 host path (capy-flash README v0.5.4, "Serve": activations of
+ * host-computed experts in 8 bits, made the output depend on where an expert
+ * ran) but not its format.  Read here as the A4 encoding with an 8-bit integer
+ * element grid: the same 16-element blocks and UE4M3 block scale, chosen as
+ * RNE(amax / (127 g)) (127 = the largest INT8 magnitude in place of E2M1's 6),
+ * and element codes q = RNE(x / (s g)) on the integers, saturating at +-127
+ * (two's complement; zero carries no sign).  The element value is q s g.     */
+int orc_scale_code8(double amax, double g) {
+  int c = 0;
+  while (c < 126) {
+    double mid = 0.5 * (orc_ue4m3(c) + orc_ue4m3(c + 1));
+    double thr = 127.0 * g * mid; /* exact: <= 12 significant bits times 2^k */
+    if (amax > thr) { c++; continue; }
+    if (amax == thr && ((c + 1) & 1) == 0) c++;
+    break;
+  }
+  return c;
+}
+
+/* q = RNE(|v| / s) on the integers 0..127 (ties to even), with the sign of v;
+ * decided by exact comparisons of |v| with (m + 1/2) s; s == 0 gives 0.      */
+int orc_int8_code(double v, double s) {
+  if (!(s > 0.0)) return 0;
+  double a = fabs(v);
+  int m = 0;
+  while (m < 127) {
+    double thr = (m + 0.5) * s;
+    if (a > thr) { m++; continue; }
+    if (a == thr && ((m + 1) & 1) == 0) m++;
+    break;
+  }
+  return signbit(v) ? -m : m;
+}
+
+/* A8 over a row-major [rows][cols] matrix: codes [rows][cols] int8, scales
+ * [rows][cols/16].                                                        */
+void orc_quant8_rows(const double* v, int64_t rows, int64_t cols, double g, int8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < cols / 16; ++b) {
+      const double* x = v + r * cols + b * 16;
+      double amax = 0.0;
+      for (int i = 0; i < 16; ++i)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+      int sc = orc_scale_code8(amax, g);
+      scales[r * (cols / 16) + b] = (uint8_t)sc;
+      double s = orc_ue4m3(sc) * g;
+      for (int i = 0; i < 16; ++i) codes[r * cols + b * 16 + i] = (int8_t)orc_int8_code(x[i], s);
+    }
+  }
+}
+
+/* NVFP4 weight row times an A8 activation row over 16-element blocks [b0, b1):
+ *   sum_b dec(sa_b) * dec(sw_b) * sum_{i in b} qa_i * e2m1(qw_i)    (FP64)  */
+static double nvfp4_a8_dot(const int8_t* qa, const uint8_t* sa, const uint8_t* qw, const uint8_t* sw, int64_t b0,
+                           int64_t b1) {
+  double acc = 0.0;
+  for (int64_t b = b0; b < b1; ++b) {
+    double inner = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      int64_t c = b * 16 + i;
+      int cw = (c & 1) ? (qw[c / 2] >> 4) : (qw[c / 2] & 15);
+      inner += (double)qa[c] * orc_e2m1(cw);
+    }
+    acc += orc_ue4m3(sa[b]) * orc_ue4m3(sw[b]) * inner;
+  }
+  return acc;
+}
+
+/* X with A8 activations (the W4A8 variant): as orc_expert_rows, with x and h
+ * encoded by A8 (xq [T][H] int8, hq [n][I] int8).                          */
+void orc_expert_rows_a8(int64_t n_rows, const int32_t* a_row, const int32_t* a_exp, const int8_t* xq,
+                        const uint8_t* xs, double g_in, const uint8_t* w13q, const uint8_t* w13s, const float* w13g,
+                        const uint8_t* w2q, const uint8_t* w2s, const float* w2g, int64_t H, int64_t I, double g_mid,
+                        int64_t kb0, int64_t kb1, const int8_t* hq_in, const uint8_t* hs_in, double* g_out,
+                        double* u_out, float* h_out, int8_t* hq_out, uint8_t* hs_out, double* y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t t = a_row[r], e = a_exp[r];
+    const int8_t* qa = xq + t * H;
+    const uint8_t* sa = xs + t * (H / 16);
+    double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+    int8_t* hq = (int8_t*)malloc((size_t)I);
+    uint8_t* hs = (uint8_t*)malloc((size_t)(I / 16));
+    const double G13 = (double)w13g[e], G2 = (double)w2g[e];
+    for (int64_t i = 0; i < I; ++i) {
+      const int64_t rg = e * 2 * I + i, ru = e * 2 * I + I + i;
+      double g = G13 * g_in * nvfp4_a8_dot(qa, sa, w13q + rg * (H / 2), w13s + rg * (H / 16), 0, H / 16);
+      double u = G13 * g_in * nvfp4_a8_dot(qa, sa, w13q + ru * (H / 2), w13s + ru * (H / 16), 0, H / 16);
+      float h = (float)(silu(g) * u);
+      hv[i] = (double)h;
+      if (g_out) g_out[r * I + i] = g;
+      if (u_out) u_out[r * I + i] = u;
+      if (h_out) h_out[r * I + i] = h;
+    }
+    orc_quant8_rows(hv, 1, I, g_mid, hq, hs);
+    if (hq_out) memcpy(hq_out + r * I, hq, (size_t)I);
+    if (hs_out) memcpy(hs_out + r * (I / 16), hs, (size_t)(I / 16));
+    const int8_t* hq_use = hq_in ? hq_in + r * I : hq;
+    const uint8_t* hs_use = hs_in ? hs_in + r * (I / 16) : hs;
+    for (int64_t n = 0; n < H; ++n) {
+      const int64_t rw = e * H + n;
+      y[r * H + n] = G2 * g_mid * nvfp4_a8_dot(hq_use, hs_use, w2q + rw * (I / 2), w2s + rw * (I / 16), kb0, kb1);
+    }
+    free(hv);
+    free(hq);
+    free(hs);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Optional shared-expert gate.  The pages print no gate on the shared expert
+ * (they list it as always on [R3][A1]); the variant read here is the plainest
+ * one: a per-token scalar g_t = sigmoid(z_t) with z_t = sum_h x[t][h] * wg[h]
+ * (wg an FP32 vector of length H), the sum in FP64 over exact products and
+ * the sigmoid 1 / (1 + exp(-z)) in FP64, rounded to FP32.  The shared
+ * expert's output row of token t is multiplied by g_t.                     */
+void orc_shared_gate(const uint16_t* x, const float* wg, int64_t T, int64_t H, float* g) {
+  for (int64_t t = 0; t < T; ++t) {
+    double z = 0.0;
+    for (int64_t h = 0; h < H; ++h) z += bf16_value(x[t * H + h]) * (double)wg[h];
+    g[t] = (float)(1.0 / (1.0 + exp(-z)));
+  }
+}
+
+/* orc_round_bf16 over an array. */
+void orc_round_bf16_array(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_round_bf16(v[i]);
+}
+
+/* ------------------------------------------------------------------ */
 /* Stack composition (a reading; the pages chain 48 MoE layers, Richland
  * article "What shipped", but print no block structure): before each MoE
  * layer the residual stream is RMS-normalised without a learned weight,

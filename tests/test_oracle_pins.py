@@ -159,6 +159,128 @@ def test_elem_code_ties_and_saturation_by_fractions():
     assert oracle.elem_code(3.0, 0.0) == 0
 
 
+# ---------------------------------------------------------------- A8 (the W4A8 variant's encoding)
+@pytest.mark.parametrize("g", [1.0, 2.0 ** -4, 2.0 ** 3])
+def test_scale_code8_exhaustive_bf16_amax(g):
+    """A8 block scale: nearest point of the 127 g UE4M3 grid by distance (ties to the
+    even code), over every BF16 amax (127 g grid values have <= 12 significant bits,
+    so the distances near amax are exact in FP64)."""
+    amax = np.unique(np.abs(_all_bf16_finite()))
+    want = _nearest_even(127.0 * g * UE4M3, amax)
+    got = np.array([oracle.scale_code8(float(a), g) for a in amax])
+    assert np.array_equal(got, want)
+
+
+def test_scale_code8_ties_by_fractions():
+    for c in range(126):
+        mid = (Fraction(UE4M3[c]) + Fraction(UE4M3[c + 1])) / 2 * 127
+        assert float(mid) == mid
+        assert oracle.scale_code8(float(mid), 1.0) == (c if c % 2 == 0 else c + 1), c
+
+
+def test_int8_codes_exhaustive_bf16_all_scales():
+    """All finite BF16 values x all 126 nonzero scales, each in a block whose amax
+    pins the scale (amax = 127 s), against numpy: rint of the FP64 quotient, ties to
+    even, saturation at 127.  |x| has 8 significant bits and s 4, so a quotient below
+    127.5 is at least 1/(15 * 512) from any half-integer it does not equal: the FP64
+    quotient rounds to the same integer as the exact one."""
+    vals = _all_bf16_finite()
+    got_all, want_all = [], []
+    for c in range(1, 127):
+        s = UE4M3[c]
+        v = vals[np.abs(vals) <= 127.0 * s]
+        pad = (-len(v)) % 15
+        v = np.concatenate([v, np.zeros(pad)])
+        blocks = v.reshape(-1, 15)
+        blk = np.concatenate([np.full((blocks.shape[0], 1), 127.0 * s), blocks], axis=1)
+        codes, scales = oracle.quantize8(blk, 1.0)
+        assert np.all(scales == c)
+        want = np.sign(blocks) * np.minimum(127.0, np.rint(np.abs(blocks) / s))
+        got_all.append(codes[:, 1:].astype(np.float64).ravel())
+        want_all.append(want.ravel())
+    assert np.array_equal(np.concatenate(got_all), np.concatenate(want_all))
+
+
+def test_int8_code_ties_saturation_and_zero_by_fractions():
+    s = 0.6875  # 4 significant bits
+    for m in range(127):
+        mid = (Fraction(m) + Fraction(1, 2)) * Fraction(s)
+        even = m if m % 2 == 0 else m + 1
+        assert oracle.int8_code(float(mid), s) == min(even, 127)
+        assert oracle.int8_code(-float(mid), s) == -min(even, 127)
+    assert oracle.int8_code(1e30, s) == 127 and oracle.int8_code(-1e30, s) == -127
+    assert oracle.int8_code(-1e-30, s) == 0 and oracle.int8_code(3.0, 0.0) == 0
+
+
+def test_quantize8_idempotent_on_grid():
+    """Blocks holding a +-127 code with any scale: quantize8(q * s) == (q, s)."""
+    rng = np.random.default_rng(13)
+    q = rng.integers(-127, 128, size=(400, 16))
+    q[np.arange(400), rng.integers(0, 16, 400)] = np.where(rng.random(400) < .5, 127, -127)
+    sc = rng.integers(1, 127, size=(400, 1))
+    codes, scales = oracle.quantize8(q * UE4M3[sc], 1.0)
+    assert np.array_equal(scales[:, 0], sc[:, 0]) and np.array_equal(codes, q)
+
+
+def test_expert_ffn_a8_exact_integer_c0():
+    """The W4A8 expert FFN as exact integers: int8 activation codes times twice the
+    E2M1 weight codes, block by block, times the two UE4M3 scales (each x 512)."""
+    L = gen.make_layer(0)
+    sh = L.shape
+    x = gen.make_tokens(0, 6, step=27)
+    g_in, g_mid = 2.0 ** -4, 2.0 ** -8
+    xq, xs = oracle.quantize8(oracle.bf16_to_f64(x), g_in)
+    rows = np.repeat(np.arange(6, dtype=np.int32), 2)
+    exps = np.tile(np.array([2, 11], np.int32), 6)
+    r = oracle.expert_rows(rows, exps, xq, xs, L.w13, L.w2, sh.H, sh.I, g_in, g_mid, want_gu=True, act_bits=8)
+
+    def dot8(qa, sa, qw, sw):  # integer N with dot = N / (2 * 512 * 512)
+        a = qa.astype(np.int64)
+        w = E2M1_X2[_unpack(qw)]
+        K = a.shape[-1]
+        inner = (a.reshape(-1, K // 16, 16)[:, None] * w.reshape(-1, K // 16, 16)[None]).sum(-1)
+        return (inner * _ue4m3_x512(sa)[:, None, :] * _ue4m3_x512(sw)[None, :, :]).sum(-1)
+
+    den = 2.0 * 512 * 512
+    for e in (2, 11):
+        N = dot8(xq, xs, L.w13["codes"][e], L.w13["scales"][e]).astype(np.float64)
+        gu = N / den * float(L.w13["gscale"][e]) * g_in
+        sel = exps == e
+        assert np.allclose(r["g"][sel], gu[rows[sel], :sh.I], rtol=1e-14, atol=1e-300)
+        assert np.allclose(r["u"][sel], gu[rows[sel], sh.I:], rtol=1e-14, atol=1e-300)
+    hq, hs = oracle.quantize8(r["h"].astype(np.float64), g_mid)
+    assert np.array_equal(hq, r["hq"]) and np.array_equal(hs, r["hs"])
+    assert np.count_nonzero(hq) > 0.9 * hq.size  # the global scale keeps h's scales off the underflow
+    for i, e in enumerate(exps[:4]):
+        N = dot8(r["hq"][i:i + 1], r["hs"][i:i + 1], L.w2["codes"][e], L.w2["scales"][e])[0]
+        assert np.allclose(r["y"][i], N / den * float(L.w2["gscale"][e]) * g_mid, rtol=1e-14, atol=1e-300)
+
+
+def test_expert_ffn_a8_dense_reduction_numpy_matmul():
+    """E = 1, k = 1: the W4A8 layer is a dense SwiGLU MLP on dequantized operands."""
+    L = gen.make_layer(0)
+    sh = L.shape
+    x = gen.make_tokens(0, 8, step=28)
+    g_in, g_mid = 2.0 ** -4, 2.0 ** -8
+    xq, xs = oracle.quantize8(oracle.bf16_to_f64(x), g_in)
+
+    def deq4(codes, scales):
+        return (E2M1_X2[_unpack(codes)] / 2.0) * np.repeat(UE4M3[scales], 16, axis=-1)
+
+    def deq8(codes, scales, g):
+        return codes.astype(np.float64) * np.repeat(UE4M3[scales], 16, axis=-1) * g
+
+    e = 5
+    W13 = deq4(L.w13["codes"][e], L.w13["scales"][e]) * float(L.w13["gscale"][e])
+    W2 = deq4(L.w2["codes"][e], L.w2["scales"][e]) * float(L.w2["gscale"][e])
+    r = oracle.expert_rows(np.arange(8, dtype=np.int32), np.full(8, e, np.int32), xq, xs, L.w13, L.w2, sh.H, sh.I,
+                           g_in, g_mid, want_gu=True, act_bits=8)
+    gu = deq8(xq, xs, g_in) @ W13.T
+    assert np.allclose(r["g"], gu[:, :sh.I], rtol=1e-12, atol=1e-15)
+    assert np.allclose(r["u"], gu[:, sh.I:], rtol=1e-12, atol=1e-15)
+    assert np.allclose(r["y"], deq8(r["hq"], r["hs"], g_mid) @ W2.T, rtol=1e-12, atol=1e-15)
+
+
 def test_quantize_idempotent_on_grid():
     rng = np.random.default_rng(3)
     # blocks containing a +-6 code: quantize(dequantize(q, s)) == (q, s)
@@ -473,25 +595,41 @@ def _layer_exact(L, x, residual=None, kb=None):
           for t in range(T)]
     idx = np.array([sorted(range(sh.E), key=lambda e: (-lg[t][e], e))[:k] for t in range(T)], np.int32)
     w32 = np.array([softmax([float(lg[t][e]) for e in idx[t]]) for t in range(T)]).astype(np.float32)
-    xq, xs = oracle.quantize(xf, 1.0)
+    a8 = getattr(L, "act_bits", 4) == 8
+    g_in, g_mid = L.a_gscale_in, L.a_gscale_mid
+    enc = oracle.quantize8 if a8 else oracle.quantize  # the encoders are pinned separately
+    xq, xs = enc(xf, g_in)
     b0, b1 = kb if kb is not None else (0, I // 16)
-    den = 4 * 512 * 512
+    den = (2 if a8 else 4) * 512 * 512
+
+    def dot(qa, sa, qw, sw, c0, c1):  # exact integer N with the dot = N / den
+        a = qa.astype(np.int64) if a8 else E2M1_X2[_unpack(qa)]
+        w = E2M1_X2[_unpack(qw)]
+        K = a.shape[-1]
+        inner = (a.reshape(-1, K // 16, 16)[:, None, c0:c1] * w.reshape(-1, K // 16, 16)[None, :, c0:c1]).sum(-1)
+        return (inner * _ue4m3_x512(sa)[:, None, c0:c1] * _ue4m3_x512(sw)[None, :, c0:c1]).sum(-1)
 
     def ffn(bank13, bank2, e, t):
-        N = _exact_dot_int(xq[t:t + 1], xs[t:t + 1], bank13["codes"][e], bank13["scales"][e])[0]
-        gu = np.array([float(Fraction(int(n), den) * Fraction(float(bank13["gscale"][e]))) for n in N])
+        N = dot(xq[t:t + 1], xs[t:t + 1], bank13["codes"][e], bank13["scales"][e], 0, H // 16)[0]
+        gsc = Fraction(float(bank13["gscale"][e])) * Fraction(g_in)
+        gu = np.array([float(Fraction(int(n), den) * gsc) for n in N])
         g, u = gu[:I], gu[I:]
         h = (g * expit(g) * u).astype(np.float32).astype(np.float64)[None]
-        hq, hs = oracle.quantize(h, 1.0)
-        Ny = _exact_dot_int_blocks(hq, hs, bank2["codes"][e], bank2["scales"][e], b0, b1)[0]
-        return [Fraction(int(n), den) * Fraction(float(bank2["gscale"][e])) for n in Ny]
+        hq, hs = enc(h, g_mid)
+        Ny = dot(hq, hs, bank2["codes"][e], bank2["scales"][e], b0, b1)[0]
+        return [Fraction(int(n), den) * Fraction(float(bank2["gscale"][e])) * Fraction(g_mid) for n in Ny]
 
     out, mag = [], []
     for t in range(T):
         rows = [ffn(L.w13, L.w2, int(idx[t, j]), t) for j in range(k)]
         terms = [[Fraction(float(w32[t, j])) * rows[j][n] for n in range(H)] for j in range(k)]
         if L.sh13 is not None:
-            terms.append(ffn(L.sh13, L.sh2, 0, t))
+            ysh = ffn(L.sh13, L.sh2, 0, t)
+            if getattr(L, "shared_gate_w", None) is not None:
+                z = sum(Fraction(float(xf[t, h])) * Fraction(float(L.shared_gate_w[h])) for h in range(H))
+                g = Fraction(float(np.float32(expit(float(z)))))
+                ysh = [g * v for v in ysh]
+            terms.append(ysh)
         if residual is not None:
             terms.append([Fraction(float(v)) for v in (residual[t].astype(np.uint32) << 16).view(np.float32)])
         out.append([sum(tt[n] for tt in terms) for n in range(H)])
@@ -551,6 +689,53 @@ def test_layer_without_shared_and_token_subset_c0():
     rs = oracle.layer(L0, x, tokens=sub)
     assert np.array_equal(rs["out_bf16"], r["out_bf16"][sub]) and np.array_equal(rs["out_f64"], r["out_f64"][sub])
     assert np.array_equal(rs["idx"], r["idx"][sub])
+
+
+def test_layer_composition_w4a8_c0():
+    """oracle.layer in the W4A8 variant (A8 encodings, power-of-two global scales)
+    against the independent composition, with the residual and the shared gate."""
+    L = gen.make_layer(0, shared_gate=True)
+    L.act_bits, L.a_gscale_in, L.a_gscale_mid = 8, 2.0 ** -4, 2.0 ** -8
+    x = gen.make_tokens(0, 5, step=29)
+    res = gen.make_tokens(0, 5, step=30)
+    r = oracle.layer(L, x, residual=res)
+    assert r["xq"].dtype == np.int8 and r["xq"].shape == (5, L.shape.H)
+    idx, w32, out, mag = _layer_exact(L, x, residual=res)
+    _assert_layer_matches_exact(r, idx, w32, out, mag)
+
+
+def test_shared_gate_exact_rational_and_closed_forms():
+    """The optional shared-expert gate: z by exact fractions and the sigmoid by
+    scipy's expit give the oracle's FP32 gate (to one FP32 rounding of the
+    sigmoid); zero weights give exactly 1/2; a gate vector aligned with x drives
+    it to 1 and its negative to 0."""
+    from scipy.special import expit
+    L = gen.make_layer(0, shared_gate=True)
+    x = gen.make_tokens(0, 8, step=24)
+    g = oracle.shared_gate(x, L.shared_gate_w)
+    xf = oracle.bf16_to_f64(x)
+    for t in range(8):
+        z = sum(Fraction(float(xf[t, h])) * Fraction(float(L.shared_gate_w[h])) for h in range(L.shape.H))
+        want = np.float32(expit(float(z)))
+        assert abs(float(g[t]) - float(want)) <= 2.0 ** -24 * float(want), t
+    assert np.all(oracle.shared_gate(x, np.zeros(L.shape.H, np.float32)) == 0.5)
+    big = (xf[0] * 10.0).astype(np.float32)
+    assert oracle.shared_gate(x[:1], big)[0] == 1.0 and oracle.shared_gate(x[:1], -big)[0] == 0.0
+
+
+def test_layer_composition_with_shared_gate_c0():
+    """oracle.layer with the shared-expert gate against the independent composition;
+    dropping the gate would be caught."""
+    L = gen.make_layer(0, shared_gate=True)
+    x = gen.make_tokens(0, 5, step=25)
+    res = gen.make_tokens(0, 5, step=26)
+    r = oracle.layer(L, x, residual=res)
+    idx, w32, out, mag = _layer_exact(L, x, residual=res)
+    ex = _assert_layer_matches_exact(r, idx, w32, out, mag)
+    L2 = gen.Layer(**{**L.__dict__, "shared_gate_w": None})
+    _, _, out2, _ = _layer_exact(L2, x, residual=res)
+    alt = np.array([[float(v) for v in row] for row in out2])
+    assert np.mean(np.abs(alt - ex) > 1e-3 * np.sqrt(np.mean(ex ** 2))) > 0.5
 
 
 # ---------------------------------------------------------------- the pages' printed sizes
