@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum {
   MOE_OK = 0,
@@ -86,14 +86,35 @@ typedef struct {
  *         kernels (prompt chunks) read the copy, whose K steps are contiguous
  *         runs; otherwise they read the row-major bank.  Results are identical
  *         either way; the decode and weight-streaming kernels always read the
- *         row-major banks.  Zero-initialise the struct to leave them unset.   */
+ *         row-major banks.  Zero-initialise the struct to leave them unset.
+ *   shared_gate_w : optional [H] FP32 gate vector of the shared expert (null:
+ *         no gate, the shared expert's weight is 1).  With it, the shared
+ *         expert's output row of token t is multiplied by
+ *         g_t = fl32(sigmoid(sum_h x[t][h] * shared_gate_w[h])), the sum in FP64
+ *         over exact products and the sigmoid in FP64 (y_shared holds the gated
+ *         rows).  The pages print no gate on the shared expert; this is the
+ *         plainest form an optional gate takes (a streamed-prefill hand-off
+ *         with such a gate is what the pages' model family runs).
+ *   router_pieces : optional [3][E][H] BF16 pieces of router_w written once by
+ *         moe_pack_router; where set, the matrix-core router reads them
+ *         instead of splitting router_w on every call (identical results).
+ *   router_mode : MOE_ROUTER_EXACT (0, the default), MOE_ROUTER_SPLIT3_F32 or
+ *         MOE_ROUTER_BF16; see moe_route.
+ *   act_bits : activation encoding of x and h: 0 or 4 = A4 (W4A4, the
+ *         default); other values are MOE_ESHAPE.                              */
 typedef struct {
   int32_t H, I, E, k, has_shared;
   const float* router_w;
   moe_nvfp4_bank w13, w2, sh13, sh2;
   float a_gscale_in, a_gscale_mid;
   moe_nvfp4_bank w13k, w2k, sh13k, sh2k;
+  const float* shared_gate_w;
+  const uint16_t* router_pieces;
+  int32_t router_mode;
+  int32_t act_bits;
 } moe_layer;
+
+enum { MOE_ROUTER_EXACT = 0, MOE_ROUTER_SPLIT3_F32 = 1, MOE_ROUTER_BF16 = 2 };
 
 /* Optional dumps of intermediate values (all nullable, device pointers).
  *   xq [T][H/2], xs [T][H/16] : A4 encoding of x (codes, UE4M3 scales)
@@ -128,13 +149,26 @@ const char* moe_strerror(int code);
  * Host call.  The workspace is scratch: nothing is kept between calls.       */
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max);
 
-/* Router: logits l[t][e] = sum_h x[t][h] * router_w[e][h] (selection on FP64
- * sums of the exact products, see route.hip),
- * the k largest per token in descending order (equal logits: lower expert id
- * first), and w[t][j] = softmax over the k selected logits.
+/* Router: logits l[t][e] = sum_h x[t][h] * router_w[e][h], the k largest per
+ * token in descending order (equal logits: lower expert id first), and
+ * w[t][j] = softmax over the k selected logits (FP64, rounded to FP32).
+ * Precision (L->router_mode):
+ *   MOE_ROUTER_EXACT      the selection is taken on FP64 sums of the exact
+ *                         products, so it does not depend on summation order
+ *                         (see route.hip)
+ *   MOE_ROUTER_SPLIT3_F32 FP32 logits from BF16 matrix-core products of x with
+ *                         the three exact BF16 pieces of router_w (FP32 sums),
+ *                         selected as they are: a reordered FP32 sum, which may
+ *                         resolve a near tie either way
+ *   MOE_ROUTER_BF16       router_w rounded to BF16 (nearest, ties to even),
+ *                         one BF16 matrix-core pass with FP32 sums, selected as
+ *                         is: a reduced-precision router, which also moves
+ *                         the logits by the rounding of the weights
+ * The two reduced modes need E % 128 == 0 and H % 32 == 0 (MOE_ESHAPE
+ * otherwise) and take the matrix cores at every T.
  *   x        [T][H] BF16 hidden states (bit patterns)
  *   logits_in [T][E] FP32, nullable: when given, these logits are used as is
- *             (test hook for tie-breaking rules)
+ *             (test hook for tie-breaking rules; the mode is then ignored)
  *   topk_idx [T][k] int32 out; topk_w [T][k] FP32 out
  * Pages: capy-flash README v0.5.4, "Measured" footnote (router on tensor cores
  * for prompt chunks; reordered sums may pick another of two tied experts).   */
@@ -157,7 +191,8 @@ int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t*
  *     gate_i, up_i = W13_e . dequant(xq, xs) in FP32, h_i = silu(gate_i)*up_i
  *     (hq, hs) = A4(h) per 16-block of I with a_gscale_mid
  *     y_rows[r][n] = W2_e[n] . dequant(hq, hs) in FP32
- *   y_shared[t][n]: the same with the shared expert for every token
+ *   y_shared[t][n]: the same with the shared expert for every token (times
+ *     the token's gate g_t when L->shared_gate_w is set)
  *   expert_off, row2pair as produced by moe_permute
  *   y_rows [T*k][H] FP32 out (permuted-row order)
  *   y_shared [T][H] FP32 out; nullable iff has_shared == 0
@@ -255,7 +290,17 @@ enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
                      uint8_t* scales, hipStream_t stream);
 
-/* K-step-major copy of one NVFP4 bank (the format of moe_nvfp4_bank: the
+/* The three BF16 pieces of a router (written once per layer, named in
+ * moe_layer.router_pieces): router_w[e][h] = p1 + p2 + p3 exactly, p1 = the
+ * upper 16 bits of the FP32 value, p2 those of the remainder, p3 those of the
+ * last remainder (truncation; FP32 keeps at most 24 significant bits, so three
+ * 8-bit pieces hold it exactly).  pieces_out [3][E][H] BF16.  This is the
+ * operand of the matrix-core router pass (capy-flash README v0.5.4, "Measured":
+ * the prompt router on tensor cores).
+ * Errors: MOE_ESHAPE (E < 1, H < 1), MOE_EINVAL (null or misaligned pointer). */
+int moe_pack_router(const float* router_w, int32_t E, int32_t H, uint16_t* pieces_out, hipStream_t stream);
+
+/* K-step-major copy of one NVFP4 bank/* K-step-major copy of one NVFP4 bank (the format of moe_nvfp4_bank: the
  * pages' 16-element E2M1 blocks with UE4M3 scales, Richland article, "What
  * shipped"), for the matrix-core kernels.  With S = K/64 steps of 64 elements:
  *   codes_out  [n_exp][S][N][32] : bytes 32s .. 32s+31 of row n (its elements

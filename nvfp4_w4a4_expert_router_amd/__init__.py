@@ -37,7 +37,11 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("has_shared", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("w13", Bank), ("w2", Bank),
                 ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float),
-                ("w13k", Bank), ("w2k", Bank), ("sh13k", Bank), ("sh2k", Bank)]
+                ("w13k", Bank), ("w2k", Bank), ("sh13k", Bank), ("sh2k", Bank), ("shared_gate_w", ctypes.c_void_p),
+                ("router_pieces", ctypes.c_void_p), ("router_mode", ctypes.c_int32), ("act_bits", ctypes.c_int32)]
+
+
+MOE_ROUTER_EXACT, MOE_ROUTER_SPLIT3_F32, MOE_ROUTER_BF16 = 0, 1, 2
 
 
 FFN_KERNELS = 3  # A4(x), gate/up + SwiGLU + A4(h), down
@@ -72,10 +76,11 @@ def _load():
     L.moe_layer_forward_noalloc.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug),
                                             vp]
     i32 = ctypes.c_int32
+    L.moe_pack_router.argtypes = [vp, i32, i32, vp, vp]
     L.moe_pack_kmajor.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
               "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32", "moe_pack_kmajor",
-              "moe_layer_forward_noalloc"):
+              "moe_layer_forward_noalloc", "moe_pack_router"):
         getattr(L, f).restype = ci
     return L
 
@@ -83,7 +88,8 @@ def _load():
 lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm", "moe_expert_ffn_krange",
-           "moe_combine_f32", "moe_pack_kmajor", "moe_noalloc_scratch_bytes", "moe_layer_forward_noalloc")
+           "moe_combine_f32", "moe_pack_kmajor", "moe_noalloc_scratch_bytes", "moe_layer_forward_noalloc",
+           "moe_pack_router")
 
 
 def strerror(code: int) -> str:
@@ -109,21 +115,47 @@ class MoELayer:
     """Device-resident layer parameters plus the C descriptor that points at them.
 
     router_w [E][H] float32; banks are dicts of uint8 codes / uint8 scales / float32
-    gscale tensors in the layouts of include/moe_nvfp4.h.  Tensors are kept alive here.
-    pack_kmajor() adds the K-step-major copies that the matrix-core kernels read.
+    gscale tensors in the layouts of include/moe_nvfp4.h; shared_gate_w [H] float32
+    (optional gate of the shared expert); router_mode MOE_ROUTER_*; act_bits 4.
+    Tensors are kept alive here.  pack_kmajor() adds the K-step-major copies that the
+    matrix-core kernels read, pack_router() the router's BF16 pieces.
     """
 
-    def __init__(self, H, I, E, k, router_w, w13, w2, sh13=None, sh2=None, a_gscale_in=1.0, a_gscale_mid=1.0):
+    def __init__(self, H, I, E, k, router_w, w13, w2, sh13=None, sh2=None, a_gscale_in=1.0, a_gscale_mid=1.0,
+                 shared_gate_w=None, router_mode=MOE_ROUTER_EXACT, act_bits=4):
         self.H, self.I, self.E, self.k = H, I, E, k
         self.has_shared = int(sh13 is not None)
         self.router_w, self.w13, self.w2, self.sh13, self.sh2 = router_w, w13, w2, sh13, sh2
+        self.shared_gate_w = shared_gate_w
 
         def bank(b):
             return Bank() if b is None else Bank(_ptr(b["codes"]), _ptr(b["scales"]), _ptr(b["gscale"]))
 
         self.desc = LayerDesc(H, I, E, k, self.has_shared, _ptr(router_w), bank(w13), bank(w2), bank(sh13), bank(sh2),
                               a_gscale_in, a_gscale_mid)
+        self.desc.shared_gate_w = _ptr(shared_gate_w)
+        self.desc.router_mode = router_mode
+        self.desc.act_bits = act_bits
         self.a_gscale_in, self.a_gscale_mid = a_gscale_in, a_gscale_mid
+        self.router_mode, self.act_bits = router_mode, act_bits
+
+    def pack_router(self, stream=None):
+        """Write the router's three BF16 pieces once (moe_pack_router) and name them in
+        the descriptor; returns self."""
+        self.router_pieces = torch.empty((3, self.E, self.H), dtype=torch.int16, device=self.router_w.device)
+        _check(lib.moe_pack_router(_ptr(self.router_w), self.E, self.H, _ptr(self.router_pieces), _stream(stream)),
+               "moe_pack_router")
+        self.desc.router_pieces = _ptr(self.router_pieces)
+        return self
+
+    def with_router_mode(self, mode):
+        """The same layer (same device tensors) with another router precision mode."""
+        other = MoELayer.__new__(MoELayer)
+        other.__dict__.update(self.__dict__)
+        other.desc = LayerDesc.from_buffer_copy(self.desc)
+        other.desc.router_mode = mode
+        other.router_mode = mode
+        return other
 
     def pack_kmajor(self, stream=None):
         """Write K-step-major copies of every bank (moe_pack_kmajor) and name them in

@@ -37,8 +37,13 @@ int check_shape(const moe_layer* L) {
   if (L->E < 1 || L->E > 1024) return MOE_ESHAPE;
   if (L->k < 1 || L->k > 32 || L->k > L->E) return MOE_ESHAPE;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ESHAPE;
+  if (L->router_mode < MOE_ROUTER_EXACT || L->router_mode > MOE_ROUTER_BF16) return MOE_ESHAPE;
+  if (L->act_bits != 0 && L->act_bits != 4) return MOE_ESHAPE;
   return MOE_OK;
 }
+
+// the shared expert's gate is applied only when the layer has a shared expert
+inline const float* shared_gate(const moe_layer* L) { return L->has_shared ? L->shared_gate_w : nullptr; }
 
 // Token counts: the router's and the matrix-core kernels' buffer resources
 // address a call's [T][H] BF16 rows with 32-bit offsets, and pair ids and
@@ -59,25 +64,29 @@ int check_kmajor(const moe_nvfp4_bank& b, int K) {
 int check_layer(const moe_layer* L, bool need_router, bool need_experts) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (need_router && !ptr_ok(L->router_w)) return MOE_EINVAL;
+  if (need_router) {
+    if (!ptr_ok(L->router_w) || !opt_ok(L->router_pieces)) return MOE_EINVAL;
+    if (!route_mode_supported(L->H, L->E, L->router_mode)) return MOE_ESHAPE;
+  }
   if (need_experts) {
     if ((rc = check_bank(L->w13)) || (rc = check_bank(L->w2))) return rc;
     if (L->has_shared && ((rc = check_bank(L->sh13)) || (rc = check_bank(L->sh2)))) return rc;
     if ((rc = check_kmajor(L->w13k, L->H)) || (rc = check_kmajor(L->w2k, L->I))) return rc;
     if (L->has_shared && ((rc = check_kmajor(L->sh13k, L->H)) || (rc = check_kmajor(L->sh2k, L->I)))) return rc;
     if (!pow2_scale(L->a_gscale_in) || !pow2_scale(L->a_gscale_mid)) return MOE_EINVAL;
+    if (!opt_ok(L->shared_gate_w)) return MOE_EINVAL;
   }
   return MOE_OK;
 }
 
 // workspace of each call, laid out from offset 0 (calls never overlap in time)
 
-size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E, L->H)); }
+size_t route_ws(const moe_layer* L, int64_t T) { return align_up(route_ws_bytes(T, L->E, L->H, L->router_mode)); }
 
 size_t permute_ws(const moe_layer* L, int64_t T) { return align_up(permute_ws_bytes(T, L->E)); }
 
 struct FfnWs {
-  size_t xq, xs, xh, hh, hq, hs, tiles, end;
+  size_t xq, xs, xh, hh, hq, hs, tiles, gate, end;
 };
 
 FfnWs ffn_ws(const moe_layer* L, int64_t T) {
@@ -98,6 +107,8 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   o = align_up(o + (size_t)R * (L->I / 16));
   w.tiles = o;
   o = align_up(o + ffn_mfma_ws_bytes(L->E, T, L->k, L->has_shared));
+  w.gate = o;  // the shared expert's per-token gate, when the layer has one
+  o = align_up(o + (shared_gate(L) ? (size_t)T * sizeof(float) : 0));
   w.end = o;
   return w;
 }
@@ -129,7 +140,8 @@ const char* moe_strerror(int code) {
 size_t fused_logits_ws(const moe_layer* L, int64_t T) {
   const int64_t t = T < 4 ? T : 4;
   return align_up((size_t)t * L->E * sizeof(double)) + align_up((size_t)t * L->k * sizeof(int4)) +
-         align_up((size_t)t * L->k * L->H * sizeof(float));
+         align_up((size_t)t * L->k * L->H * sizeof(float)) +
+         align_up(shared_gate(L) ? (size_t)t * sizeof(float) : 0);
 }
 
 size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
@@ -156,7 +168,7 @@ int moe_route(const moe_layer* L, const uint16_t* x, int64_t T, const float* log
     return MOE_EINVAL;
   }
   return launch_rc(launch_route(x, L->router_w, T, L->H, L->E, L->k, logits_in, topk_idx, topk_w,
-                                logits_in ? nullptr : ws, stream));
+                                logits_in ? nullptr : ws, L->router_mode, L->router_pieces, stream));
 }
 
 int moe_permute(const moe_layer* L, const int32_t* topk_idx, int64_t T, int32_t* expert_off, int32_t* row2pair,
@@ -262,6 +274,11 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   p.y_shared = L->has_shared ? y_shared : nullptr;
   p.kc0 = 16 * kb0;
   p.kc1 = 16 * kb1;
+  if (shared_gate(L)) {  // the shared expert's per-token gate, read by the down kernels
+    float* gate = reinterpret_cast<float*>(base + lay.gate);
+    if ((rc = launch_rc(launch_shared_gate(x, L->shared_gate_w, T, L->H, gate, stream)))) return rc;
+    p.sh_gate = gate;
+  }
   if (mfma_path)
     return launch_rc(launch_ffn_mfma(p, reinterpret_cast<int32_t*>(base + lay.tiles), stream, ev));
   if (decode_path) {
@@ -332,7 +349,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
   if (!debug_ok(dbg)) return MOE_EINVAL;
   const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
-  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps) {
+  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT) {
     if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_permute(L, topk_idx, T, expert_off, row2pair, pair2row, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_expert_ffn(L, x, T, expert_off, row2pair, y_rows, y_shared, dbg, ws, ws_bytes, stream))) return rc;
@@ -362,6 +379,14 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   q.off = expert_off;
   q.r2p = row2pair;
   q.p2r = pair2row;
+  float* gate = nullptr;
+  if (shared_gate(L)) {  // computed by the routing workgroup, read by the down kernel
+    gate = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +
+                                    align_up((size_t)T * L->k * sizeof(int4)) +
+                                    align_up((size_t)T * L->k * L->H * sizeof(float)));
+    q.wg = L->shared_gate_w;
+    q.gate = gate;
+  }
   if ((rc = launch_rc(launch_route_decode(q, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)))) return rc;
   // kernels 2, 3: gate/up and down over the slot table; kernel 4: combine
   FfnParams p = {};
@@ -395,6 +420,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.shared_split = 1;
   p.kc0 = 0;
   p.kc1 = L->I;
+  p.sh_gate = gate;
   // the down kernel also writes the routed rows in token-major order, so the
   // combine reads them without the dependent pair2row load (same values)
   p.y_tok = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +
@@ -410,6 +436,12 @@ int moe_rms_norm(const uint16_t* x, int64_t T, int32_t H, double eps, uint16_t* 
   if (T == 0) return MOE_OK;
   if (!ptr_ok(x) || !ptr_ok(out)) return MOE_EINVAL;
   return launch_rc(launch_rms_norm(x, T, H, eps, out, stream));
+}
+
+int moe_pack_router(const float* router_w, int32_t E, int32_t H, uint16_t* pieces_out, hipStream_t stream) {
+  if (E < 1 || H < 1) return MOE_ESHAPE;
+  if (!ptr_ok(router_w) || !ptr_ok(pieces_out)) return MOE_EINVAL;
+  return launch_rc(launch_pack_router(router_w, E, H, pieces_out, stream));
 }
 
 int moe_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int32_t n_exp, int32_t N, int32_t K,

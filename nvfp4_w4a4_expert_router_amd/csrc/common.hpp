@@ -149,6 +149,55 @@ __device__ __forceinline__ uint32_t encode_a4_block16(const float (&v)[16], floa
   return sc;
 }
 
+// ---------------------------------------------------------------- A8 (the W4A8 variant)
+// A8 keeps A4's 16-element blocks and UE4M3 block scale, chosen as
+// RNE(amax / (127 g)) (scale_code with 127 g in place of 6 g: the thresholds
+// 127 g x midpoint have at most 12 significant bits, exact in FP32), and
+// encodes each element as q = RNE(|v| / s) on the integers, saturating at 127,
+// with the sign of v (two's complement INT8; zero carries no sign).
+//
+// int8_code: a first guess from |v| times the reciprocal of s, then the exact
+// thresholds (m +- 1/2) s (at most 8 + 4 significant bits, exact in FP32)
+// move it to the rounding of the exact quotient, ties to the even integer.  The
+// guess is off by at most one.  s = +inf (scale code 0) gives 0.
+__device__ __forceinline__ int int8_code(float v, float s) {
+  const float a = fabsf(v);
+  int m = (int)__builtin_rintf(a * __builtin_amdgcn_rcpf(s));
+  m = m > 127 ? 127 : m;
+  if (m < 127) {
+    const float up = ((float)m + 0.5f) * s;
+    if (a > up || (a == up && (m & 1))) ++m;
+  }
+  if (m > 0) {
+    const float dn = ((float)m - 0.5f) * s;
+    if (a < dn || (a == dn && (m & 1))) --m;
+  }
+  return (__float_as_uint(v) >> 31) ? -m : m;
+}
+
+// 32 A8 codes (32 B: two 16-element blocks) times their UE4M3 scales (sc2: low
+// byte = first block) -> 32 FP16 values at dst (16-byte aligned).  Each value
+// q * s has at most 7 + 4 significant bits and magnitude at most 127 * 448:
+// exact in FP16.
+__device__ __forceinline__ void decode32_a8_fp16(uint4 q0, uint4 q1, uint32_t sc2, half_t* dst) {
+  const float s0 = ue4m3_value(sc2 & 0xFFu), s1 = ue4m3_value((sc2 >> 8) & 0xFFu);
+  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  half8_t out[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float s = d < 2 ? s0 : s1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = w[2 * d + i / 4];
+      const int q = (int)(int8_t)(uint8_t)(word >> (8 * (i & 3)));
+      out[d][i] = (half_t)((float)q * s);
+    }
+  }
+  half8_t* o = reinterpret_cast<half8_t*>(dst);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = out[d];
+}
+
 // Two E2M1 codes (byte kByte of w, low nibble first) -> two exact FP16 values
 template <int kByte>
 __device__ __forceinline__ half2_t fp4x2(uint32_t w) {
@@ -518,6 +567,12 @@ struct FfnParams {
   // partial; the full sum is kc0 = 0, kc1 = I).  Generic and matrix-core
   // kernels; kc0, kc1 multiples of 32 (of 64 on the matrix cores).
   int kc0, kc1;
+  // optional gate of the shared expert: [T] FP32 per-token factors (null: none);
+  // a shared output row is fl32(fl32(G * sum) * sh_gate[t])
+  const float* sh_gate;
+  // activation encoding: 0 = A4 (E2M1 codes, two per byte), 1 = A8 (INT8 codes,
+  // one per byte) for x codes, h codes and their dumps
+  int act8;
 };
 
 // Fused decode routing (moe_layer_forward, T <= 4): FP64 logits and A4(x),
@@ -536,6 +591,8 @@ struct RouteDecodeParams {
   int32_t* r2p;
   int32_t* p2r;
   int4* slot_tab;      // [T*k]
+  const float* wg;     // [H] shared-expert gate vector (null: no gate)
+  float* gate;         // [T] gate values out (when wg is set)
 };
 
 // Launch with optional events that take the kernel's own start (e0) and end
@@ -562,10 +619,15 @@ inline hipError_t record_idle(hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
 // kernel named by each, as launch_timed does
 hipError_t launch_quant_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,
                             uint8_t* scales, half_t* deq, hipStream_t s, hipEvent_t e0 = nullptr,
-                            hipEvent_t e1 = nullptr);
-size_t route_ws_bytes(int64_t T, int E, int H);
+                            hipEvent_t e1 = nullptr, int act_bits = 4);
+size_t route_ws_bytes(int64_t T, int E, int H, int mode);
+bool route_mode_supported(int H, int E, int mode);
+hipError_t launch_pack_router(const float* W, int E, int H, uint16_t* pieces, hipStream_t s);
+// per-token gate of the shared expert: gate[t] = fl32(sigmoid(x_t . wg)), the
+// dot in FP64 over exact products
+hipError_t launch_shared_gate(const uint16_t* x, const float* wg, int64_t T, int H, float* gate, hipStream_t s);
 hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int E, int k, const float* logits_in,
-                        int32_t* idx, float* w, void* ws, hipStream_t s);
+                        int32_t* idx, float* w, void* ws, int mode, const uint16_t* pieces, hipStream_t s);
 size_t permute_ws_bytes(int64_t T, int E);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* off, int32_t* r2p, int32_t* p2r,
                           void* ws, hipStream_t s);

@@ -157,7 +157,8 @@ constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use th
 // x are read from the workspace and decoded to FP16 in LDS while the weight
 // burst is in flight.
 constexpr int kGuCols = 32;  // intermediate columns per workgroup (gate and up rows: 2 kGuCols)
-template <bool kTable>
+// kA8: the W4A8 variant (x and h encoded by A8: INT8 codes, one byte each).
+template <bool kTable, bool kA8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
   constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
   __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
@@ -176,10 +177,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int xchunks = H / 32;
   const int xt = tid / xchunks, xc = tid % xchunks;
   const bool xmine = xt < T;  // T * H / 32 <= 256
-  uint4 xq4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 xq4 = make_uint4(0u, 0u, 0u, 0u), xq4b = make_uint4(0u, 0u, 0u, 0u);
   uint32_t xs2 = 0u;
   if (xmine) {
-    xq4 = *reinterpret_cast<const uint4*>(p.xq + (size_t)xt * (H / 2) + xc * 16);
+    if (kA8) {
+      const uint4* src = reinterpret_cast<const uint4*>(p.xq + (size_t)xt * H + xc * 32);
+      xq4 = src[0];
+      xq4b = src[1];
+    } else {
+      xq4 = *reinterpret_cast<const uint4*>(p.xq + (size_t)xt * (H / 2) + xc * 16);
+    }
     xs2 = *reinterpret_cast<const uint16_t*>(p.xs + (size_t)xt * (H / 16) + xc * 2);
   }
   // 2. this slot's expert and activation rows
@@ -228,7 +235,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   __builtin_amdgcn_sched_barrier(0);
   const float G = gsc * p.g_in;
   // 3. A4(x) to FP16 in LDS while the weights are in flight
-  if (xmine) decode32_fp16(xq4, xs2, xs + (size_t)xt * H + xc * 32);
+  if (xmine) {
+    if (kA8)
+      decode32_a8_fp16(xq4, xq4b, xs2, xs + (size_t)xt * H + xc * 32);
+    else
+      decode32_fp16(xq4, xs2, xs + (size_t)xt * H + xc * 32);
+  }
   if (tid < nrows) toks[tid] = shared ? row0 + tid : kTable ? (int)(((unsigned)ent.w >> (8 * tid)) & 0xFFu) : tok;
   // the scale transfers are complete once at most the kJ code loads are in flight
   static_assert(kJ == 16, "vmcnt immediate below");
@@ -267,17 +279,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float g = G * gu[rr][i], u = G * gu[rr][kGuCols + i];
     const float h = silu(g) * u;
     const float amax = row16_absmax(h);
-    const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
-    const float sv = ue4m3_value(scode);
-    const uint32_t c = elem_code_s(h, scode ? sv * p.g_mid : __builtin_inff());
-    const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
-    const half2_t hd = fp4x2<0>(c2) * half2_t{(half_t)sv, (half_t)sv};  // exact: <= 6 significant bits
     const int64_t orow = shared ? (int64_t)T * p.k + row0 + rr : (int64_t)row0 + rr;
     const int64_t col = (int64_t)cg * kGuCols + i;
-    if ((i & 1) == 0) *reinterpret_cast<uint32_t*>(p.hh + orow * I + col) = __builtin_bit_cast(uint32_t, hd);
+    if (kA8) {
+      const uint32_t scode = scale_code(amax, 127.0f * p.g_mid);
+      const float sv = ue4m3_value(scode);
+      const int q = int8_code(h, scode ? sv * p.g_mid : __builtin_inff());
+      p.hh[orow * I + col] = (half_t)((float)q * sv);  // exact: <= 11 significant bits
+      if (p.hq_dbg) p.hq_dbg[orow * I + col] = (uint8_t)(q & 0xFF);
+      if (p.hs_dbg && (i & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
+    } else {
+      const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
+      const float sv = ue4m3_value(scode);
+      const uint32_t c = elem_code_s(h, scode ? sv * p.g_mid : __builtin_inff());
+      const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
+      const half2_t hd = fp4x2<0>(c2) * half2_t{(half_t)sv, (half_t)sv};  // exact: <= 6 significant bits
+      if ((i & 1) == 0) *reinterpret_cast<uint32_t*>(p.hh + orow * I + col) = __builtin_bit_cast(uint32_t, hd);
+      if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)c2;
+      if (p.hs_dbg && (i & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
+    }
     if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-    if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)c2;
-    if (p.hs_dbg && (i & 15) == 0) p.hs_dbg[orow * (I / 16) + col / 16] = (uint8_t)scode;
   }
 }
 
@@ -357,6 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   for (int j = 0; j < kJ; ++j) sc[j] = *reinterpret_cast<const uint16_t*>(&sct[w][j][2 * l]);
   const float G = gsc * p.g_mid;
   float* dst0 = shared ? p.y_shared + (int64_t)row0 * H : p.y_rows + (int64_t)row0 * H;
+  const float* gate = shared && p.sh_gate ? p.sh_gate + row0 : nullptr;  // shared rows are tokens row0..
   // pair ids of the slot's rows for the token-major copy (loaded with the burst in flight)
   int pair[kDecMaxT] = {};
   const bool tok_copy = p.y_tok != nullptr && !shared;
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       for (int i = 0; i < kKeep; ++i) {
         const int n = base_n + kRPI * (w + 4 * (jb + i));
         if (n < H) {
-          dst0[(int64_t)rr * H + n] = G * acc[i];
+          dst0[(int64_t)rr * H + n] = gate ? (G * acc[i]) * gate[rr] : G * acc[i];
           if (tok_copy) {
             int pr = pair[0];
 #pragma unroll
@@ -413,8 +435,12 @@ hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev
   const int slots = decode_slots(p);
   if (slots == 0) return record_idle(s, ev_before, ev_after);
   const dim3 grid((unsigned)(slots * (p.I / kGuCols)));
-  if (p.slot_tab) return launch_timed(k_gateup_decode<true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
-  return launch_timed(k_gateup_decode<false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  if (p.act8) {
+    if (p.slot_tab) return launch_timed(k_gateup_decode<true, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+    return launch_timed(k_gateup_decode<false, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  }
+  if (p.slot_tab) return launch_timed(k_gateup_decode<true, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  return launch_timed(k_gateup_decode<false, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
 }
 
 bool fused_decode_supported(int H, int I, int E, int k, int64_t T) {

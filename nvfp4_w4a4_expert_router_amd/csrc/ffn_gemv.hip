@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_ffn_down(FfnParams p) {
         const float y = G * sum;
         const int64_t col = (int64_t)nb * kWRows + w;
         if (si.shared)
-          p.y_shared[(int64_t)(r0 + rr) * H + col] = y;
+          p.y_shared[(int64_t)(r0 + rr) * H + col] = p.sh_gate ? y * p.sh_gate[r0 + rr] : y;
         else
           p.y_rows[(int64_t)(si.row0 + r0 + rr) * H + col] = y;
       }

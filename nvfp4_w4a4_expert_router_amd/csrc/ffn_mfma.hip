@@ -419,6 +419,24 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
   const uint32_t voff0 = (uint32_t)(4 * (lane >> 5) * H) * 4u;
+  if (shared && p.sh_gate) {
+    // shared rows are tokens m0 + row: each scaled by its gate (rows past the
+    // segment read the last token's and are dropped by the store's range check)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int dm = 32 * i + 8 * (q >> 2) + (q & 3) + 4 * (lane >> 5);
+        const float gr = p.sh_gate[m0 + dm < T ? m0 + dm : T - 1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = nt * kBN + bj(j) + (lane & 31);
+          buffer_store4_nt(__float_as_uint((G * acc[i][j][q]) * gr), y_r,
+                           voff0 + (uint32_t)((dm - 4 * (lane >> 5)) * H * 4) + (uint32_t)(n * 4));
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -285,10 +285,11 @@ __global__ __launch_bounds__(256) void k_down_stream(FfnParams p, int lpr_log2) 
     }
     if (ch == 0) {
       float* dst = si.shared ? p.y_shared + (int64_t)rr * H : p.y_rows + ((int64_t)si.row0 + rr) * H;
+      const float gr = si.shared && p.sh_gate ? p.sh_gate[rr] : 1.0f;  // shared row rr is token rr
 #pragma unroll
       for (int j = 0; j < kDRows; ++j) {
         const int n = n0 + rpp * j;
-        if (n < H) dst[n] = G * part[j];
+        if (n < H) dst[n] = si.shared && p.sh_gate ? (G * part[j]) * gr : G * part[j];
       }
     }
   }

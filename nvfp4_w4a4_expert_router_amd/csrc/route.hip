@@ -108,14 +108,25 @@ __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ 
   Wp[2 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-// LDS stage: 256 token rows and 3 x 128 expert rows of a K step (64 B = 4 chunks
-// of 16 B per row; chunk c of row r sits in slot c ^ f(r), f(r) = bit 2 of r plus
-// twice (bit 1 xor bit 3), so the MFMA reads of 16 consecutive rows fall in 16
-// different 16-byte bank groups).  A ring of 3 stages (120 KB, one workgroup per
-// CU) filled by buffer loads that write LDS directly, two steps ahead.
+// W [E][H] FP32 -> Wp [E][H] BF16, round to nearest even: the operand of the
+// reduced-precision (BF16) router mode
+__global__ __launch_bounds__(256) void k_router_round_bf16(const float* __restrict__ W, int64_t n,
+                                                           uint16_t* __restrict__ Wp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  Wp[i] = f32_to_bf16_rne(W[i]);
+}
+
+// LDS stage: 256 token rows and NP x 128 expert rows of a K step (64 B = 4
+// chunks of 16 B per row; chunk c of row r sits in slot c ^ f(r), f(r) = bit 2
+// of r plus twice (bit 1 xor bit 3), so the MFMA reads of 16 consecutive rows
+// fall in 16 different 16-byte bank groups).  A ring of 3 stages (120 KB with
+// 3 pieces, one workgroup per CU) filled by buffer loads that write LDS
+// directly, two steps ahead.
+template <int NP>
 struct RouterRing {
   uint4 a[RM_S][RM_T * 4];
-  uint4 b[RM_S][3][RM_E * 4];
+  uint4 b[RM_S][NP][RM_E * 4];
 };
 
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
@@ -125,10 +136,14 @@ typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 // one MFMA per wave, each A fragment four).  K order inside a step is
 // lane-contiguous (lanes 0..31 supply elements 8s.., lanes 32..63 16+8s.. in
 // MFMA s), the same for both operands.
+// NP: BF16 pieces per router row (3: the exact split; 1: a BF16 router).
+template <int NP>
 __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ Wp, int T, int H, int E,
                                                             float* __restrict__ logits) {
-  __shared__ RouterRing ring;
+  static_assert(NP == 1 || NP == 3, "pieces");
+  constexpr int kWaitStep = NP == 3 ? 0xF75 : 0xF73;  // vmcnt(2 + NP), expcnt 7, lgkmcnt 15
+  __shared__ RouterRing<NP> ring;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   // expert tile major within each XCD's run: one XCD keeps one expert tile's
   // router rows (3 pieces x 128 rows x H) in its L2 while token tiles stream by
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
   const int t0 = (lt % ntb) * RM_T, e0 = (lt / ntb) * RM_E;
   const int n = H / RM_K;
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * H * 2u);
-  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(Wp, 3u * E * H * 2u);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(Wp, (uint32_t)NP * E * H * 2u);
   // transfers: lane -> row (lane / 4) of a 16-row group, slot lane % 4
   auto swz_of = [](int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); };
   const uint32_t sw = (uint32_t)(((lane & 3) ^ swz_of(lane >> 2)) * 16);
@@ -148,7 +163,7 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
     aoff[i] = (uint32_t)(ta < T ? ta : T - 1) * H * 2u + sw;  // rows past T repeat the last; dropped
   }
   const uint32_t boff = (uint32_t)(e0 + (lane >> 2)) * H * 2u + sw;
-  // two A and three B transfers per wave and step (steps past the last repeat it)
+  // two A and NP B transfers per wave and step (steps past the last repeat it)
   auto dma = [&](int t, int st) {
     const uint32_t k0 = (uint32_t)((t < n ? t : n - 1) * RM_K);
 #pragma unroll
@@ -156,8 +171,8 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&ring.a[st][(32 * wave + 16 * i) * 4], 16, aoff[i],
                                                k0 * 2, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int q = 3 * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
+    for (int i = 0; i < NP; ++i) {
+      const int q = NP * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&ring.b[st][pc][16 * c * 4], 16, boff,
                                                k0 * 2 + (uint32_t)(pc * E + 16 * c) * H * 2u, 0, 0);
     }
@@ -170,11 +185,11 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
   }
   const int hk = lane >> 5, r32 = lane & 31;
   const int swz = swz_of(r32);
-  // vmcnt(5): the newest step's transfers may be in flight, the one before is
-  // complete (the barrier then publishes it)
+  // vmcnt(2 + NP): the newest step's transfers may be in flight, the one before
+  // is complete (the barrier then publishes it)
   dma(0, 0);
   dma(1, 1);
-  __builtin_amdgcn_s_waitcnt(0xF75);
+  __builtin_amdgcn_s_waitcnt(kWaitStep);
   __syncthreads();
   int st = 0;  // t % 3
   for (int t = 0; t < n; ++t) {
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
       const int slot = (2 * hk + s2) ^ swz;
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring.a[st][(32 * wave + r32) * 4 + slot]);
 #pragma unroll
-      for (int pc = 2; pc >= 0; --pc)
+      for (int pc = NP - 1; pc >= 0; --pc)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ring.b[st][pc][(32 * j + r32) * 4 + slot]);
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
         grp[j] = floatx16{};
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xF75);  // this wave's transfers for step t + 1 are complete
+    __builtin_amdgcn_s_waitcnt(kWaitStep);  // this wave's transfers for step t + 1 are complete
     __syncthreads();
     st = st == 2 ? 0 : st + 1;
   }
@@ -273,6 +288,26 @@ struct RoutingLds {
   int4 slot[kRdMaxT * 32];  // slot table, written out after the last barrier
   int wsum[4], wnz[4];      // per-wave totals of the scan
 };
+
+// ---------------------------------------------------------------- shared-expert gate
+// z = sum_h x[t][h] * wg[h] over one wave (two elements per lane and step, FP64
+// sums of exact BF16 x FP32 products, a fixed reduction order), then
+// gate = fl32(1 / (1 + exp(-z))) in FP64.  An optional gate on the shared
+// expert is not on the pages (they list the shared expert as always on); this
+// is the plainest form such a gate takes.
+__device__ __forceinline__ float shared_gate_wave(const uint16_t* __restrict__ xr, const float* __restrict__ wg,
+                                                  int H) {
+  const int lane = lane_id();
+  double a = 0.0;
+  for (int h = 2 * lane; h < H; h += 2 * kWave) {
+    const uint32_t xv = *reinterpret_cast<const uint32_t*>(xr + h);
+    const float2 w = *reinterpret_cast<const float2*>(wg + h);
+    a = fma((double)__uint_as_float(xv << 16), (double)w.x, a);
+    a = fma((double)__uint_as_float(xv & 0xFFFF0000u), (double)w.y, a);
+  }
+  const double z = wave_sum_f64(a);
+  return (float)(1.0 / (1.0 + exp(-z)));
+}
 
 // The routing of all T tokens in one workgroup (wave t takes token t).  Rows
 // of an expert are in token order, so a pair's row is the expert's offset
@@ -353,6 +388,10 @@ __device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, Routing
     q.w[pi] = my_w;
     q.p2r[pi] = row;
     q.r2p[row] = pi;
+  }
+  if (q.wg && wave < T) {  // the shared expert's gate of token `wave`
+    const float g = shared_gate_wave(q.x + (int64_t)wave * q.H, q.wg, q.H);
+    if (lane == 0) q.gate[wave] = g;
   }
 }
 
@@ -800,6 +839,20 @@ __global__ __launch_bounds__(256) void k_route_select_refine(RouteB p) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_shared_gate(const uint16_t* __restrict__ x, const float* __restrict__ wg,
+                                                     int64_t T, int H, float* __restrict__ gate) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float g = shared_gate_wave(x + t * H, wg, H);
+  if (lane_id() == 0) gate[t] = g;
+}
+
+hipError_t launch_shared_gate(const uint16_t* x, const float* wg, int64_t T, int H, float* gate, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_shared_gate, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, wg, T, H, gate);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 bool route_decode_supported(int H, int E, int k, int64_t T) {
   return T >= 1 && T <= kRdMaxT && E <= kRdMaxE && k <= 32 && H % 32 == 0;
@@ -820,18 +873,30 @@ static float gamma_for_depth(int d) {
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-static bool router_mfma_ok(int64_t T, int H, int E) { return T > kGemvMaxT && E % RM_E == 0 && H % RM_K == 0; }
+static bool router_mfma_shape(int H, int E) { return E % RM_E == 0 && H % RM_K == 0; }
+
+static bool router_mfma_ok(int64_t T, int H, int E) { return T > kGemvMaxT && router_mfma_shape(H, E); }
+
+bool route_mode_supported(int H, int E, int mode) { return mode == MOE_ROUTER_EXACT || router_mfma_shape(H, E); }
 
 // logits (FP64 at decode, FP32 otherwise), ||W_e|| and, on the matrix-core
-// path, the three BF16 pieces of W
-size_t route_ws_bytes(int64_t T, int E, int H) {
-  const size_t lg = T <= kGemvMaxT ? (size_t)(T * E) * sizeof(double) : (size_t)(T * E) * sizeof(float);
-  const size_t pieces = router_mfma_ok(T, H, E) ? 3 * (size_t)E * H * sizeof(uint16_t) : 0;
+// path, the BF16 pieces of W (three; one in the BF16 mode)
+size_t route_ws_bytes(int64_t T, int E, int H, int mode) {
+  const bool mfma = mode != MOE_ROUTER_EXACT || router_mfma_ok(T, H, E);
+  const size_t lg = (T <= kGemvMaxT && mode == MOE_ROUTER_EXACT) ? (size_t)(T * E) * sizeof(double)
+                                                                   : (size_t)(T * E) * sizeof(float);
+  const size_t pieces = mfma ? (mode == MOE_ROUTER_BF16 ? 1 : 3) * (size_t)E * H * sizeof(uint16_t) : 0;
   return align256(lg) + align256((size_t)E * sizeof(float)) + align256(pieces);
 }
 
+hipError_t launch_pack_router(const float* W, int E, int H, uint16_t* pieces, hipStream_t s) {
+  const int64_t nw = (int64_t)E * H;
+  hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, pieces);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int E, int k, const float* logits_in,
-                        int32_t* idx, float* w, void* ws, hipStream_t s) {
+                        int32_t* idx, float* w, void* ws, int mode, const uint16_t* pieces, hipStream_t s) {
   RouteB p = {};
   p.T = T;
   p.H = H;
@@ -844,7 +909,7 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
   if (logits_in) {
     p.l32 = logits_in;
     p.mode = kSelF32;
-  } else if (T <= kGemvMaxT) {
+  } else if (T <= kGemvMaxT && mode == MOE_ROUTER_EXACT) {
     RouteDecodeParams q = {};
     q.x = x;
     q.W = W;
@@ -860,23 +925,35 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
     float* lg = static_cast<float*>(ws);
     char* after_lg = static_cast<char*>(ws) + align256((size_t)(T * E) * sizeof(float));
     float* wn = reinterpret_cast<float*>(after_lg);
-    if (router_mfma_ok(T, H, E)) {
-      uint16_t* wp = reinterpret_cast<uint16_t*>(after_lg + align256((size_t)E * sizeof(float)));
-      const int64_t nw = (int64_t)E * H;
-      hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
-      const dim3 grid((unsigned)(E / RM_E), (unsigned)((T + RM_T - 1) / RM_T));
-      hipLaunchKernelGGL(k_router_logits_mfma, grid, dim3(512), 0, s, x, (const uint16_t*)wp, (int)T, H, E, lg);
+    uint16_t* wp = reinterpret_cast<uint16_t*>(after_lg + align256((size_t)E * sizeof(float)));
+    const int64_t nw = (int64_t)E * H;
+    const dim3 grid((unsigned)(E / RM_E), (unsigned)((T + RM_T - 1) / RM_T));
+    if (mode == MOE_ROUTER_BF16) {  // one BF16 pass on the rounded router, selection on its FP32 logits
+      hipLaunchKernelGGL(k_router_round_bf16, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
+      hipLaunchKernelGGL(k_router_logits_mfma<1>, grid, dim3(512), 0, s, x, (const uint16_t*)wp, (int)T, H, E, lg);
+      p.l32 = lg;
+      p.mode = kSelF32;
+    } else if (mode == MOE_ROUTER_SPLIT3_F32 || router_mfma_ok(T, H, E)) {
+      if (!pieces) {
+        hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
+        pieces = wp;
+      }
+      hipLaunchKernelGGL(k_router_logits_mfma<3>, grid, dim3(512), 0, s, x, pieces, (int)T, H, E, lg);
       // u = 2^-23 (twice the FP32 unit roundoff), and the pieces' 1 + 2^-7 + 2^-14
       p.gamma = 2.0f * gamma_for_depth(3 * 2 * 16 + 8 + (H / RM_K + 7) / 8) * (1.0f + 0x1p-6f);
+      p.l32 = lg;
+      p.mode = mode == MOE_ROUTER_SPLIT3_F32 ? kSelF32 : kSelRefine;
     } else {
-      const dim3 grid((unsigned)((E + RE - 1) / RE), (unsigned)((T + RT - 1) / RT));
-      hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(256), 0, s, x, W, (int)T, H, E, lg);
+      const dim3 tgrid((unsigned)((E + RE - 1) / RE), (unsigned)((T + RT - 1) / RT));
+      hipLaunchKernelGGL(k_router_logits_tiled, tgrid, dim3(256), 0, s, x, W, (int)T, H, E, lg);
       p.gamma = gamma_for_depth(RK + H / RK);
+      p.l32 = lg;
+      p.mode = kSelRefine;
     }
-    hipLaunchKernelGGL(k_router_norms, dim3((E + 3) / 4), dim3(256), 0, s, W, H, E, wn);
-    p.l32 = lg;
-    p.wnorm = wn;
-    p.mode = kSelRefine;
+    if (p.mode == kSelRefine) {
+      hipLaunchKernelGGL(k_router_norms, dim3((E + 3) / 4), dim3(256), 0, s, W, H, E, wn);
+      p.wnorm = wn;
+    }
   }
   if (p.mode == kSelRefine && E <= 512 && k <= 32 && H % 2048 == 0)
     hipLaunchKernelGGL(k_route_select_refine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, p);

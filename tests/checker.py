@@ -83,6 +83,43 @@ def check_topk(idx_g, w_g, logits64, k, rep: Report):
     return idx_ad.astype(np.int32), w_ad.astype(np.float32)
 
 
+def check_topk_radius(idx_g, w_g, logits64, radius, k, rep: Report):
+    """A reduced-precision router against the oracle's top k on that router's own
+    FP64 logits: every difference must lie within the kernel's FP32 error radius
+    (radius[t][e] bounds |l32 - l64| for each logit), since FP32 sums in another
+    order may resolve a near tie either way (capy-flash README v0.5.4, "Measured",
+    footnote on the tensor-core router).  The weights are the softmax of FP32
+    logits, so they may move by the same radius.  Returns the number of tokens
+    whose selected set differs from the oracle's on these logits."""
+    idx_o, _ = oracle.topk_softmax(logits64, k)
+    T, E = logits64.shape
+    flips = 0
+    for t in np.where((idx_g != idx_o).any(axis=1))[0]:
+        l, r = logits64[t], radius[t]
+        sg, so = set(idx_g[t].tolist()), set(idx_o[t].tolist())
+        assert len(sg) == k and all(0 <= e < E for e in sg), "token %d: invalid ids %s" % (t, idx_g[t])
+        for a in sg - so:
+            for b in so - sg:
+                assert l[b] - l[a] <= r[a] + r[b], "token %d: chose %d over %d, margin %.3g > radius %.3g" % (
+                    t, a, b, l[b] - l[a], r[a] + r[b])
+        seq = idx_g[t]
+        for j in range(k - 1):
+            a, b = seq[j], seq[j + 1]
+            assert l[a] >= l[b] - (r[a] + r[b]), "token %d: slot order %d,%d" % (t, a, b)
+        flips += sg != so
+    sel = np.take_along_axis(logits64, idx_g.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    w_o = ex / ex.sum(axis=1, keepdims=True)
+    rmax = np.take_along_axis(radius, idx_g.astype(np.int64), axis=1).max(axis=1, keepdims=True)
+    err = np.abs(w_g.astype(np.float64) - w_o)
+    tol = 2.0 * w_o * (2.0 * rmax) + 1e-6 * w_o + 1e-7
+    assert np.all(err <= tol), "router weights beyond the radius: worst %.3g" % (err - tol).max()
+    s = w_g.astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(s - 1.0) <= 16 * 2.0 ** -24)
+    rep["set_flips_within_radius"] = int(flips)
+    return flips
+
+
 def check_permutation(idx_ad, E, off_g, r2p_g, p2r_g):
     off, r2p, p2r = oracle.permute(idx_ad, E)
     assert np.array_equal(off_g, off), "expert_off differs"

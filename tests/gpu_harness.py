@@ -36,8 +36,10 @@ def device_layer(L, router_w=None, kmajor=True) -> moe.MoELayer:
     matrix-core kernels read (the product configuration)."""
     sh = L.shape
     rw = L.router_w if router_w is None else router_w
+    wg = getattr(L, "shared_gate_w", None)
     DL = moe.MoELayer(sh.H, sh.I, sh.E, sh.k, to_dev(rw), bank_to_dev(L.w13), bank_to_dev(L.w2),
-                      bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid)
+                      bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid,
+                      shared_gate_w=None if wg is None else to_dev(wg))
     if kmajor and sh.H % 64 == 0 and sh.I % 64 == 0:
         DL.pack_kmajor()
     return DL
@@ -124,6 +126,9 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
         s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
                                  L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s)
         y_sh = s_t["y"]
+        wg = getattr(L, "shared_gate_w", None)
+        if wg is not None:  # the shared expert's rows times the token's gate
+            y_sh = y_sh * oracle.shared_gate(x[tok], wg).astype(np.float64)[:, None]
         checker.check_fp32_rows(g["y_shared"][tok], y_sh, rep, "y_shared")
     checker.check_fp32_rows(g["y_rows"][rows], r_t["y"], rep, "y_rows")
     resid = None if residual is None else residual[tok]
@@ -187,6 +192,9 @@ def check_krange(L, x, g, part, kb0, kb1, rep=None):
         hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
                                            L.a_gscale_mid, rep, "hsh")
         y_sh = oracle.expert_rows(tok, np.zeros(T, np.int32), *sargs, kb=(kb0, kb1), hq_in=hq_s, hs_in=hs_s)["y"]
+        wg = getattr(L, "shared_gate_w", None)
+        if wg is not None:
+            y_sh = y_sh * oracle.shared_gate(x, wg).astype(np.float64)[:, None]
         checker.check_fp32_rows(part["y_shared"], y_sh, rep, "y_shared_part")
     o64, _ = oracle.combine(r_t["y"].reshape(T, sh.k, sh.H), w_ad, y_sh)
     rms = float(np.sqrt(np.mean(o64 ** 2)))

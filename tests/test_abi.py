@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.lib.moe_abi_version() == 2
+    assert moe.lib.moe_abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert moe.strerror(code) and moe.strerror(code) != "unknown error"
     assert moe.strerror(-99) == "unknown error"
@@ -98,6 +98,31 @@ def test_negative_T_and_zero_T():
     assert moe.lib.moe_expert_ffn(ctypes.byref(L), None, 0, None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert moe.lib.moe_combine(ctypes.byref(L), 0, None, None, None, None, None, None, None) == moe.MOE_OK
     assert moe.lib.moe_quantize_act(None, 0, 0, 64, 1.0, None, None, None) == moe.MOE_OK
+
+
+def test_router_mode_gate_and_act_bits_validated():
+    """Router precision modes, the shared-expert gate vector, the cached router pieces
+    and the activation width are checked on the host."""
+    for mode in (-1, 3):
+        assert route(layer(router_mode=mode)) == moe.MOE_ESHAPE
+    for bits in (1, 5, 16):
+        assert route(layer(act_bits=bits)) == moe.MOE_ESHAPE
+    # the reduced-precision routers run on the matrix cores: E a multiple of 128
+    for mode in (moe.MOE_ROUTER_SPLIT3_F32, moe.MOE_ROUTER_BF16):
+        assert route(layer(E=96, router_mode=mode), wsb=0) == moe.MOE_ESHAPE
+        assert route(layer(router_mode=mode), wsb=0) == moe.MOE_EWORKSPACE
+    assert route(layer(E=96), wsb=0) == moe.MOE_EWORKSPACE  # the exact router takes any E
+    assert route(layer(router_pieces=FAKE + 8)) == moe.MOE_EINVAL
+    bad_gate = layer(shared_gate_w=FAKE + 4)
+    rc = moe.lib.moe_expert_ffn(ctypes.byref(bad_gate), FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == moe.MOE_EINVAL
+    # a gate adds T floats of workspace, only with a shared expert
+    base = moe.lib.moe_workspace_bytes(ctypes.byref(layer()), 4096)
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(layer(shared_gate_w=FAKE)), 4096) > base
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(layer(shared=0, shared_gate_w=FAKE)), 4096) == \
+        moe.lib.moe_workspace_bytes(ctypes.byref(layer(shared=0)), 4096)
+    assert moe.lib.moe_pack_router(FAKE, 0, 2048, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_pack_router(FAKE, 512, 2048, None, None) == moe.MOE_EINVAL
 
 
 def test_token_bound():
