@@ -101,7 +101,14 @@ typedef struct {
  *   router_mode : MOE_ROUTER_EXACT (0, the default), MOE_ROUTER_SPLIT3_F32 or
  *         MOE_ROUTER_BF16; see moe_route.
  *   act_bits : activation encoding of x and h: 0 or 4 = A4 (W4A4, the
- *         default); other values are MOE_ESHAPE.                              */
+ *         default); 8 = A8, the W4A8 variant (the pages' older host path,
+ *         capy-flash README v0.5.4, "Serve"; its format is not given there):
+ *         the same 16-element blocks and UE4M3 block scale, chosen as
+ *         RNE(amax / (127 g)), with INT8 element codes q = RNE(x / (s g))
+ *         saturating at +-127.  A power-of-two activation global scale below 1
+ *         (e.g. 2^-4 for N(0,1) hidden states) keeps its block scales in UE4M3's
+ *         normal range.  Other values are MOE_ESHAPE.  A8 layers run the
+ *         separate calls (moe_layer_forward does not fuse them).            */
 typedef struct {
   int32_t H, I, E, k, has_shared;
   const float* router_w;
@@ -117,9 +124,10 @@ typedef struct {
 enum { MOE_ROUTER_EXACT = 0, MOE_ROUTER_SPLIT3_F32 = 1, MOE_ROUTER_BF16 = 2 };
 
 /* Optional dumps of intermediate values (all nullable, device pointers).
- *   xq [T][H/2], xs [T][H/16] : A4 encoding of x (codes, UE4M3 scales)
- *   h  [R][I] FP32            : h = silu(gate) * up before its A4 encoding
- *   hq [R][I/2], hs [R][I/16] : A4 encoding of h
+ *   xq [T][H/2], xs [T][H/16] : A4 encoding of x (codes, UE4M3 scales);
+ *                               A8 layers: xq [T][H] INT8 codes
+ *   h  [R][I] FP32            : h = silu(gate) * up before its encoding
+ *   hq [R][I/2], hs [R][I/16] : A4 encoding of h; A8 layers: hq [R][I] INT8
  * R = T*k routed rows in permuted-row order, followed by T shared-expert rows
  * (token order) when has_shared.
  *   events (host array, nullable): 2*MOE_FFN_KERNELS created HIP events (a null
@@ -300,7 +308,27 @@ int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float
  * Errors: MOE_ESHAPE (E < 1, H < 1), MOE_EINVAL (null or misaligned pointer). */
 int moe_pack_router(const float* router_w, int32_t E, int32_t H, uint16_t* pieces_out, hipStream_t stream);
 
-/* K-step-major copy of one NVFP4 bank/* K-step-major copy of one NVFP4 bank (the format of moe_nvfp4_bank: the
+/* A8 encoding (the W4A8 variant's, see moe_layer.act_bits) of a row-major
+ * [rows][cols] matrix (cols % 16 == 0): codes [rows][cols] INT8 out, scales
+ * [rows][cols/16] out.  Per 16-element block: scale = RNE(amax/(127*gscale))
+ * on the UE4M3 grid, saturating at 448; codes = RNE(x/(scale*gscale)) on the
+ * integers, saturating at +-127.  Exact (decided by comparisons with exact
+ * thresholds).  Errors and dtype as moe_quantize_act.
+ * Pages: capy-flash README v0.5.4, "Serve" (the older W4A8 host path).      */
+int moe_quantize_act8(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, int8_t* codes,
+                      uint8_t* scales, hipStream_t stream);
+
+/* K-step-major copy of one NVFP4 bank/* A8 encoding (the W4A8 variant's, see moe_layer.act_bits) of a row-major
+ * [rows][cols] matrix (cols % 16 == 0): codes [rows][cols] INT8 out, scales
+ * [rows][cols/16] out.  Per 16-element block: scale = RNE(amax/(127*gscale))
+ * on the UE4M3 grid, saturating at 448; codes = RNE(x/(scale*gscale)) on the
+ * integers, saturating at +-127.  Exact (decided by comparisons with exact
+ * thresholds).  Errors and dtype as moe_quantize_act.
+ * Pages: capy-flash README v0.5.4, "Serve" (the older W4A8 host path).      */
+int moe_quantize_act8(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, int8_t* codes,
+                      uint8_t* scales, hipStream_t stream);
+
+/* K-step-major copy of one NVFP4 bank (the format of moe_nvfp4_bank: the
  * pages' 16-element E2M1 blocks with UE4M3 scales, Richland article, "What
  * shipped"), for the matrix-core kernels.  With S = K/64 steps of 64 elements:
  *   codes_out  [n_exp][S][N][32] : bytes 32s .. 32s+31 of row n (its elements

@@ -67,6 +67,7 @@ def _load():
     L.moe_expert_ffn.argtypes = [pl, vp, i64, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz, vp]
     L.moe_combine.argtypes = [pl, i64, vp, vp, vp, vp, vp, vp, vp]
     L.moe_quantize_act.argtypes = [vp, ci, i64, ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+    L.moe_quantize_act8.argtypes = [vp, ci, i64, ctypes.c_int32, ctypes.c_float, vp, vp, vp]
     L.moe_layer_forward.argtypes = [pl, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug), vp, sz,
                                     vp]
     L.moe_rms_norm.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_double, vp, vp]
@@ -80,7 +81,7 @@ def _load():
     L.moe_pack_kmajor.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_quantize_act", "moe_layer_forward",
               "moe_rms_norm", "moe_expert_ffn_krange", "moe_combine_f32", "moe_pack_kmajor",
-              "moe_layer_forward_noalloc", "moe_pack_router"):
+              "moe_layer_forward_noalloc", "moe_pack_router", "moe_quantize_act8"):
         getattr(L, f).restype = ci
     return L
 
@@ -89,7 +90,7 @@ lib = _load()
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_combine", "moe_quantize_act", "moe_layer_forward", "moe_rms_norm", "moe_expert_ffn_krange",
            "moe_combine_f32", "moe_pack_kmajor", "moe_noalloc_scratch_bytes", "moe_layer_forward_noalloc",
-           "moe_pack_router")
+           "moe_pack_router", "moe_quantize_act8")
 
 
 def strerror(code: int) -> str:
@@ -116,7 +117,8 @@ class MoELayer:
 
     router_w [E][H] float32; banks are dicts of uint8 codes / uint8 scales / float32
     gscale tensors in the layouts of include/moe_nvfp4.h; shared_gate_w [H] float32
-    (optional gate of the shared expert); router_mode MOE_ROUTER_*; act_bits 4.
+    (optional gate of the shared expert); router_mode MOE_ROUTER_*; act_bits 4 (W4A4)
+    or 8 (the W4A8 variant).
     Tensors are kept alive here.  pack_kmajor() adds the K-step-major copies that the
     matrix-core kernels read, pack_router() the router's BF16 pieces.
     """
@@ -238,6 +240,15 @@ def moe_quantize_act(x, codes, scales, gscale=1.0, stream=None):
     rows, cols = x.shape
     _check(lib.moe_quantize_act(_ptr(x), dtype, rows, cols, gscale, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize_act")
+
+
+def moe_quantize_act8(x, codes, scales, gscale=1.0, stream=None):
+    """A8 encoding (the W4A8 variant's): codes int8 [rows][cols], scales [rows][cols/16]."""
+    dtype = {torch.bfloat16: MOE_DTYPE_BF16, torch.int16: MOE_DTYPE_BF16, torch.uint16: MOE_DTYPE_BF16,
+             torch.float32: MOE_DTYPE_F32}[x.dtype]
+    rows, cols = x.shape
+    _check(lib.moe_quantize_act8(_ptr(x), dtype, rows, cols, gscale, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_act8")
 
 
 def moe_expert_ffn_krange(layer: MoELayer, x, expert_off, row2pair, kb0, kb1, y_rows, y_shared, ws, T=None,

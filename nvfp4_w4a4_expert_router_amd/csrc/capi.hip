@@ -38,9 +38,12 @@ int check_shape(const moe_layer* L) {
   if (L->k < 1 || L->k > 32 || L->k > L->E) return MOE_ESHAPE;
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ESHAPE;
   if (L->router_mode < MOE_ROUTER_EXACT || L->router_mode > MOE_ROUTER_BF16) return MOE_ESHAPE;
-  if (L->act_bits != 0 && L->act_bits != 4) return MOE_ESHAPE;
+  if (L->act_bits != 0 && L->act_bits != 4 && L->act_bits != 8) return MOE_ESHAPE;
   return MOE_OK;
 }
+
+// A8 (the W4A8 variant): one code byte per element instead of two per byte
+inline bool act8(const moe_layer* L) { return L->act_bits == 8; }
 
 // the shared expert's gate is applied only when the layer has a shared expert
 inline const float* shared_gate(const moe_layer* L) { return L->has_shared ? L->shared_gate_w : nullptr; }
@@ -94,7 +97,7 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   const int64_t R = T * L->k + (L->has_shared ? T : 0);
   size_t o = 0;
   w.xq = o;
-  o = align_up(o + (size_t)T * (L->H / 2));
+  o = align_up(o + (size_t)T * (act8(L) ? L->H : L->H / 2));
   w.xs = o;
   o = align_up(o + (size_t)T * (L->H / 16));
   w.xh = o;
@@ -102,7 +105,7 @@ FfnWs ffn_ws(const moe_layer* L, int64_t T) {
   w.hh = o;
   o = align_up(o + (size_t)R * L->I * sizeof(half_t));
   w.hq = o;
-  o = align_up(o + (size_t)R * (L->I / 2));
+  o = align_up(o + (size_t)R * (act8(L) ? L->I : L->I / 2));
   w.hs = o;
   o = align_up(o + (size_t)R * (L->I / 16));
   w.tiles = o;
@@ -230,13 +233,14 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
     if ((rc = launch_rc(launch_quant_act(x, MOE_DTYPE_BF16, T, L->H, L->a_gscale_in, xq, xs,
                                          self_encoding || decode_path ? nullptr : xh, stream,
                                          ev ? ev[0] : nullptr,
-                                         ev ? ev[1] : nullptr))))
+                                         ev ? ev[1] : nullptr, act8(L) ? 8 : 4))))
       return rc;
   } else if (ev && record_idle(stream, ev[0], ev[1]) != hipSuccess) {
     return MOE_ELAUNCH;
   }
   if (dbg && dbg->xq)
-    if (hipMemcpyAsync(dbg->xq, xq, (size_t)T * (L->H / 2), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    if (hipMemcpyAsync(dbg->xq, xq, (size_t)T * (act8(L) ? L->H : L->H / 2), hipMemcpyDeviceToDevice, stream) !=
+        hipSuccess)
       return MOE_ELAUNCH;
   if (dbg && dbg->xs)
     if (hipMemcpyAsync(dbg->xs, xs, (size_t)T * (L->H / 16), hipMemcpyDeviceToDevice, stream) != hipSuccess)
@@ -274,6 +278,7 @@ static int expert_ffn(const moe_layer* L, const uint16_t* x, int64_t T, const in
   p.y_shared = L->has_shared ? y_shared : nullptr;
   p.kc0 = 16 * kb0;
   p.kc1 = 16 * kb1;
+  p.act8 = act8(L) ? 1 : 0;
   if (shared_gate(L)) {  // the shared expert's per-token gate, read by the down kernels
     float* gate = reinterpret_cast<float*>(base + lay.gate);
     if ((rc = launch_rc(launch_shared_gate(x, L->shared_gate_w, T, L->H, gate, stream)))) return rc;
@@ -349,7 +354,8 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
   if (!debug_ok(dbg)) return MOE_EINVAL;
   const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
-  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT) {
+  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT ||
+      act8(L)) {
     if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_permute(L, topk_idx, T, expert_off, row2pair, pair2row, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_expert_ffn(L, x, T, expert_off, row2pair, y_rows, y_shared, dbg, ws, ws_bytes, stream))) return rc;
@@ -450,6 +456,17 @@ int moe_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int32_t n_exp, 
   if (!ptr_ok(codes) || !ptr_ok(codes_out) || !scales || !scales_out) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(scales_out) % 4) return MOE_EINVAL;
   return launch_rc(launch_pack_kmajor(codes, scales, n_exp, N, K, codes_out, scales_out, stream));
+}
+
+int moe_quantize_act8(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, int8_t* codes,
+                      uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 16) return MOE_ESHAPE;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_EINVAL;
+  if (!pow2_scale(gscale)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!ptr_ok(x) || !ptr_ok(codes) || !ptr_ok(scales)) return MOE_EINVAL;
+  return launch_rc(launch_quant_act(x, dtype, rows, cols, gscale, reinterpret_cast<uint8_t*>(codes), scales, nullptr,
+                                    stream, nullptr, nullptr, 8));
 }
 
 int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, uint8_t* codes,

@@ -123,16 +123,18 @@ __global__ __launch_bounds__(256) void k_ffn_gateup(FfnParams p) {
       float amax = fabsf(h);
 #pragma unroll
       for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
-      const uint32_t sc = scale_code(amax, 6.0f * p.g_mid);
+      const uint32_t sc = scale_code(amax, (p.act8 ? 127.0f : 6.0f) * p.g_mid);
       const float sv = ue4m3_value(sc);
-      const uint32_t c = elem_code(h, sv * p.g_mid);
+      const uint32_t c = p.act8 ? (uint32_t)int8_code(h, sc ? sv * p.g_mid : __builtin_inff())
+                                : elem_code(h, sv * p.g_mid);
       const uint32_t c_hi = __shfl_down(c, 1, 16);
       if (rr < nr) {
         const int64_t orow = out_row(p, si, r0 + rr);
         const int64_t col = (int64_t)hb * 16 + i;
-        p.hh[orow * I + col] = (half_t)(e2m1_value(c) * sv);
+        p.hh[orow * I + col] = p.act8 ? (half_t)((float)(int)c * sv) : (half_t)(e2m1_value(c) * sv);
         if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-        if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
+        if (p.hq_dbg && p.act8) p.hq_dbg[orow * I + col] = (uint8_t)(c & 0xFFu);
+        if (p.hq_dbg && !p.act8 && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
         if (p.hs_dbg && i == 0) p.hs_dbg[orow * (I / 16) + hb] = (uint8_t)sc;
       }
     }

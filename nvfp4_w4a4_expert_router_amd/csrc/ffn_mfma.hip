@@ -298,9 +298,11 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   const __amdgpu_buffer_rsrc_t hh_r = buffer_rsrc(p.hh + orow0 * I, (uint32_t)nrows * I * 2u);
   const int hi = lane >> 5;
   const float c_exp = -G * 1.4426950408889634f, inv_g2 = 1.0f / (G * G);
-  // (the debug dumps take a separate copy of the epilogue)
-  auto epilogue = [&](auto dumps_c) {
+  // (the debug dumps and the A8 encoding of the W4A8 variant take separate
+  // copies of the epilogue)
+  auto epilogue = [&](auto dumps_c, auto a8_c) {
     constexpr bool kDumps = decltype(dumps_c)::value != 0;
+    constexpr bool kA8 = decltype(a8_c)::value != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 32 * i + (lane & 31);  // tile row
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
         lane_pair(p0, &x0, &y0);
         lane_pair(p1, &x1, &y1);
         const float amax = __uint_as_float(hi ? max(x1, y1) : max(x0, y0));
-        const uint32_t mine = scale_code(amax, g6) | ((uint32_t)hi << 8);
+        const uint32_t mine = scale_code(amax, kA8 ? 127.0f * p.g_mid : g6) | ((uint32_t)hi << 8);
         uint32_t ca, cb;
         lane_pair(mine, &ca, &cb);
         const uint32_t sc0 = ((ca >> 8) == 0u ? ca : cb) & 0xFFu, sc1 = ((ca >> 8) == 0u ? cb : ca) & 0xFFu;
@@ -329,6 +331,32 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
         const half_t uh0 = (half_t)u0, uh1 = (half_t)u1;  // exact: UE4M3 values
         if (kDumps && p.hs_dbg && m < nrows)
           p.hs_dbg[(orow0 + m) * (I / 16) + (nt * 128 + wn) / 16 + hi] = (uint8_t)(hi ? sc1 : sc0);
+        if (kA8) {  // INT8 codes; FP16 values q * scale (exact)
+          const float s0 = sc0 ? u0 * p.g_mid : __builtin_inff(), s1 = sc1 ? u1 * p.g_mid : __builtin_inff();
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float sg = g < 2 ? s0 : s1, ug = g < 2 ? u0 : u1;
+            int qv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qv[e] = int8_code(hv[4 * g + e], sg);
+            const half2_t h01 = half2_t{(half_t)((float)qv[0] * ug), (half_t)((float)qv[1] * ug)};
+            const half2_t h23 = half2_t{(half_t)((float)qv[2] * ug), (half_t)((float)qv[3] * ug)};
+            const uint32_t voff = (uint32_t)(m * I + col0 + 8 * g) * 2u;
+            buffer_store8(u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)}, hh_r, voff);
+            if (kDumps && m < nrows) {
+              const int64_t orow = orow0 + m;
+              const int c = col0 + 8 * g;
+              if (p.hq_dbg)
+                *reinterpret_cast<uint32_t*>(p.hq_dbg + orow * I + c) =
+                    (uint32_t)(qv[0] & 0xFF) | (uint32_t)(qv[1] & 0xFF) << 8 | (uint32_t)(qv[2] & 0xFF) << 16 |
+                    (uint32_t)(qv[3] & 0xFF) << 24;
+              if (p.h_dbg)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p.h_dbg[orow * I + c + e] = hv[4 * g + e];
+            }
+          }
+          continue;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {  // columns col0 + 8 g .. + 3: entries 4 g .. 4 g + 3
           const E2M1Thresholds& Tg = g < 2 ? T0 : T1;
@@ -356,10 +384,17 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
       }
     }
   };
-  if (p.h_dbg || p.hq_dbg || p.hs_dbg)
-    epilogue(IntC<1>{});
-  else
-    epilogue(IntC<0>{});
+  const bool dumps = p.h_dbg || p.hq_dbg || p.hs_dbg;
+  if (p.act8) {
+    if (dumps)
+      epilogue(IntC<1>{}, IntC<1>{});
+    else
+      epilogue(IntC<0>{}, IntC<1>{});
+  } else if (dumps) {
+    epilogue(IntC<1>{}, IntC<0>{});
+  } else {
+    epilogue(IntC<0>{}, IntC<0>{});
+  }
 }
 
 // ---------------------------------------------------------------- G2

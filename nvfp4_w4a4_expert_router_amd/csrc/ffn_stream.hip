@@ -164,14 +164,25 @@ __global__ __launch_bounds__(256) void k_gateup_stream(FfnParams p) {
         v[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
         amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
       }
-      const uint32_t scode = scale_code(amax, g6);
-      const float sv = ue4m3_value(scode);
-      const float s = sv * p.g_in;
       half8_t h0, h1;
+      if (p.act8) {  // A8: INT8 codes on a scale from amax / 127
+        const uint32_t scode = scale_code(amax, 127.0f * p.g_in);
+        const float sv = ue4m3_value(scode);
+        const float s = scode ? sv * p.g_in : __builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        h0[i] = (half_t)(e2m1_value(elem_code(v[i], s)) * sv);
-        h1[i] = (half_t)(e2m1_value(elem_code(v[8 + i], s)) * sv);
+        for (int i = 0; i < 8; ++i) {
+          h0[i] = (half_t)((float)int8_code(v[i], s) * sv);
+          h1[i] = (half_t)((float)int8_code(v[8 + i], s) * sv);
+        }
+      } else {
+        const uint32_t scode = scale_code(amax, g6);
+        const float sv = ue4m3_value(scode);
+        const float s = sv * p.g_in;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          h0[i] = (half_t)(e2m1_value(elem_code(v[i], s)) * sv);
+          h1[i] = (half_t)(e2m1_value(elem_code(v[8 + i], s)) * sv);
+        }
       }
       half8_t* dst = reinterpret_cast<half8_t*>(xs + (size_t)rr * H + b * 16);
       dst[0] = h0;
@@ -225,16 +236,18 @@ __global__ __launch_bounds__(256) void k_gateup_stream(FfnParams p) {
       float amax = fabsf(h);
 #pragma unroll
       for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
-      const uint32_t scode = scale_code(amax, 6.0f * p.g_mid);
+      const uint32_t scode = scale_code(amax, (p.act8 ? 127.0f : 6.0f) * p.g_mid);
       const float sv = ue4m3_value(scode);
-      const uint32_t c = elem_code(h, sv * p.g_mid);
+      const uint32_t c = p.act8 ? (uint32_t)int8_code(h, scode ? sv * p.g_mid : __builtin_inff())
+                                : elem_code(h, sv * p.g_mid);
       const uint32_t c_hi = __shfl_down(c, 1, 16);
       if (rr < nr) {
         const int64_t orow = si.shared ? (int64_t)p.T * p.k + r0 + rr : (int64_t)si.row0 + r0 + rr;
         const int64_t col = (int64_t)hb * 16 + i;
-        p.hh[orow * I + col] = (half_t)(e2m1_value(c) * sv);
+        p.hh[orow * I + col] = p.act8 ? (half_t)((float)(int)c * sv) : (half_t)(e2m1_value(c) * sv);
         if (p.h_dbg) p.h_dbg[orow * I + col] = h;
-        if (p.hq_dbg && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
+        if (p.hq_dbg && p.act8) p.hq_dbg[orow * I + col] = (uint8_t)(c & 0xFFu);
+        if (p.hq_dbg && !p.act8 && (i & 1) == 0) p.hq_dbg[orow * (I / 2) + col / 2] = (uint8_t)(c | (c_hi << 4));
         if (p.hs_dbg && i == 0) p.hs_dbg[orow * (I / 16) + hb] = (uint8_t)scode;
       }
     }

@@ -206,6 +206,47 @@ def check_h_codes(h_o, hq_o, hs_o, hq_g, hs_g, g_mid, rep: Report, prefix="h"):
     return hq_ad, hs_ad
 
 
+def check_h_codes8(h_o, hq_o, hs_o, hq_g, hs_g, g_mid, rep: Report, prefix="h"):
+    """check_h_codes for the A8 encoding of the W4A8 variant (INT8 codes, scale from
+    amax / 127): a block scale may be the neighbouring code, and an element code the
+    neighbouring integer, only where the oracle's h lies within the FP32 rounding
+    band of that decision's threshold.  Returns the oracle's codes with every
+    accepted decision taken on the other side."""
+    n, I = h_o.shape
+    h = h_o.astype(np.float64)
+    amax = np.abs(h.reshape(n, I // 16, 16)).max(-1)
+    flips = 0
+    sd = np.argwhere(hs_o != hs_g)
+    for r, b in sd:
+        a, c = int(hs_o[r, b]), int(hs_g[r, b])
+        assert abs(a - c) == 1, "row %d block %d: scale codes %d vs %d" % (r, b, a, c)
+        lo = min(a, c)
+        thr = 127.0 * g_mid * 0.5 * (oracle.ue4m3(lo) + oracle.ue4m3(lo + 1))
+        assert abs(amax[r, b] - thr) <= BAND_REL * thr, "row %d block %d: scale flip outside band" % (r, b)
+        flips += 1
+    qo, qg = np.asarray(hq_o, np.int64), np.asarray(hq_g, np.int8).astype(np.int64)
+    q_ad = qo.copy()
+    hs_ad = np.array(hs_o, copy=True)
+    for r, b in sd:  # the block re-encoded under the GPU's scale
+        hs_ad[r, b] = hs_g[r, b]
+        s = oracle.ue4m3(int(hs_g[r, b])) * g_mid
+        for i in range(16):
+            q_ad[r, b * 16 + i] = oracle.int8_code(float(h[r, b * 16 + i]), s)
+    for r, i in np.argwhere(q_ad != qg):
+        co, cg = int(q_ad[r, i]), int(qg[r, i])
+        assert abs(co - cg) == 1 and (co * cg >= 0), "row %d col %d: codes %d vs %d" % (r, i, co, cg)
+        s = oracle.ue4m3(int(hs_g[r, i // 16])) * g_mid
+        thr = (min(abs(co), abs(cg)) + 0.5) * s
+        assert abs(abs(h[r, i]) - thr) <= BAND_REL * thr, "row %d col %d: code flip outside band (%.9g vs %.9g)" % (
+            r, i, abs(h[r, i]), thr)
+        q_ad[r, i] = cg
+        flips += 1
+    rep[prefix + "_flips"] = flips
+    assert flips <= max(1, 1e-4 * n * I), "%d A8(h) flips exceed 1e-4 of %d elements" % (flips, n * I)
+    assert np.array_equal(q_ad, qg) and np.array_equal(hs_ad, hs_g)
+    return q_ad.astype(np.int8), hs_ad
+
+
 # ---------------------------------------------------------------- output
 def f32_to_bf16_rne_bits(v32):
     """FP32 values -> BF16 bit patterns, round to nearest even (finite inputs)."""

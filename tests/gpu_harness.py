@@ -39,7 +39,7 @@ def device_layer(L, router_w=None, kmajor=True) -> moe.MoELayer:
     wg = getattr(L, "shared_gate_w", None)
     DL = moe.MoELayer(sh.H, sh.I, sh.E, sh.k, to_dev(rw), bank_to_dev(L.w13), bank_to_dev(L.w2),
                       bank_to_dev(L.sh13), bank_to_dev(L.sh2), L.a_gscale_in, L.a_gscale_mid,
-                      shared_gate_w=None if wg is None else to_dev(wg))
+                      shared_gate_w=None if wg is None else to_dev(wg), act_bits=getattr(L, "act_bits", 4))
     if kmajor and sh.H % 64 == 0 and sh.I % 64 == 0:
         DL.pack_kmajor()
     return DL
@@ -50,17 +50,18 @@ def run_layer(DL: moe.MoELayer, x: np.ndarray, residual=None, dump=("xq", "xs", 
     T = x.shape[0]
     H, I, k = DL.H, DL.I, DL.k
     R = T * k + (T if DL.has_shared else 0)
+    a8 = DL.act_bits == 8  # one code byte per element
     xd = to_dev(x.view(np.int16))
     buf = moe.Buffers(DL, T, DEV)
     dbg = {}
     if "xq" in dump:
-        dbg["xq"] = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+        dbg["xq"] = torch.empty((T, H if a8 else H // 2), dtype=torch.uint8, device=DEV)
     if "xs" in dump:
         dbg["xs"] = torch.empty((T, H // 16), dtype=torch.uint8, device=DEV)
     if "h" in dump:
         dbg["h"] = torch.empty((R, I), dtype=torch.float32, device=DEV)
     if "hq" in dump:
-        dbg["hq"] = torch.empty((R, I // 2), dtype=torch.uint8, device=DEV)
+        dbg["hq"] = torch.empty((R, I if a8 else I // 2), dtype=torch.uint8, device=DEV)
     if "hs" in dump:
         dbg["hs"] = torch.empty((R, I // 16), dtype=torch.uint8, device=DEV)
     res = None if residual is None else to_dev(residual.view(np.int16))
@@ -81,6 +82,8 @@ def run_layer(DL: moe.MoELayer, x: np.ndarray, residual=None, dump=("xq", "xs", 
         out["y_shared"] = buf.y_shared.cpu().numpy()
     for key, t in dbg.items():
         out[key] = t.cpu().numpy()
+        if a8 and key in ("xq", "hq"):
+            out[key] = out[key].view(np.int8)
     return out
 
 
@@ -94,25 +97,27 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
         logits64 = oracle.router_logits(x, L.router_w)
     idx_ad, w_ad = checker.check_topk(g["idx"], g["w"], logits64, sh.k, rep)
     checker.check_permutation(idx_ad, sh.E, g["off"], g["r2p"], g["p2r"])
-    xq_o, xs_o = oracle.quantize(oracle.bf16_to_f64(x), L.a_gscale_in)
-    assert np.array_equal(g["xq"], xq_o), "A4(x) codes differ"
-    assert np.array_equal(g["xs"], xs_o), "A4(x) scales differ"
+    bits = getattr(L, "act_bits", 4)
+    xq_o, xs_o = oracle.encode(oracle.bf16_to_f64(x), L.a_gscale_in, bits)
+    assert np.array_equal(g["xq"], xq_o), "A%d(x) codes differ" % bits
+    assert np.array_equal(g["xs"], xs_o), "A%d(x) scales differ" % bits
+    hcheck = checker.check_h_codes8 if bits == 8 else checker.check_h_codes
     tok = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, dtype=np.int32)
     n = tok.shape[0]
     a_row = np.repeat(tok, sh.k).astype(np.int32)
     a_exp = idx_ad[tok].reshape(-1).astype(np.int32)
     rows = g["p2r"][(tok[:, None] * sh.k + np.arange(sh.k)[None, :]).reshape(-1)]
     srows = T * sh.k + tok
-    r_o = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid)
+    r_o = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid,
+                             act_bits=bits)
     shared = L.sh13 is not None
     if shared:
         s_o = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
-                                 L.a_gscale_mid)
-    hq_r, hs_r = checker.check_h_codes(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid,
-                                       rep, "h")
+                                 L.a_gscale_mid, act_bits=bits)
+    hq_r, hs_r = hcheck(r_o["h"], r_o["hq"], r_o["hs"], g["hq"][rows], g["hs"][rows], L.a_gscale_mid, rep, "h")
     if shared:
-        hq_s, hs_s = checker.check_h_codes(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows],
-                                           L.a_gscale_mid, rep, "hsh")
+        hq_s, hs_s = hcheck(s_o["h"], s_o["hq"], s_o["hs"], g["hq"][srows], g["hs"][srows], L.a_gscale_mid, rep,
+                            "hsh")
     if "h" in g:
         hr = g["h"][rows].astype(np.float64)
         d = np.abs(hr - r_o["h"]) / (np.abs(r_o["h"]).max() + 1e-30)
@@ -120,11 +125,11 @@ def check_layer(L, x, g, tokens=None, residual=None, logits64=None, rep=None):
     # down projection on the oracle's own h codes, accepted band decisions taken on
     # their other side (identical to the oracle's codes when nothing flipped)
     r_t = oracle.expert_rows(a_row, a_exp, xq_o, xs_o, L.w13, L.w2, sh.H, sh.I, L.a_gscale_in, L.a_gscale_mid,
-                             hq_in=hq_r, hs_in=hs_r)
+                             hq_in=hq_r, hs_in=hs_r, act_bits=bits)
     y_sh = None
     if shared:
         s_t = oracle.expert_rows(tok, np.zeros(n, np.int32), xq_o, xs_o, L.sh13, L.sh2, sh.H, sh.I, L.a_gscale_in,
-                                 L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s)
+                                 L.a_gscale_mid, hq_in=hq_s, hs_in=hs_s, act_bits=bits)
         y_sh = s_t["y"]
         wg = getattr(L, "shared_gate_w", None)
         if wg is not None:  # the shared expert's rows times the token's gate

@@ -125,6 +125,18 @@ def test_router_mode_gate_and_act_bits_validated():
     assert moe.lib.moe_pack_router(FAKE, 512, 2048, None, None) == moe.MOE_EINVAL
 
 
+def test_w4a8_validation_and_workspace():
+    """act_bits 8 (the W4A8 variant) is accepted; its code buffers take one byte per
+    element, so its workspace is larger; moe_quantize_act8 validates like its A4 twin."""
+    a4 = moe.lib.moe_workspace_bytes(ctypes.byref(layer()), 300)
+    a8 = moe.lib.moe_workspace_bytes(ctypes.byref(layer(act_bits=8)), 300)
+    assert a8 > a4
+    assert moe.lib.moe_quantize_act8(FAKE, 0, 4, 20, 1.0, FAKE, FAKE, None) == moe.MOE_ESHAPE
+    assert moe.lib.moe_quantize_act8(FAKE, 2, 4, 32, 1.0, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_quantize_act8(FAKE, 0, 4, 32, 0.3, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_quantize_act8(None, 0, 0, 32, 1.0, None, None, None) == moe.MOE_OK
+
+
 def test_token_bound():
     """T * H * 2 and T * (k + 1) must stay below 2^31 (32-bit row offsets of the
     router's and the matrix-core kernels' buffer resources, int32 pair ids): the
