@@ -245,10 +245,11 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
  * (topk_idx, topk_w [T][k]; expert_off [E+1]; row2pair, pair2row [T*k];
  * y_rows [T*k][H]; y_shared [T][H] (nullable iff !has_shared); out [T][H];
  * residual nullable).  For decode batches (T <= 4, H <= 2048, E <= 512, no
- * dumps requested; events allowed) it runs fused in five kernels: router
- * (FP64 logits and the A4 codes of x), routing (one workgroup: top k, softmax
- * weights, permutation and a table of the experts to run; events 0/1 of
- * moe_debug span these two), gate/up (events 2/3), down projection (events
+ * dumps requested, the exact router, A4 activations; events allowed) it runs
+ * fused in four kernels: router (FP64 logits and the A4 codes of x; events 0/1
+ * of moe_debug), gate/up (events 2/3; each workgroup selects the top k of the
+ * batch, the softmax weights, the permutation and its expert from the FP64
+ * logits, and one extra workgroup writes them out), down projection (events
  * 4/5), combine.  Otherwise it runs the four calls in order.  Results are
  * identical either way.  ws must hold moe_workspace_bytes(L, T_max) bytes with
  * T <= T_max.
@@ -309,16 +310,6 @@ int moe_quantize_act(const void* x, int dtype, int64_t rows, int32_t cols, float
 int moe_pack_router(const float* router_w, int32_t E, int32_t H, uint16_t* pieces_out, hipStream_t stream);
 
 /* A8 encoding (the W4A8 variant's, see moe_layer.act_bits) of a row-major
- * [rows][cols] matrix (cols % 16 == 0): codes [rows][cols] INT8 out, scales
- * [rows][cols/16] out.  Per 16-element block: scale = RNE(amax/(127*gscale))
- * on the UE4M3 grid, saturating at 448; codes = RNE(x/(scale*gscale)) on the
- * integers, saturating at +-127.  Exact (decided by comparisons with exact
- * thresholds).  Errors and dtype as moe_quantize_act.
- * Pages: capy-flash README v0.5.4, "Serve" (the older W4A8 host path).      */
-int moe_quantize_act8(const void* x, int dtype, int64_t rows, int32_t cols, float gscale, int8_t* codes,
-                      uint8_t* scales, hipStream_t stream);
-
-/* K-step-major copy of one NVFP4 bank/* A8 encoding (the W4A8 variant's, see moe_layer.act_bits) of a row-major
  * [rows][cols] matrix (cols % 16 == 0): codes [rows][cols] INT8 out, scales
  * [rows][cols/16] out.  Per 16-element block: scale = RNE(amax/(127*gscale))
  * on the UE4M3 grid, saturating at 448; codes = RNE(x/(scale*gscale)) on the

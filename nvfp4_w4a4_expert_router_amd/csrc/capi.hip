@@ -367,7 +367,8 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   char* base = static_cast<char*>(ws);
   char* fbase = base + lg_bytes;
   hipEvent_t* ev = dbg ? dbg->events : nullptr;
-  // kernel 1: FP64 logits + A4(x), then one workgroup: the routing and slot table
+  // kernel 1: FP64 logits + A4(x); the routing itself is selected inside the
+  // gate/up kernel (kernel 2), whose last workgroup writes it out
   RouteDecodeParams q = {};
   q.x = x;
   q.W = L->router_w;
@@ -394,7 +395,8 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
     q.gate = gate;
   }
   if ((rc = launch_rc(launch_route_decode(q, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)))) return rc;
-  // kernels 2, 3: gate/up and down over the slot table; kernel 4: combine
+  // kernels 2, 3: gate/up (with the routing) and down over the slot table;
+  // kernel 4: combine
   FfnParams p = {};
   p.H = L->H;
   p.I = L->I;
@@ -427,6 +429,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.kc0 = 0;
   p.kc1 = L->I;
   p.sh_gate = gate;
+  p.rq = q;  // the gate/up workgroups select the routing from q.logits
   // the down kernel also writes the routed rows in token-major order, so the
   // combine reads them without the dependent pair2row load (same values)
   p.y_tok = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +

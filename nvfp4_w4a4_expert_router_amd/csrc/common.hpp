@@ -538,6 +538,27 @@ __device__ __forceinline__ int find_active_expert(const int32_t* __restrict__ of
 }
 
 // ---------------------------------------------------------------- launch parameter blocks
+// Fused decode routing (moe_layer_forward, T <= 4): FP64 logits and A4(x)
+// from the router kernel; top k, softmax weights, permutation and slot table
+// formed in the gate/up kernel's workgroups from those logits.
+struct RouteDecodeParams {
+  const uint16_t* x;   // [T][H] BF16
+  const float* W;      // [E][H]
+  int T, H, E, k;
+  float g_in;
+  double* logits;      // [T][E]
+  uint8_t* xq;         // [T][H/2]
+  uint8_t* xs;         // [T][H/16]
+  int32_t* idx;
+  float* w;
+  int32_t* off;
+  int32_t* r2p;
+  int32_t* p2r;
+  int4* slot_tab;      // [T*k]
+  const float* wg;     // [H] shared-expert gate vector (null: no gate)
+  float* gate;         // [T] gate values out (when wg is set)
+};
+
 struct FfnParams {
   int H, I, E, k, T, has_shared;
   int n_routed_slots;  // grid slots for routed experts (min(E, T*k))
@@ -573,26 +594,10 @@ struct FfnParams {
   // activation encoding: 0 = A4 (E2M1 codes, two per byte), 1 = A8 (INT8 codes,
   // one per byte) for x codes, h codes and their dumps
   int act8;
-};
-
-// Fused decode routing (moe_layer_forward, T <= 4): FP64 logits and A4(x),
-// then in one workgroup top k, softmax weights, permutation and slot table.
-struct RouteDecodeParams {
-  const uint16_t* x;   // [T][H] BF16
-  const float* W;      // [E][H]
-  int T, H, E, k;
-  float g_in;
-  double* logits;      // [T][E]
-  uint8_t* xq;         // [T][H/2]
-  uint8_t* xs;         // [T][H/16]
-  int32_t* idx;
-  float* w;
-  int32_t* off;
-  int32_t* r2p;
-  int32_t* p2r;
-  int4* slot_tab;      // [T*k]
-  const float* wg;     // [H] shared-expert gate vector (null: no gate)
-  float* gate;         // [T] gate values out (when wg is set)
+  // fused decode path (slot_tab set): the routing inputs and outputs; the
+  // gate/up kernel's routed workgroups select from rq.logits and its last
+  // workgroup publishes the outputs
+  RouteDecodeParams rq;
 };
 
 // Launch with optional events that take the kernel's own start (e0) and end

@@ -18,6 +18,7 @@
 // shipped" and "Why it matters").  Dot products are finished by recursive
 // halving across lanes (fixed pairing: deterministic).
 #include "common.hpp"
+#include "routing.hpp"
 
 namespace moe {
 
@@ -158,22 +159,43 @@ constexpr int kDecMaxT = 4;  // the 4-token verify window; larger batches use th
 // burst is in flight.
 constexpr int kGuCols = 32;  // intermediate columns per workgroup (gate and up rows: 2 kGuCols)
 // kA8: the W4A8 variant (x and h encoded by A8: INT8 codes, one byte each).
+// kTable (the fused decode call): each routed workgroup selects the routing of
+// all T tokens from the FP64 logits in LDS (route_select) and takes its slot's
+// entry from it; the grid's last workgroup also publishes the routing outputs
+// (ids, weights, permutation, slot table, shared gate) for the later kernels.
+constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
+struct GateUpLds {
+  half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
+  uint8_t sct[4][kJ][128];     // each wave's rows' block scales (H/16 bytes)
+  float gu[kDecMaxT][2 * kGuCols];
+  int toks[kDecMaxT];
+};
+union DecodeLds {
+  RoutingLds route;  // before the weight burst
+  GateUpLds gu;      // from the weight burst on
+};
+
 template <bool kTable, bool kA8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
-  constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
-  __shared__ __align__(16) half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
-  __shared__ __align__(16) uint8_t sct[4][kJ][128];      // each wave's rows' block scales (H/16 bytes)
-  __shared__ float gu[kDecMaxT][2 * kGuCols];
-  __shared__ int toks[kDecMaxT];
+  __shared__ __align__(16) DecodeLds lds;
+  half_t* const xs = lds.gu.xs;
+  auto& sct = lds.gu.sct;
+  auto& gu = lds.gu.gu;
+  int* const toks = lds.gu.toks;
+  if (kTable && blockIdx.x == gridDim.x - 1) {  // the publishing workgroup
+    const RouteSel rs = route_select<true>(p.rq, lds.route);
+    route_publish(p.rq, lds.route, rs);
+    return;
+  }
   const int H = p.H, I = p.I, T = p.T;
   const int n_cg = I / kGuCols;
   const int cg = blockIdx.x % n_cg, slot = blockIdx.x / n_cg;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
   const int sh_slot = slot - p.n_routed_slots;
   const bool shared = p.has_shared && sh_slot >= 0;
-  // 1. the slot's table entry, then the A4(x) codes (32 elements per thread)
+  // 1. the A4(x) codes (32 elements per thread), then the routing of the
+  // batch (fused call, routed slot) from its FP64 logits
   int4 ent = make_int4(0, 0, 0, 0);
-  if (kTable && !shared) ent = p.slot_tab[slot];
   const int xchunks = H / 32;
   const int xt = tid / xchunks, xc = tid % xchunks;
   const bool xmine = xt < T;  // T * H / 32 <= 256
@@ -188,6 +210,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       xq4 = *reinterpret_cast<const uint4*>(p.xq + (size_t)xt * (H / 2) + xc * 16);
     }
     xs2 = *reinterpret_cast<const uint16_t*>(p.xs + (size_t)xt * (H / 16) + xc * 2);
+  }
+  if (kTable && !shared) {
+    const RouteSel rs = route_select<false>(p.rq, lds.route);
+    ent = slot < rs.n_slots ? lds.route.slot[slot] : make_int4(-1, 0, 0, 0);
+    __syncthreads();  // the routing's LDS is reused from here on
   }
   // 2. this slot's expert and activation rows
   int e, row0, nrows;
@@ -434,7 +461,8 @@ static int decode_slots(const FfnParams& p) {
 hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int slots = decode_slots(p);
   if (slots == 0) return record_idle(s, ev_before, ev_after);
-  const dim3 grid((unsigned)(slots * (p.I / kGuCols)));
+  // the fused call's grid has one more workgroup: it publishes the routing
+  const dim3 grid((unsigned)(slots * (p.I / kGuCols) + (p.slot_tab ? 1 : 0)));
   if (p.act8) {
     if (p.slot_tab) return launch_timed(k_gateup_decode<true, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
     return launch_timed(k_gateup_decode<false, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);

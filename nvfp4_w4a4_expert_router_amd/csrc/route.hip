@@ -21,6 +21,7 @@
 // Two experts whose router rows agree wherever x is nonzero get identical
 // logits in both passes, so the tie rule (lower id first) decides.
 #include "common.hpp"
+#include "routing.hpp"
 
 namespace moe {
 
@@ -270,131 +271,13 @@ __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ 
 // sum of the two waves' totals.
 //
 // Fused variant (moe_layer_forward at T <= 4): the workgroups also write the
-// A4 codes of x; then one workgroup (k_route_tokens) selects the top k of every
-// token, forms the softmax weights and the permutation, and writes the slot
-// table of the expert kernels: the routing is computed once per call, not once
-// per expert tile.  (A last-workgroup-done election inside the logits kernel
-// needs a device-scope release per workgroup, which measured slower than the
-// kernel boundary.)
+// A4 codes of x; the selection of the top k of every token, the softmax
+// weights, the permutation and the slot table are then formed inside the
+// gate/up kernel's workgroups (routing.hpp), each from the FP64 logits, so no
+// separate one-workgroup kernel sits on the chain.  (A last-workgroup-done
+// election inside the logits kernel needs a device-scope hand-off per
+// workgroup, which measured slower than the kernel boundary.)
 constexpr int kGemvMaxT = 8;
-constexpr int kRdMaxT = 4;  // fused variant: one wave per token in the last workgroup
-constexpr int kRdMaxE = 512;
-
-struct RoutingLds {
-  TopkScratch ts[kRdMaxT];  // top-k scratch, one per token wave
-  unsigned int tmask[kRdMaxE];  // tokens that chose expert e (bit t)
-  int off[kRdMaxE + 1];
-  int nzr[kRdMaxE];  // experts with pairs and a smaller id (slot of the expert)
-  int4 slot[kRdMaxT * 32];  // slot table, written out after the last barrier
-  int wsum[4], wnz[4];      // per-wave totals of the scan
-};
-
-// ---------------------------------------------------------------- shared-expert gate
-// z = sum_h x[t][h] * wg[h] over one wave (two elements per lane and step, FP64
-// sums of exact BF16 x FP32 products, a fixed reduction order), then
-// gate = fl32(1 / (1 + exp(-z))) in FP64.  An optional gate on the shared
-// expert is not on the pages (they list the shared expert as always on); this
-// is the plainest form such a gate takes.
-__device__ __forceinline__ float shared_gate_wave(const uint16_t* __restrict__ xr, const float* __restrict__ wg,
-                                                  int H) {
-  const int lane = lane_id();
-  double a = 0.0;
-  for (int h = 2 * lane; h < H; h += 2 * kWave) {
-    const uint32_t xv = *reinterpret_cast<const uint32_t*>(xr + h);
-    const float2 w = *reinterpret_cast<const float2*>(wg + h);
-    a = fma((double)__uint_as_float(xv << 16), (double)w.x, a);
-    a = fma((double)__uint_as_float(xv & 0xFFFF0000u), (double)w.y, a);
-  }
-  const double z = wave_sum_f64(a);
-  return (float)(1.0 / (1.0 + exp(-z)));
-}
-
-// The routing of all T tokens in one workgroup (wave t takes token t).  Rows
-// of an expert are in token order, so a pair's row is the expert's offset
-// plus the number of earlier tokens in the expert's token mask.
-__device__ __forceinline__ void route_tokens(const RouteDecodeParams& q, RoutingLds& R) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int T = q.T, E = q.E, k = q.k, P = T * k;
-  // the logits loads first; the token masks are cleared while they are in flight
-  double v[8];
-  int id[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = lane + kWave * j;
-    const bool ok = wave < T && e < E;
-    v[j] = ok ? q.logits[(int64_t)wave * E + e] : -INFINITY;
-    id[j] = ok ? e : 0x7FFFFFFF;
-  }
-  for (int e = tid; e < E; e += 256) R.tmask[e] = 0u;
-  __syncthreads();
-  // global outputs are written after the last barrier: a barrier here also
-  // waits for this wave's outstanding stores
-  int my_e = 0;
-  float my_w = 0.0f;
-  if (wave < T) {
-    double my_v = 0.0;
-    wave_topk512(v, id, k, R.ts[wave], &my_v, &my_e);
-    my_w = topk_softmax_weight(my_v, k);
-    if (lane < k) atomicOr(&R.tmask[my_e], 1u << wave);
-  }
-  __syncthreads();
-  // scan over the experts, thread tid owning experts 2 tid and 2 tid + 1 (E <=
-  // 512): pair counts and nonzero counts, wave scans, then the wave totals
-  unsigned int tm[2];
-  int c[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = 2 * tid + j;
-    tm[j] = e < E ? R.tmask[e] : 0u;
-    c[j] = __popc(tm[j]);
-  }
-  const int sc = c[0] + c[1], snz = (c[0] > 0) + (c[1] > 0);
-  const int ic = wave_incl_scan_i32(sc), inz = wave_incl_scan_i32(snz);
-  if (lane == kWave - 1) {
-    R.wsum[wave] = ic;
-    R.wnz[wave] = inz;
-  }
-  __syncthreads();
-  int rc = ic - sc, rnz = inz - snz;
-  for (int w = 0; w < wave; ++w) {
-    rc += R.wsum[w];
-    rnz += R.wnz[w];
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = 2 * tid + j;
-    if (e < E) {
-      R.off[e] = rc;
-      R.nzr[e] = rnz;
-    }
-    // slot entry: expert, first row, rows, tokens (one byte each, ascending);
-    // at most 4 tokens (bits of tm), peeled without a loop
-    const unsigned int t1 = tm[j] & (tm[j] - 1u), t2 = t1 & (t1 - 1u), t3 = t2 & (t2 - 1u);
-    auto low = [](unsigned int t) { return t ? (unsigned)(__ffs(t) - 1) : 0u; };  // bytes past the count: 0
-    const unsigned int toks = low(tm[j]) | low(t1) << 8 | low(t2) << 16 | low(t3) << 24;
-    if (c[j] > 0) R.slot[rnz] = make_int4(e, rc, c[j], (int)toks);
-    rc += c[j];
-    rnz += c[j] > 0;
-  }
-  if (tid == 255) R.off[E] = rc;  // the last thread's running count is the total
-  __syncthreads();
-  for (int e = tid; e <= E; e += 256) q.off[e] = R.off[e];
-  const int n_slots = R.wnz[0] + R.wnz[1] + R.wnz[2] + R.wnz[3];
-  for (int s = tid; s < P; s += 256) q.slot_tab[s] = s < n_slots ? R.slot[s] : make_int4(-1, 0, 0, 0);
-  if (wave < T && lane < k) {
-    const int pi = wave * k + lane;
-    const int row = R.off[my_e] + __popc(R.tmask[my_e] & ((1u << wave) - 1u));
-    q.idx[pi] = my_e;
-    q.w[pi] = my_w;
-    q.p2r[pi] = row;
-    q.r2p[row] = pi;
-  }
-  if (q.wg && wave < T) {  // the shared expert's gate of token `wave`
-    const float g = shared_gate_wave(q.x + (int64_t)wave * q.H, q.wg, q.H);
-    if (lane == 0) q.gate[wave] = g;
-  }
-}
-
 template <bool kFused>
 __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   __shared__ double part[2][kGemvMaxT][2];
@@ -484,11 +367,6 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   __syncthreads();
   if ((wave & 1) == 0 && lane < T && e < E)
     q.logits[(int64_t)lane * E + e] = part[wave >> 1][lane][0] + part[wave >> 1][lane][1];
-}
-
-__global__ __launch_bounds__(256) void k_route_tokens(RouteDecodeParams q) {
-  __shared__ RoutingLds R;
-  route_tokens(q, R);
 }
 
 // ---------------------------------------------------------------- pass B: selection
@@ -858,12 +736,10 @@ bool route_decode_supported(int H, int E, int k, int64_t T) {
   return T >= 1 && T <= kRdMaxT && E <= kRdMaxE && k <= 32 && H % 32 == 0;
 }
 
-// two kernels: the event pair spans the start of the first and the end of the second
+// the FP64 logits and the A4 codes of x; the selection runs in the gate/up
+// kernel's workgroups (routing.hpp)
 hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
-  const hipError_t e =
-      launch_timed(k_route_decode<true>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before, nullptr, q);
-  if (e != hipSuccess) return e;
-  return launch_timed(k_route_tokens, dim3(1), dim3(256), 0, s, nullptr, ev_after, q);
+  return launch_timed(k_route_decode<true>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before, ev_after, q);
 }
 
 static float gamma_for_depth(int d) {
