@@ -406,7 +406,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
 // against all of them with broadcast reads, 16 in flight (a single wave has no
 // other wave to hide latency behind).  S: this wave's LDS scratch.
 constexpr int kTopkScratch = 512 + 32;
-struct TopkScratch {
+struct __attribute__((aligned(16))) TopkScratch {
   uint64_t key[kTopkScratch];
   double val[kTopkScratch];
 };
@@ -446,8 +446,13 @@ __device__ __forceinline__ void wave_topk512(const double (&v)[8], const int (&i
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int hr = 0;
-#pragma unroll 16
-  for (int q = 0; q < 64; ++q) hr += S.key[q] > hk;
+  const uint4* kp = reinterpret_cast<const uint4*>(S.key);  // two keys per 16-byte read
+#pragma unroll 8
+  for (int q = 0; q < 32; ++q) {
+    const uint4 pk = kp[q];
+    hr += (((uint64_t)pk.y << 32) | pk.x) > hk;
+    hr += (((uint64_t)pk.w << 32) | pk.z) > hk;
+  }
   const uint64_t at = __ballot(hr == k - 1);
   const int L = __ffsll((long long)at) - 1;
   const uint64_t tau = readlane_u64(hk, L);
@@ -482,11 +487,14 @@ __device__ __forceinline__ void wave_topk512(const double (&v)[8], const int (&i
     const uint64_t ck = c < nc ? S.key[c] : 0ull;
     const double cv = c < nc ? S.val[c] : 0.0;
     int r = 0;
-    int q = 0;
-    for (; q + 16 <= nc; q += 16)
+    // 16 reads in flight per round; the last round's reads past nc stay inside
+    // the scratch (nc <= 512 < kTopkScratch - 15) and are masked
+    for (int q = 0; q < nc; q += 16)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) r += S.key[q + u] > ck;
-    for (; q < nc; ++q) r += S.key[q] > ck;
+      for (int u = 0; u < 16; ++u) {
+        const uint64_t kq = S.key[q + u];
+        r += (q + u < nc) & (kq > ck);
+      }
     if (c < nc && r < k) {  // results after the 512 candidate slots
       S.key[512 + r] = ck;
       S.val[512 + r] = cv;
