@@ -60,7 +60,7 @@ HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_decode.txt")
-DECODE_SOURCES = ("ffn_decode.hip", "common.hpp")
+DECODE_SOURCES = ("ffn_decode.hip", "common.hpp", "routing.hpp")
 
 
 def log(*a):
@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--stream-chunks", type=int, default=4)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode legs (profiling the prefill only)")
     ap.add_argument("--skip-t1", action="store_true", help="skip the 1-token decode leg")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not run amd-smi for the clock log (under a counter-collecting profiler)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, for counter calibration")
     return ap.parse_args()
@@ -224,7 +226,7 @@ def main():
                    "tokens_per_step": T, "layers_rotated": args.layers, "parallelism": "single GPU"},
         "roofline": None, "cpu_baseline": None, "detail": {},
     }
-    rec["detail"]["clocks_start"] = read_clocks()
+    rec["detail"]["clocks_start"] = None if args.no_clocks else read_clocks()
 
     # plain 1 GiB device copy: the practical HBM bandwidth of this machine
     a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -294,9 +296,10 @@ def main():
             rows = T * k + T
             act_in = T * (H // 2 + H // 16)
             h_out = rows * (I // 2 + I // 16)
+            logits = T * E * 8  # FP64 router logits, read by the routing selection inside gate/up
             out.update({
                 "n_distinct": float(n_distinct.mean()),
-                "gateup_bytes": float(np.mean((n_distinct + 1) * w13_bytes)) + act_in + h_out,
+                "gateup_bytes": float(np.mean((n_distinct + 1) * w13_bytes)) + act_in + h_out + logits,
                 "down_bytes": float(np.mean((n_distinct + 1) * w2_bytes)) + h_out + rows * H * 4,
                 "layer_bytes": 4 * E * H + float(np.mean((n_distinct + 1) * (w13_bytes + w2_bytes))) + T * H * 2 * 2,
             })
@@ -351,14 +354,14 @@ def main():
             rec["config"]["launch"] = "eager (one host launch per kernel)"
         rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                           "kernel": "k_gateup_decode<true>", "algorithmic_bytes_per_launch": round(d["gateup_bytes"]),
+                           "kernel": "k_gateup_decode<true, false>", "algorithmic_bytes_per_launch": round(d["gateup_bytes"]),
                            "avg_duration_us": round(d["t_gateup"] * 1e3, 3),
                            "frac_of_copy_bandwidth": round(achieved / copy_gbs, 4)}
 
         def summary(d):
             s = {
                 "eager_tok_s": round(d["eager_tok_s"], 1),
-                "kernel_avg_us": {"route_logits_and_select": round(d["t_first"] * 1e3, 3),
+                "kernel_avg_us": {"route_logits_and_act_quant": round(d["t_first"] * 1e3, 3),
                                   "gateup": round(d["t_gateup"] * 1e3, 3), "down": round(d["t_down"] * 1e3, 3)},
                 "gateup_achieved_GBs": round(d["gateup_bytes"] / (d["t_gateup"] * 1e-3) / 1e9, 1),
                 "down_achieved_GBs": round(d["down_bytes"] / (d["t_down"] * 1e-3) / 1e9, 1),
@@ -425,7 +428,9 @@ def main():
     def prefill_leg(cfg_p, Tp, n):
         t0 = time.time()
         Lp = gen.make_layer(cfg_p)
-        DLp = device_layer(Lp).pack_kmajor()  # K-step-major weight copies for the matrix-core kernels
+        # once per layer, outside any timed region: the K-step-major weight copies the
+        # matrix-core kernels read and the router's BF16 pieces
+        DLp = device_layer(Lp).pack_kmajor().pack_router()
         xp = up(gen.make_tokens(cfg_p, Tp).view(np.int16))
         log("prefill layer and %d tokens generated (%.1f s)" % (Tp, time.time() - t0))
         buf = moe.Buffers(DLp, Tp, dev)
@@ -473,6 +478,22 @@ def main():
                          "flop_per_chunk": fl_g1 + fl_g2, "avg_duration_us": round((t_g1 + t_g2) * 1e3, 2)},
         }
         log("prefill %d: %d chunks, median %.3f ms" % (Tp, n, pct(t_chunk, 50)))
+        if cfg_p == 3:
+            # the router alone in each precision mode (same chunk, same cached BF16 pieces)
+            modes = {}
+            for name, mode in (("exact", moe.MOE_ROUTER_EXACT), ("split3_f32", moe.MOE_ROUTER_SPLIT3_F32),
+                               ("bf16", moe.MOE_ROUTER_BF16)):
+                Lm = DLp.with_router_mode(mode)
+                moe.moe_route(Lm, xp, buf.topk_idx, buf.topk_w, buf.ws, T=Tp)
+                pairs = [(ev(), ev()) for _ in range(n)]
+                for a_, b_ in pairs:
+                    a_.record(stream)
+                    moe.moe_route(Lm, xp, buf.topk_idx, buf.topk_w, buf.ws, T=Tp)
+                    b_.record(stream)
+                torch.cuda.synchronize()
+                modes[name] = round(pct([a_.elapsed_time(b_) for a_, b_ in pairs], 50), 4)
+            out["route_ms_by_router_mode"] = modes
+            log("router modes (ms): %s" % modes)
         return out, DLp, buf
 
     if args.prefill_tokens > 0:
@@ -520,7 +541,7 @@ def main():
         rec["detail"]["prefill_4096" if args.c2_tokens == 4096 else "prefill_%d" % args.c2_tokens] = p2
         del DLp, buf
     torch.cuda.synchronize()
-    rec["detail"]["clocks_end"] = read_clocks()
+    rec["detail"]["clocks_end"] = None if args.no_clocks else read_clocks()
 
     # ---------------------------------------------------------------- oracle on the host
     if args.cpu_seconds > 0 and host_layer0 is not None:
