@@ -283,18 +283,15 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   __shared__ double part[2][kGemvMaxT][2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = q.T, H = q.H, E = q.E;
-  // 1. loads in dependency order: this thread's A4 block of x (fused: block
-  // tid * grid + workgroup, so every workgroup encodes a few), then the first
-  // router and x chunks; the encoding runs while the router rows are in flight
+  // 1. loads in dependency order: this lane's element of an A4 block of x
+  // (fused: 16 lanes per block, blocks workgroup + grid * (tid / 16) + ..., so
+  // every workgroup encodes a few), then the first router and x chunks; the
+  // encoding runs while the router rows are in flight
   const int64_t nb = kFused ? (int64_t)T * (H / 16) : 0;
-  const int64_t b = (int64_t)tid * gridDim.x + blockIdx.x;
+  const int64_t b = (int64_t)(tid >> 4) * gridDim.x + blockIdx.x;
   const bool enc = b < nb;
-  uint4 ab[2] = {};
-  if (enc) {
-    const uint4* src = reinterpret_cast<const uint4*>(q.x + b * 16);
-    ab[0] = src[0];
-    ab[1] = src[1];
-  }
+  uint32_t xe = 0u;
+  if (enc) xe = q.x[b * 16 + (tid & 15)];
   // logits of expert e: lane L of the expert's wave pair owns elements h0 .. h0 + 15
   const int e = 2 * blockIdx.x + (wave >> 1);
   const int L = kWave * (wave & 1) + lane;
@@ -328,25 +325,19 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   };
   const bool has = e < E && 16 * L < H;
   if (has) load(16 * L);
-  // 2. A4 codes of x (fused): blocks b, b + 256 * grid, ... (the first one loaded above)
-  if (kFused && enc) {
-    for (int64_t bb = b; bb < nb; bb += (int64_t)256 * gridDim.x) {
-      if (bb != b) {
-        const uint4* src = reinterpret_cast<const uint4*>(q.x + bb * 16);
-        ab[0] = src[0];
-        ab[1] = src[1];
-      }
-      const uint32_t wb[8] = {ab[0].x, ab[0].y, ab[0].z, ab[0].w, ab[1].x, ab[1].y, ab[1].z, ab[1].w};
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = __uint_as_float(wb[i] << 16);
-        v[2 * i + 1] = __uint_as_float(wb[i] & 0xFFFF0000u);
-      }
-      uint2 pk;
-      const uint32_t sc = encode_a4_block16(v, q.g_in, 6.0f * q.g_in, &pk);
-      reinterpret_cast<uint2*>(q.xq)[bb] = pk;
-      q.xs[bb] = (uint8_t)sc;
+  // 2. A4 codes of x (fused): each DPP row of 16 lanes encodes one block (block
+  // maximum and code pairs by DPP; the even lanes store one byte of two codes),
+  // blocks b, b + 16 * grid, ... (the first element loaded above).  A whole
+  // row takes the same branch, so the row operations see all 16 lanes.
+  if (kFused) {
+    for (int64_t bb = b; bb < nb; bb += (int64_t)16 * gridDim.x) {
+      if (bb != b) xe = q.x[bb * 16 + (tid & 15)];
+      const float v = __uint_as_float(xe << 16);
+      const uint32_t sc = scale_code(row16_absmax(v), 6.0f * q.g_in);
+      const uint32_t c = elem_code_s(v, sc ? ue4m3_value(sc) * q.g_in : __builtin_inff());
+      const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
+      if ((tid & 1) == 0) q.xq[bb * 8 + ((tid & 15) >> 1)] = (uint8_t)c2;
+      if ((tid & 15) == 0) q.xs[bb] = (uint8_t)sc;
     }
   }
   // 3. the FP64 sums
