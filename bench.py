@@ -300,7 +300,9 @@ def main():
             out.update({
                 "n_distinct": float(n_distinct.mean()),
                 "gateup_bytes": float(np.mean((n_distinct + 1) * w13_bytes)) + act_in + h_out + logits,
-                "down_bytes": float(np.mean((n_distinct + 1) * w2_bytes)) + h_out + rows * H * 4,
+                # down projection with the combine: W2 of the distinct experts, A4(h) read,
+                # the FP32 rows written, the BF16 output written
+                "down_bytes": float(np.mean((n_distinct + 1) * w2_bytes)) + h_out + rows * H * 4 + T * H * 2,
                 "layer_bytes": 4 * E * H + float(np.mean((n_distinct + 1) * (w13_bytes + w2_bytes))) + T * H * 2 * 2,
             })
             if args.graph_steps > 0:
@@ -362,9 +364,10 @@ def main():
             s = {
                 "eager_tok_s": round(d["eager_tok_s"], 1),
                 "kernel_avg_us": {"route_logits_and_act_quant": round(d["t_first"] * 1e3, 3),
-                                  "gateup": round(d["t_gateup"] * 1e3, 3), "down": round(d["t_down"] * 1e3, 3)},
+                                  "gateup": round(d["t_gateup"] * 1e3, 3),
+                                  "down_and_combine": round(d["t_down"] * 1e3, 3)},
                 "gateup_achieved_GBs": round(d["gateup_bytes"] / (d["t_gateup"] * 1e-3) / 1e9, 1),
-                "down_achieved_GBs": round(d["down_bytes"] / (d["t_down"] * 1e-3) / 1e9, 1),
+                "down_and_combine_achieved_GBs": round(d["down_bytes"] / (d["t_down"] * 1e-3) / 1e9, 1),
                 "distinct_experts_per_step": round(d["n_distinct"], 3),
                 "layer_algorithmic_bytes": round(d["layer_bytes"]),
             }

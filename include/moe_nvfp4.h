@@ -249,9 +249,11 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
  * fused in four kernels: router (FP64 logits and the A4 codes of x; events 0/1
  * of moe_debug), gate/up (events 2/3; each workgroup selects the top k of the
  * batch, the softmax weights, the permutation and its expert from the FP64
- * logits, and one extra workgroup writes them out), down projection (events
- * 4/5), combine.  Otherwise it runs the four calls in order.  Results are
- * identical either way.  ws must hold moe_workspace_bytes(L, T_max) bytes with
+ * logits, and one extra workgroup writes them out), down projection with the
+ * combine (events 4/5; one workgroup per token and 8 output columns, when
+ * (k + has_shared) * I / 32 <= 256, else a down kernel and the combine
+ * kernel).  Otherwise it runs the four calls in order.  Results are identical
+ * either way.  ws must hold moe_workspace_bytes(L, T_max) bytes with
  * T <= T_max.
  * Pages: capy-flash README v0.5.4, "What it does" (a routed layer computed
  * per expert id with the W4A4 quantization).                                */

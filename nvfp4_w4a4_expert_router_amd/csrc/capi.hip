@@ -435,6 +435,12 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.y_tok = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +
                                      align_up((size_t)T * L->k * sizeof(int4)));
   if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
+  if (down_combine_decode_supported(L->H, L->I, L->k, L->has_shared)) {
+    // kernel 3 also combines: one workgroup per (token, 8 output columns)
+    p.residual = residual;
+    p.out = out;
+    return launch_rc(launch_down_combine_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
+  }
   if ((rc = launch_rc(launch_down_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr)))) return rc;
   return launch_rc(launch_combine(T, L->H, L->k, p.y_tok, p.y_shared, nullptr, topk_w, residual, out, stream));
 }

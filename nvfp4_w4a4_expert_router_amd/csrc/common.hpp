@@ -606,6 +606,10 @@ struct FfnParams {
   // gate/up kernel's routed workgroups select from rq.logits and its last
   // workgroup publishes the outputs
   RouteDecodeParams rq;
+  // fused decode path, down projection with the combine: residual [T][H] BF16
+  // (nullable) and the layer output [T][H] BF16
+  const uint16_t* residual;
+  uint16_t* out;
 };
 
 // Launch with optional events that take the kernel's own start (e0) and end
@@ -653,6 +657,8 @@ bool fused_decode_supported(int H, int I, int E, int k, int64_t T);
 bool route_decode_supported(int H, int E, int k, int64_t T);
 hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_down_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+bool down_combine_decode_supported(int H, int I, int k, int has_shared);
+hipError_t launch_down_combine_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 // matrix-core grouped GEMM (prefill): H % 128 == 0, I % 64 == 0, E <= 1000
 bool ffn_mfma_supported(int H, int I, int E, int64_t T, int k);
 size_t ffn_mfma_ws_bytes(int E, int64_t T, int k, int has_shared);

@@ -41,7 +41,8 @@ __device__ __forceinline__ float chunk32(uint4 q, uint32_t sc2, const half8_t* a
   b0 = dot8(q.y, a[1], b0);
   float b1 = dot8(q.z, a[2], 0.0f);
   b1 = dot8(q.w, a[3], b1);
-  return b0 * ue4m3_value(sc2 & 0xFFu) + b1 * ue4m3_value((sc2 >> 8) & 0xFFu);
+  // one fixed contraction, so every kernel that uses it rounds alike
+  return __builtin_fmaf(b0, ue4m3_value(sc2 & 0xFFu), b1 * ue4m3_value((sc2 >> 8) & 0xFFu));
 }
 
 // Opaque copy: keeps the compiler from hoisting the FP4 decode of loop-
@@ -447,7 +448,139 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
+// ---------------------------------------------------------------- down + combine
+// Fused decode path: one workgroup per (token t, kDcCols output columns).
+// Lane group j (kLPR lanes, one per 32-element chunk of I) takes the j-th
+// expert of the token in rank order (j = k: the shared expert), loads that
+// expert's kDcCols W2 rows and the token's h row, and forms the rows' dot
+// products with the down kernel's per-lane chunks and lane reduction (the same
+// FP32 values).  The rows are written to y_rows / y_shared as the down kernel
+// writes them, and the workgroup then combines its columns in LDS in the
+// combine kernel's order (j ascending, FMA with the router weight, then the
+// shared row, then the residual, one BF16 rounding).  That takes the combine
+// kernel and one kernel boundary off the decode chain; the price is that an
+// expert chosen by several tokens is read once per token (from the caches
+// after the first).
+constexpr int kDcCols = 8;
+template <int kLPR>
+__global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
+  constexpr int kSrow = 2 * kLPR;  // scale bytes per W2 row (I / 16)
+  static_assert(kDcCols * kSrow == 16 * kLPR, "one 16-byte scale piece per lane");
+  const int H = p.H, I = p.I, T = p.T, k = p.k;
+  const int n_cb = H / kDcCols;
+  const int t = blockIdx.x / n_cb, n0 = (blockIdx.x % n_cb) * kDcCols;
+  const int tid = threadIdx.x, l = lane_id();
+  const int j = tid / kLPR, c = tid % kLPR;
+  const int n_e = k + (p.has_shared ? 1 : 0);
+  const bool live = j < n_e;
+  const bool shared = live && j == k;
+  __shared__ __align__(16) uint8_t sct[256 / kLPR][kDcCols * kSrow];
+  __shared__ float ycomb[256 / kLPR][kDcCols];
+  __shared__ float wsh[256 / kLPR];
+  // 1. the pair's routing (written by the routing's publishing workgroup)
+  int e = 0;
+  int64_t hrow = 0;
+  float wj = 0.0f, gate = 1.0f;
+  if (live) {
+    if (shared) {
+      hrow = (int64_t)T * k + t;
+      if (p.sh_gate) gate = p.sh_gate[t];
+    } else {
+      e = p.rq.idx[t * k + j];
+      hrow = p.rq.p2r[t * k + j];
+      wj = p.rq.w[t * k + j];
+    }
+  }
+  const uint8_t* bcodes = shared ? p.sh2.codes : p.w2.codes;
+  const uint8_t* bscales = shared ? p.sh2.scales : p.w2.scales;
+  const float* bg = shared ? p.sh2.gscale : p.w2.gscale;
+  const int64_t row0 = (int64_t)e * H + n0;
+  // 2. loads in the order they are consumed: the rows' block scales (one
+  // 16-byte piece per lane), the h chunk, the gscale, then the code burst
+  uint4 scv = make_uint4(0u, 0u, 0u, 0u);
+  half8_t a[4];
+  uint4 q[kDcCols];
+  float gsc = 0.0f;
+  if (live) {
+    scv = *reinterpret_cast<const uint4*>(bscales + row0 * kSrow + 16 * c);
+    const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + hrow * I + 32 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = src[i];
+    gsc = bg[e];
+#pragma unroll
+    for (int r = 0; r < kDcCols; ++r)
+      q[r] = *reinterpret_cast<const uint4*>(bcodes + (row0 + r) * (I / 2) + 16 * c);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = half8_t{};
+#pragma unroll
+    for (int r = 0; r < kDcCols; ++r) q[r] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (j < 256 / kLPR) {
+    *reinterpret_cast<uint4*>(&sct[j][16 * c]) = scv;
+    if (c == 0) wsh[j] = wj;
+  }
+  __syncthreads();
+  uint32_t sc[kDcCols];
+#pragma unroll
+  for (int r = 0; r < kDcCols; ++r) sc[r] = *reinterpret_cast<const uint16_t*>(&sct[j < 256 / kLPR ? j : 0][r * kSrow + 2 * c]);
+  // 3. the rows' dot products (the down kernel's chunks and reduction)
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < kDcCols; ++r) {
+    acc[r] = chunk32(q[r], sc[r], a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ReduceScatter<kLPR, kDcCols>::run(acc, l);
+  const float G = gsc * p.g_mid;
+  constexpr int kKeep = kDcCols / kLPR > 1 ? kDcCols / kLPR : 1;
+  const bool writer = live && (kLPR <= kDcCols || (l & (kLPR / kDcCols - 1)) == 0);
+  if (writer) {
+    const int jb = ReduceScatter<kLPR, kDcCols>::base(l);
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i) {
+      const int r = jb + i;
+      const float y = shared && p.sh_gate ? (G * acc[i]) * gate : G * acc[i];
+      if (shared)
+        p.y_shared[(int64_t)t * H + n0 + r] = y;
+      else
+        p.y_rows[hrow * H + n0 + r] = y;
+      ycomb[j][r] = y;
+    }
+  }
+  __syncthreads();
+  // 4. the combine of this workgroup's columns
+  if (tid < kDcCols) {
+    float o = 0.0f;
+    for (int jj = 0; jj < k; ++jj) o = fmaf(wsh[jj], ycomb[jj][tid], o);
+    if (p.has_shared) o += ycomb[k][tid];
+    if (p.residual) o += bf16_to_f32(p.residual[(int64_t)t * H + n0 + tid]);
+    p.out[(int64_t)t * H + n0 + tid] = f32_to_bf16_rne(o);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+bool down_combine_decode_supported(int H, int I, int k, int has_shared) {
+  const int lpr = I / 32;
+  return H % kDcCols == 0 && lpr >= 2 && lpr <= 64 && (lpr & (lpr - 1)) == 0 &&
+         (k + (has_shared ? 1 : 0)) * lpr <= 256;
+}
+
+hipError_t launch_down_combine_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev_before,
+                                      hipEvent_t ev_after) {
+  const int lpr = p.I / 32;
+  const int threads = ((p.k + (p.has_shared ? 1 : 0)) * lpr + kWave - 1) / kWave * kWave;
+  const dim3 grid((unsigned)(p.T * (p.H / kDcCols))), block((unsigned)threads);
+  switch (lpr) {
+    case 2: return launch_timed(k_down_combine_decode<2>, grid, block, 0, s, ev_before, ev_after, p);
+    case 4: return launch_timed(k_down_combine_decode<4>, grid, block, 0, s, ev_before, ev_after, p);
+    case 8: return launch_timed(k_down_combine_decode<8>, grid, block, 0, s, ev_before, ev_after, p);
+    case 16: return launch_timed(k_down_combine_decode<16>, grid, block, 0, s, ev_before, ev_after, p);
+    case 32: return launch_timed(k_down_combine_decode<32>, grid, block, 0, s, ev_before, ev_after, p);
+    default: return launch_timed(k_down_combine_decode<64>, grid, block, 0, s, ev_before, ev_after, p);
+  }
+}
+
 bool ffn_decode_supported(int H, int I, int64_t T) {
   const int lpr = I / 32;
   return T <= kDecMaxT && H <= 2048 && H % 32 == 0 && I % 32 == 0 && lpr >= 1 && lpr <= 64 &&
