@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const uint32_t vq = l < nch ? (uint32_t)(cg * kGuCols + w) * qrow + l * 16u : 0x80000000u;
   uint4 q[kJ];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) q[j] = buffer_load16(rq, vq, rowoff(j) * qrow);
+  for (int j = 0; j < kJ; ++j) q[j] = buffer_load16_nt(rq, vq, rowoff(j) * qrow);
   __builtin_amdgcn_sched_barrier(0);
   const float G = gsc * p.g_in;
   // 3. A4(x) to FP16 in LDS while the weights are in flight
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
     gsc = bg[e];
 #pragma unroll
     for (int r = 0; r < kDcCols; ++r)
-      q[r] = *reinterpret_cast<const uint4*>(bcodes + (row0 + r) * (I / 2) + 16 * c);
+      q[r] = load16_nt(bcodes + (row0 + r) * (I / 2) + 16 * c);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = half8_t{};
