@@ -250,7 +250,7 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
  * of moe_debug), gate/up (events 2/3; each workgroup selects the top k of the
  * batch, the softmax weights, the permutation and its expert from the FP64
  * logits, and one extra workgroup writes them out), down projection with the
- * combine (events 4/5; one workgroup per token and 8 output columns, when
+ * combine (events 4/5; one workgroup per token and 4 output columns, when
  * (k + has_shared) * I / 32 <= 256, else a down kernel and the combine
  * kernel).  Otherwise it runs the four calls in order.  Results are identical
  * either way.  ws must hold moe_workspace_bytes(L, T_max) bytes with

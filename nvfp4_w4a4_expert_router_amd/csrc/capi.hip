@@ -436,7 +436,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
                                      align_up((size_t)T * L->k * sizeof(int4)));
   if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
   if (down_combine_decode_supported(L->H, L->I, L->k, L->has_shared)) {
-    // kernel 3 also combines: one workgroup per (token, 8 output columns)
+    // kernel 3 also combines: one workgroup per (token, 4 output columns)
     p.residual = residual;
     p.out = out;
     return launch_rc(launch_down_combine_decode(p, stream, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr));
