@@ -11,7 +11,12 @@ reach (every kernel the library can launch is compared with the oracle somewhere
     experts, the decode kernels' slot search) and at 300 tokens (the matrix-core
     router with the general refinement kernel, the chunked permutation, the
     weight-streaming kernels), and 640 experts at 300 tokens (the grouped-GEMM
-    tile map over more than 512 segments).
+    tile map over more than 512 segments);
+  * the fused decode path (moe_layer_forward at 1 and 4 tokens) at intermediate
+    sizes 64, 256, 1,024 and 2,048 (2 to 64 lanes per W2 row in the down
+    projection with the combine) and at a shape whose (k + 1) * I / 32 exceeds
+    256 (the fused path's separate down and combine kernels): bit-exact against
+    the four separate calls and checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -23,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import gpu_harness as gh
+    import nvfp4_w4a4_expert_router_amd as moe
 
 ODD = gen.Shape(H=288, E=24, k=3, I=96)
 _layers = {}
@@ -70,4 +76,36 @@ def test_many_experts(E, T):
     g = gh.run_layer(DL, x, dump=("xq", "xs", "hq", "hs"))
     assert len(np.unique(g["idx"])) > (30 if T == 4 else 500)
     rep = gh.check_layer(L, x, g, tokens=None if T <= 8 else sample_tokens(T, 32, E))
+    gh.log("  ", rep.line())
+
+
+FUSED_SHAPES = {
+    "I64": gen.Shape(H=256, E=32, k=4, I=64),
+    "I256": gen.Shape(H=512, E=64, k=6, I=256),
+    "I1024": gen.Shape(H=256, E=32, k=3, I=1024),
+    "I2048": gen.Shape(H=128, E=16, k=3, I=2048),
+    "I1024k8": gen.Shape(H=256, E=64, k=8, I=1024),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_SHAPES))
+@pytest.mark.parametrize("T", [1, 4])
+def test_fused_decode_shapes(name, T):
+    sh = FUSED_SHAPES[name]
+    gh.log("case: fused decode H=%d E=%d k=%d I=%d T=%d" % (sh.H, sh.E, sh.k, sh.I, T))
+    L, DL = layer_for(name, sh, 1)
+    x = gen.make_tokens(1, T, step=41, H=sh.H)
+    res = gen.make_tokens(1, T, step=42, H=sh.H)
+    ref = gh.run_layer(DL, x, residual=res, dump=())
+    buf = moe.Buffers(DL, T, gh.DEV)
+    moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf, residual=gh.to_dev(res.view(np.int16)))
+    torch.cuda.synchronize()
+    got = {"idx": buf.topk_idx, "w": buf.topk_w, "off": buf.expert_off, "r2p": buf.row2pair, "p2r": buf.pair2row,
+           "y_rows": buf.y_rows, "y_shared": buf.y_shared, "out": buf.out}
+    for key, t in got.items():
+        a = t.cpu().numpy()
+        if key == "out":
+            a = a.view(np.uint16)
+        assert np.array_equal(a, ref[key]), key
+    rep = gh.check_layer(L, x, dict(ref, **gh.run_layer(DL, x, residual=res)), residual=res)
     gh.log("  ", rep.line())
