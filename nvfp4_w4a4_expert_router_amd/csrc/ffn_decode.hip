@@ -53,10 +53,47 @@ __device__ __forceinline__ uint4 opaque(uint4 v) {
   return v;
 }
 
+// The value of lane l ^ m (m <= 8) by DPP: quad permutations for 1 and 2, the
+// half-row mirror then a quad reversal for 4, a rotation by 8 within the row
+// for 8 (lane layouts checked on the device).
+template <int m>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int u = __float_as_int(v);
+  if constexpr (m == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0xB1, 0xF, 0xF, true));
+  if constexpr (m == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x4E, 0xF, 0xF, true));
+  if constexpr (m == 4) {
+    const int h = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, true));  // quad_perm [3,2,1,0]
+  }
+  if constexpr (m == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x128, 0xF, 0xF, true));  // row_ror:8
+  static_assert(m == 1 || m == 2 || m == 4 || m == 8, "DPP exchange within a row");
+  return v;
+}
+
+// keep + the partner's send for the pair (x kept by lanes without bit m, y by
+// lanes with it; the other value is sent): for m = 16 and 32 one
+// v_permlane16/32_swap of (x, y) leaves each lane's keep in one result and
+// its partner's send in the other.
+template <int m>
+__device__ __forceinline__ float pair_sum(float x, float y, bool upper) {
+  if constexpr (m == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(y), false, false);
+    return __int_as_float(p[0]) + __int_as_float(p[1]);
+  } else if constexpr (m == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(y), false, false);
+    return __int_as_float(p[0]) + __int_as_float(p[1]);
+  } else {
+    const float send = upper ? x : y;
+    const float keep = upper ? y : x;
+    return keep + xor_lane<m>(send);
+  }
+}
+
 // Sum v[0..15] over aligned groups of kG lanes by recursive halving (all steps
-// resolved at compile time).  Afterwards lane l holds the group total of
-// indices base + i for i < max(1, kN / kG), where base adds `half` for every
-// halving step whose mask bit the lane has.
+// resolved at compile time; each step adds a lane's kept value and its
+// partner's, so the sums do not depend on how the values move).  Afterwards
+// lane l holds the group total of indices base + i for i < max(1, kN / kG),
+// where base adds `half` for every halving step whose mask bit the lane has.
 template <int kG, int kN>
 struct ReduceScatter {
   __device__ __forceinline__ static void run(float (&v)[16], int lane) {
@@ -66,14 +103,10 @@ struct ReduceScatter {
       if constexpr (kN > 1) {
         constexpr int half = kN / 2;
 #pragma unroll
-        for (int i = 0; i < half; ++i) {
-          const float send = upper ? v[i] : v[half + i];
-          const float keep = upper ? v[half + i] : v[i];
-          v[i] = keep + __shfl_xor(send, m);
-        }
+        for (int i = 0; i < half; ++i) v[i] = pair_sum<m>(v[i], v[half + i], upper);
         ReduceScatter<m, half>::run(v, lane);
       } else {
-        v[0] += __shfl_xor(v[0], m);
+        v[0] = pair_sum<m>(v[0], v[0], upper);
         ReduceScatter<m, 1>::run(v, lane);
       }
     }
