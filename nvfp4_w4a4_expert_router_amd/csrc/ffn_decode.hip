@@ -17,6 +17,8 @@
 // weight's UE4M3 scale (exact), FP32 accumulation (Richland article, "What
 // shipped" and "Why it matters").  Dot products are finished by recursive
 // halving across lanes (fixed pairing: deterministic).
+#include <type_traits>
+
 #include "common.hpp"
 #include "routing.hpp"
 
@@ -310,8 +312,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
   for (int j = 0; j < kJ; ++j) sc[j] = *reinterpret_cast<const uint16_t*>(&sct[w][j][2 * l]);
   __syncthreads();
-  // 4. dot products, one activation row at a time
-  for (int rr = 0; rr < nrows; ++rr) {
+  // 4. dot products, one activation row at a time (the first row straight from
+  // the loaded codes; later rows through opaque copies, so the compiler cannot
+  // keep the decoded weights of the first row live across the loop)
+  auto dot_row = [&](int rr, auto reload) {
     half8_t a[4];
     const half8_t* src = reinterpret_cast<const half8_t*>(xs + (size_t)toks[rr] * H + l * 32);
     if (l < nch) {
@@ -324,13 +328,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     float acc[16];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      acc[j] = chunk32(opaque(q[j]), sc[j], a);
+      acc[j] = chunk32(decltype(reload)::value ? opaque(q[j]) : q[j], sc[j], a);
       __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: bounded live registers
     }
     ReduceScatter<64, kJ>::run(acc, l);
     // row w + 4j of the tile: gate column w + 4j, or up column w + 4j - kGuCols
     if ((l & (64 / kJ - 1)) == 0) gu[rr][w + 4 * ReduceScatter<64, kJ>::base(l)] = acc[0];
-  }
+  };
+  if (nrows > 0) dot_row(0, std::false_type{});
+  for (int rr = 1; rr < nrows; ++rr) dot_row(rr, std::true_type{});
   __syncthreads();
   // 5. SwiGLU + A4(h): kGuCols lanes per activation row (each 16-element block
   // a DPP row of 16 lanes); block maxima and code pairing by DPP, pairs of FP16
