@@ -245,8 +245,8 @@ int moe_combine(const moe_layer* L, int64_t T, const float* y_rows, const float*
  * (topk_idx, topk_w [T][k]; expert_off [E+1]; row2pair, pair2row [T*k];
  * y_rows [T*k][H]; y_shared [T][H] (nullable iff !has_shared); out [T][H];
  * residual nullable).  For decode batches (T <= 4, H <= 2048, E <= 512, no
- * dumps requested, the exact router, A4 activations; events allowed) it runs
- * fused in four kernels: router (FP64 logits and the A4 codes of x; events 0/1
+ * dumps requested, the exact router; A4 or A8 activations; events allowed) it
+ * runs fused in three kernels: router (FP64 logits and the codes of x; events 0/1
  * of moe_debug), gate/up (events 2/3; each workgroup selects the top k of the
  * batch, the softmax weights, the permutation and its expert from the FP64
  * logits, and one extra workgroup writes them out), down projection with the

@@ -354,8 +354,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
   if (!debug_ok(dbg)) return MOE_EINVAL;
   const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
-  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT ||
-      act8(L)) {
+  if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT) {
     if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_permute(L, topk_idx, T, expert_off, row2pair, pair2row, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_expert_ffn(L, x, T, expert_off, row2pair, y_rows, y_shared, dbg, ws, ws_bytes, stream))) return rc;
@@ -377,6 +376,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   q.E = L->E;
   q.k = L->k;
   q.g_in = L->a_gscale_in;
+  q.act8 = act8(L) ? 1 : 0;
   q.logits = reinterpret_cast<double*>(base);
   q.slot_tab = reinterpret_cast<int4*>(base + align_up((size_t)T * L->E * sizeof(double)));
   q.xq = reinterpret_cast<uint8_t*>(fbase + lay.xq);
@@ -422,6 +422,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.sh2k = L->has_shared ? L->sh2k : moe_nvfp4_bank{};
   p.g_in = L->a_gscale_in;
   p.g_mid = L->a_gscale_mid;
+  p.act8 = q.act8;
   p.hh = reinterpret_cast<half_t*>(fbase + lay.hh);
   p.y_rows = y_rows;
   p.y_shared = L->has_shared ? y_shared : nullptr;

@@ -576,6 +576,7 @@ struct RouteDecodeParams {
   int4* slot_tab;      // [T*k]
   const float* wg;     // [H] shared-expert gate vector (null: no gate)
   float* gate;         // [T] gate values out (when wg is set)
+  int act8;            // A8 codes of x (one INT8 per element, xq [T][H]) instead of A4
 };
 
 struct FfnParams {

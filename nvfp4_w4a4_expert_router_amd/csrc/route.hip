@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   };
   const bool has = e < E && 16 * L < H;
   if (has) load(16 * L);
-  // 2. A4 codes of x (fused): each DPP row of 16 lanes encodes one block (block
+  // 2. A4 (or A8) codes of x (fused): each DPP row of 16 lanes encodes one block (block
   // maximum and code pairs by DPP; the even lanes store one byte of two codes),
   // blocks b, b + 16 * grid, ... (the first element loaded above).  A whole
   // row takes the same branch, so the row operations see all 16 lanes.
@@ -333,11 +333,18 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
     for (int64_t bb = b; bb < nb; bb += (int64_t)16 * gridDim.x) {
       if (bb != b) xe = q.x[bb * 16 + (tid & 15)];
       const float v = __uint_as_float(xe << 16);
-      const uint32_t sc = scale_code(row16_absmax(v), 6.0f * q.g_in);
-      const uint32_t c = elem_code_s(v, sc ? ue4m3_value(sc) * q.g_in : __builtin_inff());
-      const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
-      if ((tid & 1) == 0) q.xq[bb * 8 + ((tid & 15) >> 1)] = (uint8_t)c2;
-      if ((tid & 15) == 0) q.xs[bb] = (uint8_t)sc;
+      const float amax = row16_absmax(v);
+      if (q.act8) {  // the W4A8 variant: UE4M3 scale from amax / (127 g), one INT8 code per element
+        const uint32_t sc = scale_code(amax, 127.0f * q.g_in);
+        q.xq[bb * 16 + (tid & 15)] = (uint8_t)(int8_code(v, sc ? ue4m3_value(sc) * q.g_in : __builtin_inff()) & 0xFF);
+        if ((tid & 15) == 0) q.xs[bb] = (uint8_t)sc;
+      } else {
+        const uint32_t sc = scale_code(amax, 6.0f * q.g_in);
+        const uint32_t c = elem_code_s(v, sc ? ue4m3_value(sc) * q.g_in : __builtin_inff());
+        const uint32_t c2 = c | ((uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xF, 0xF, true) << 4);
+        if ((tid & 1) == 0) q.xq[bb * 8 + ((tid & 15) >> 1)] = (uint8_t)c2;
+        if ((tid & 15) == 0) q.xs[bb] = (uint8_t)sc;
+      }
     }
   }
   // 3. the FP64 sums
