@@ -86,6 +86,7 @@ def parse():
     ap.add_argument("--stream-chunks", type=int, default=4)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode legs (profiling the prefill only)")
     ap.add_argument("--skip-t1", action="store_true", help="skip the 1-token decode leg")
+    ap.add_argument("--no-variants", action="store_true", help="skip the W4A8 and shared-gate decode timings")
     ap.add_argument("--no-clocks", action="store_true",
                     help="do not run amd-smi for the clock log (under a counter-collecting profiler)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -384,6 +385,46 @@ def main():
         if d1 is not None:
             rec["detail"]["decode_T1"] = summary(d1)
 
+        # ------------------------------------------------------------ layer variants
+        # the same 48 layers and token rotation at T tokens per step, one HIP graph of
+        # K steps per variant: the W4A8 activation encoding and the shared expert's gate
+        if args.graph_steps > 0 and not args.no_variants:
+            wg = (torch.randn(H, generator=torch.Generator().manual_seed(4242)) * 0.02).float().to(dev)
+            pool_v = [up(gen.make_tokens(4, T, step=s).view(np.int16)) for s in range(args.pool)]
+
+            def graph_us(variant):
+                lv = [variant(DL) for DL in layers]
+                bv = moe.Buffers(lv[0], T, dev)
+
+                def run():
+                    for i in range(K):
+                        moe.moe_layer_forward(lv[i % len(lv)], pool_v[i % len(pool_v)], bv, T=T)
+
+                run()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                evs = [(ev(), ev()) for _ in range(max(3, math.ceil(args.spread_steps / K)))]
+                for a_, b_ in evs:
+                    a_.record(stream)
+                    g.replay()
+                    b_.record(stream)
+                torch.cuda.synchronize()
+                us = pct([a_.elapsed_time(b_) * 1e3 / K for a_, b_ in evs], 50)
+                del g, bv
+                return round(us, 3)
+
+            var = {"tokens_per_step": T, "w4a4_us_per_step": round(d.get("us_per_step_median", float("nan")), 3)}
+            var["w4a8_us_per_step"] = graph_us(lambda DL: DL.with_act_bits(8))
+            var["shared_gate_us_per_step"] = graph_us(lambda DL: DL.with_shared_gate(wg))
+            rec["detail"]["decode_variants"] = var
+            log("decode variants (us per step at T=%d): %s" % (T, var))
+            del pool_v
+
         # ------------------------------------------------------------ the stack
         if not args.no_stack:
             stack = {}
@@ -497,6 +538,23 @@ def main():
                 modes[name] = round(pct([a_.elapsed_time(b_) for a_, b_ in pairs], 50), 4)
             out["route_ms_by_router_mode"] = modes
             log("router modes (ms): %s" % modes)
+            if not args.no_variants:
+                # the whole chunk through moe_layer_forward per layer variant
+                wg = (torch.randn(H, generator=torch.Generator().manual_seed(4242)) * 0.02).float().to(dev)
+                vms = {}
+                for name, Lv in (("w4a4", DLp), ("w4a8", DLp.with_act_bits(8)), ("shared_gate", DLp.with_shared_gate(wg))):
+                    bv = moe.Buffers(Lv, Tp, dev)
+                    moe.moe_layer_forward(Lv, xp, bv, T=Tp)
+                    pairs = [(ev(), ev()) for _ in range(n)]
+                    for a_, b_ in pairs:
+                        a_.record(stream)
+                        moe.moe_layer_forward(Lv, xp, bv, T=Tp)
+                        b_.record(stream)
+                    torch.cuda.synchronize()
+                    vms[name] = round(pct([a_.elapsed_time(b_) for a_, b_ in pairs], 50), 4)
+                    del bv
+                out["layer_forward_ms_by_variant"] = vms
+                log("prefill variants (ms per chunk): %s" % vms)
         return out, DLp, buf
 
     if args.prefill_tokens > 0:

@@ -159,6 +159,21 @@ class MoELayer:
         other.router_mode = mode
         return other
 
+    def with_act_bits(self, bits):
+        """The same layer (same device tensors) with another activation encoding (4 or 8)."""
+        other = self.with_router_mode(self.router_mode)
+        other.desc.act_bits = bits
+        other.act_bits = bits
+        return other
+
+    def with_shared_gate(self, shared_gate_w):
+        """The same layer (same device tensors) with the shared expert's gate vector
+        shared_gate_w ([H] float32 on the device; None: no gate)."""
+        other = self.with_router_mode(self.router_mode)
+        other.shared_gate_w = shared_gate_w
+        other.desc.shared_gate_w = _ptr(shared_gate_w)
+        return other
+
     def pack_kmajor(self, stream=None):
         """Write K-step-major copies of every bank (moe_pack_kmajor) and name them in
         the descriptor; returns self.  Needs H and I to be multiples of 64."""
