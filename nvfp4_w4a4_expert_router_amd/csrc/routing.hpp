@@ -28,8 +28,8 @@ struct RoutingLds {
 };
 
 // ---------------------------------------------------------------- shared-expert gate
-// z = sum_h x[t][h] * wg[h] over one wave (two elements per lane and step, FP64
-// sums of exact BF16 x FP32 products, a fixed reduction order), then
+// z = sum_h x[t][h] * wg[h] over one wave (FP64 sums of exact BF16 x FP32
+// products, a fixed reduction order), then
 // gate = fl32(1 / (1 + exp(-z))) in FP64.  An optional gate on the shared
 // expert is not on the pages (they list the shared expert as always on); this
 // is the plainest form such a gate takes.
@@ -37,11 +37,27 @@ __device__ __forceinline__ float shared_gate_wave(const uint16_t* __restrict__ x
                                                   int H) {
   const int lane = lane_id();
   double a = 0.0;
-  for (int h = 2 * lane; h < H; h += 2 * kWave) {
-    const uint32_t xv = *reinterpret_cast<const uint32_t*>(xr + h);
-    const float2 w = *reinterpret_cast<const float2*>(wg + h);
-    a = fma((double)__uint_as_float(xv << 16), (double)w.x, a);
-    a = fma((double)__uint_as_float(xv & 0xFFFF0000u), (double)w.y, a);
+  if (H % 8 == 0) {  // 8 elements per lane and step (16-byte loads, four steps in flight)
+#pragma unroll 4
+    for (int h = 8 * lane; h < H; h += 8 * kWave) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xr + h);
+      const float4 w0 = *reinterpret_cast<const float4*>(wg + h);
+      const float4 w1 = *reinterpret_cast<const float4*>(wg + h + 4);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a = fma((double)__uint_as_float(xw[i] << 16), (double)wf[2 * i], a);
+        a = fma((double)__uint_as_float(xw[i] & 0xFFFF0000u), (double)wf[2 * i + 1], a);
+      }
+    }
+  } else {
+    for (int h = 2 * lane; h < H; h += 2 * kWave) {
+      const uint32_t xv = *reinterpret_cast<const uint32_t*>(xr + h);
+      const float2 w = *reinterpret_cast<const float2*>(wg + h);
+      a = fma((double)__uint_as_float(xv << 16), (double)w.x, a);
+      a = fma((double)__uint_as_float(xv & 0xFFFF0000u), (double)w.y, a);
+    }
   }
   const double z = wave_sum_f64(a);
   return (float)(1.0 / (1.0 + exp(-z)));
