@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum {
   MOE_OK = 0,
@@ -107,8 +107,13 @@ typedef struct {
  *         RNE(amax / (127 g)), with INT8 element codes q = RNE(x / (s g))
  *         saturating at +-127.  A power-of-two activation global scale below 1
  *         (e.g. 2^-4 for N(0,1) hidden states) keeps its block scales in UE4M3's
- *         normal range.  Other values are MOE_ESHAPE.  A8 layers run the
- *         separate calls (moe_layer_forward does not fuse them).            */
+ *         normal range.  Other values are MOE_ESHAPE.
+ *   pre_norm, pre_norm_eps : moe_layer_forward only.  pre_norm = 1: the layer's
+ *         input is moe_rms_norm(x, pre_norm_eps) instead of x (the stack's
+ *         composition in one call; the residual argument is still added as
+ *         given), with results identical to the two calls; 0 (the default):
+ *         x as given.  The separate calls ignore these fields.  Other values,
+ *         or pre_norm_eps outside [0, 1], are MOE_EINVAL.                     */
 typedef struct {
   int32_t H, I, E, k, has_shared;
   const float* router_w;
@@ -119,6 +124,8 @@ typedef struct {
   const uint16_t* router_pieces;
   int32_t router_mode;
   int32_t act_bits;
+  int32_t pre_norm;
+  double pre_norm_eps;
 } moe_layer;
 
 enum { MOE_ROUTER_EXACT = 0, MOE_ROUTER_SPLIT3_F32 = 1, MOE_ROUTER_BF16 = 2 };

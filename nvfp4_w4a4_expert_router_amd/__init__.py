@@ -38,7 +38,8 @@ class LayerDesc(ctypes.Structure):
                 ("has_shared", ctypes.c_int32), ("router_w", ctypes.c_void_p), ("w13", Bank), ("w2", Bank),
                 ("sh13", Bank), ("sh2", Bank), ("a_gscale_in", ctypes.c_float), ("a_gscale_mid", ctypes.c_float),
                 ("w13k", Bank), ("w2k", Bank), ("sh13k", Bank), ("sh2k", Bank), ("shared_gate_w", ctypes.c_void_p),
-                ("router_pieces", ctypes.c_void_p), ("router_mode", ctypes.c_int32), ("act_bits", ctypes.c_int32)]
+                ("router_pieces", ctypes.c_void_p), ("router_mode", ctypes.c_int32), ("act_bits", ctypes.c_int32),
+                ("pre_norm", ctypes.c_int32), ("pre_norm_eps", ctypes.c_double)]
 
 
 MOE_ROUTER_EXACT, MOE_ROUTER_SPLIT3_F32, MOE_ROUTER_BF16 = 0, 1, 2
@@ -164,6 +165,14 @@ class MoELayer:
         other = self.with_router_mode(self.router_mode)
         other.desc.act_bits = bits
         other.act_bits = bits
+        return other
+
+    def with_pre_norm(self, eps=1e-6):
+        """The same layer whose moe_layer_forward takes RMSNorm(x) (moe_rms_norm with eps)
+        as its input: the stack's norm and layer in one call."""
+        other = self.with_router_mode(self.router_mode)
+        other.desc.pre_norm = 1
+        other.desc.pre_norm_eps = float(eps)
         return other
 
     def with_shared_gate(self, shared_gate_w):

@@ -153,6 +153,7 @@ size_t moe_workspace_bytes(const moe_layer* L, int64_t T_max) {
   if (permute_ws(L, T_max) > need) need = permute_ws(L, T_max);
   if (ffn_ws(L, T_max).end > need) need = ffn_ws(L, T_max).end;
   need += fused_logits_ws(L, T_max);
+  if (L->pre_norm == 1) need += align_up((size_t)T_max * L->H * sizeof(uint16_t));  // the normed input
   return need < kAlign ? kAlign : need;
 }
 
@@ -353,12 +354,36 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
     return MOE_EINVAL;
   if (L->has_shared && !ptr_ok(y_shared)) return MOE_EINVAL;
   if (!debug_ok(dbg)) return MOE_EINVAL;
+  if (L->pre_norm != 0 && L->pre_norm != 1) return MOE_EINVAL;
+  if (L->pre_norm && !(L->pre_norm_eps >= 0.0 && L->pre_norm_eps <= 1.0)) return MOE_EINVAL;
+  // pre_norm: the normed input [T][H] BF16 at the start of the workspace, the rest after it
+  uint16_t* xn = nullptr;
+  if (L->pre_norm) {
+    const size_t xn_bytes = align_up((size_t)T * L->H * sizeof(uint16_t));
+    if (ws_bytes < xn_bytes) return MOE_EWORKSPACE;
+    xn = static_cast<uint16_t*>(ws);
+    ws = static_cast<char*>(ws) + xn_bytes;
+    ws_bytes -= xn_bytes;
+  }
   const bool dumps = dbg && (dbg->xq || dbg->xs || dbg->h || dbg->hq || dbg->hs);
   if (!fused_decode_supported(L->H, L->I, L->E, L->k, T) || dumps || L->router_mode != MOE_ROUTER_EXACT) {
+    if (xn) {
+      if ((rc = launch_rc(launch_rms_norm(x, T, L->H, L->pre_norm_eps, xn, stream)))) return rc;
+      x = xn;
+    }
     if ((rc = moe_route(L, x, T, nullptr, topk_idx, topk_w, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_permute(L, topk_idx, T, expert_off, row2pair, pair2row, ws, ws_bytes, stream))) return rc;
     if ((rc = moe_expert_ffn(L, x, T, expert_off, row2pair, y_rows, y_shared, dbg, ws, ws_bytes, stream))) return rc;
     return moe_combine(L, T, y_rows, y_shared, pair2row, topk_w, residual, out, stream);
+  }
+  // pre_norm in the fused call: the router kernel norms x itself up to 2 tokens
+  // (every router workgroup recomputes the norm of every row: at 1 token it saves
+  // the norm kernel and its boundary, at 4 it costs more than it saves); from 3
+  // tokens on the norm kernel runs first
+  if (xn && T > 2) {
+    if ((rc = launch_rc(launch_rms_norm(x, T, L->H, L->pre_norm_eps, xn, stream)))) return rc;
+    x = xn;
+    xn = nullptr;
   }
   const size_t lg_bytes = fused_logits_ws(L, T);
   const FfnWs lay = ffn_ws(L, T);
@@ -377,6 +402,9 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   q.k = L->k;
   q.g_in = L->a_gscale_in;
   q.act8 = act8(L) ? 1 : 0;
+  q.pre_norm = xn ? 1 : 0;  // the router kernel norms x itself and writes the normed rows to xn
+  q.norm_eps = L->pre_norm_eps;
+  q.xn = xn;
   q.logits = reinterpret_cast<double*>(base);
   q.slot_tab = reinterpret_cast<int4*>(base + align_up((size_t)T * L->E * sizeof(double)));
   q.xq = reinterpret_cast<uint8_t*>(fbase + lay.xq);
@@ -395,6 +423,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
     q.gate = gate;
   }
   if ((rc = launch_rc(launch_route_decode(q, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr)))) return rc;
+  if (xn) q.x = xn;  // the layer's input from here on (the publisher's shared-expert gate)
   // kernels 2, 3: gate/up (with the routing) and down over the slot table;
   // kernel 4: combine
   FfnParams p = {};

@@ -243,6 +243,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// FP64 -> BF16 bits, round to nearest even (finite inputs; BF16 subnormal
+// results go through FP32, where they are exact after this rounding)
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  const int e = (int)((u >> 52) & 0x7FF) - 1023;
+  if (v == 0.0) return (uint16_t)sign;
+  if (e < -126 || e > 127) return f32_to_bf16_rne((float)v);
+  const unsigned long long m = u & 0xFFFFFFFFFFFFFull;
+  unsigned long long q = m >> 45;                        // 7 mantissa bits
+  const unsigned long long rest = m & ((1ull << 45) - 1);
+  const unsigned long long half = 1ull << 44;
+  uint32_t be = (uint32_t)(e + 127);
+  if (rest > half || (rest == half && (q & 1ull))) {
+    if (++q == 128ull) {
+      q = 0ull;
+      ++be;
+    }
+  }
+  return (uint16_t)(sign | (be << 7) | (uint32_t)q);
+}
+
+
 // silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (a few ulp; far
 // inside the FP32 accumulation error of the sums that produce z).  Large negative
 // z gives exp = inf and a signed zero, keeping the sign of the exact value.
@@ -577,6 +600,9 @@ struct RouteDecodeParams {
   const float* wg;     // [H] shared-expert gate vector (null: no gate)
   float* gate;         // [T] gate values out (when wg is set)
   int act8;            // A8 codes of x (one INT8 per element, xq [T][H]) instead of A4
+  int pre_norm;        // x is normed first (RMS norm, norm_eps) and the normed rows go to xn
+  double norm_eps;
+  uint16_t* xn;        // [T][H] BF16
 };
 
 struct FfnParams {

@@ -8,28 +8,6 @@
 
 namespace moe {
 
-// FP64 -> BF16 bits, round to nearest even (finite inputs; BF16 subnormal
-// results go through FP32, where they are exact after this rounding)
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
-  const unsigned long long u = __double_as_longlong(v);
-  const uint32_t sign = (uint32_t)(u >> 63) << 15;
-  const int e = (int)((u >> 52) & 0x7FF) - 1023;
-  if (v == 0.0) return (uint16_t)sign;
-  if (e < -126 || e > 127) return f32_to_bf16_rne((float)v);
-  const unsigned long long m = u & 0xFFFFFFFFFFFFFull;
-  unsigned long long q = m >> 45;                        // 7 mantissa bits
-  const unsigned long long rest = m & ((1ull << 45) - 1);
-  const unsigned long long half = 1ull << 44;
-  uint32_t be = (uint32_t)(e + 127);
-  if (rest > half || (rest == half && (q & 1ull))) {
-    if (++q == 128ull) {
-      q = 0ull;
-      ++be;
-    }
-  }
-  return (uint16_t)(sign | (be << 7) | (uint32_t)q);
-}
-
 // One workgroup per row: each thread holds 8 consecutive elements (one 16-byte
 // load, a second round only for H > 2048), the FP64 sum of squares goes
 // through the wave sums and LDS, and the thread scales and stores its own

@@ -278,34 +278,53 @@ __global__ __launch_bounds__(256) void k_router_norms(const float* __restrict__ 
 // election inside the logits kernel needs a device-scope hand-off per
 // workgroup, which measured slower than the kernel boundary.)
 constexpr int kGemvMaxT = 8;
-template <bool kFused>
+// kNorm (fused call with pre_norm, T <= 4, H <= 2048): x is first normed in the
+// workgroup exactly as k_rms_norm norms it (each thread's 8 consecutive
+// elements, FP64 sums of squares in the same order, the wave sums and the four
+// wave totals in order, the product in FP64 rounded once to BF16), the normed
+// rows are kept in LDS for the encoding and the FP64 sums, and workgroup 0
+// writes them to q.xn.
+template <bool kFused, bool kNorm>
 __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   __shared__ double part[2][kGemvMaxT][2];
+  __shared__ __align__(16) uint16_t xnl[kNorm ? 4 * 2048 : 8];
+  __shared__ double nsum[kNorm ? 4 * 4 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int T = q.T, H = q.H, E = q.E;
-  // 1. loads in dependency order: this lane's element of an A4 block of x
-  // (fused: 16 lanes per block, blocks workgroup + grid * (tid / 16) + ..., so
-  // every workgroup encodes a few), then the first router and x chunks; the
-  // encoding runs while the router rows are in flight
+  // 1. loads in dependency order: (kNorm) this thread's 8 elements of every row,
+  // (fused) this lane's element of an A4 block of x (16 lanes per block, blocks
+  // workgroup + grid * (tid / 16) + ..., so every workgroup encodes a few), then
+  // the first router and x chunks; the encoding runs while the router rows are
+  // in flight
+  uint4 xr[kNorm ? 4 : 1];
+  if (kNorm) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xr[t] = (t < T && 8 * tid < H) ? *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + 8 * tid)
+                                                               : make_uint4(0u, 0u, 0u, 0u);
+  }
   const int64_t nb = kFused ? (int64_t)T * (H / 16) : 0;
   const int64_t b = (int64_t)(tid >> 4) * gridDim.x + blockIdx.x;
   const bool enc = b < nb;
   uint32_t xe = 0u;
-  if (enc) xe = q.x[b * 16 + (tid & 15)];
+  if (!kNorm && enc) xe = q.x[b * 16 + (tid & 15)];
   // logits of expert e: lane L of the expert's wave pair owns elements h0 .. h0 + 15
   const int e = 2 * blockIdx.x + (wave >> 1);
   const int L = kWave * (wave & 1) + lane;
   double acc[kGemvMaxT][2] = {};
   float4 wv[4];
   uint4 xv[kGemvMaxT][2];
-  auto load = [&](int h0) {
+  auto load_w = [&](int h0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const float4*>(q.W + (int64_t)e * H + h0 + 4 * i);
+  };
+  auto load_x = [&](int h0) {
 #pragma unroll
     for (int t = 0; t < kGemvMaxT; ++t)
       if (t < T)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) xv[t][i] = *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + h0 + 8 * i);
+        for (int i = 0; i < 2; ++i)
+          xv[t][i] = kNorm ? *reinterpret_cast<const uint4*>(&xnl[t * H + h0 + 8 * i])
+                           : *reinterpret_cast<const uint4*>(q.x + (int64_t)t * H + h0 + 8 * i);
   };
   auto fma_chunk = [&]() {
     const float wf[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
@@ -324,14 +343,64 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
     }
   };
   const bool has = e < E && 16 * L < H;
-  if (has) load(16 * L);
+  if (has) {
+    load_w(16 * L);
+    if (!kNorm) load_x(16 * L);
+  }
+  if (kNorm) {
+    // the RMS norm of every row (k_rms_norm's arithmetic and order)
+    double ss[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t w4[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double lo = __uint_as_float(w4[i] << 16), hi = __uint_as_float(w4[i] & 0xFFFF0000u);
+        a = fma(lo, lo, a);
+        a = fma(hi, hi, a);
+      }
+      ss[t] = a;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < T) {
+        const double sw = wave_sum_f64(ss[t]);
+        if (lane == 0) nsum[t * 4 + wave] = sw;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < T && 8 * tid < H) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) tot += nsum[t * 4 + w];
+        const double inv = 1.0 / sqrt(tot / (double)H + q.norm_eps);
+        const uint32_t w4[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = f64_to_bf16_rne((double)__uint_as_float(w4[i] << 16) * inv);
+          const uint32_t hi = f64_to_bf16_rne((double)__uint_as_float(w4[i] & 0xFFFF0000u) * inv);
+          o[i] = lo | (hi << 16);
+        }
+        const uint4 nv = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(&xnl[t * H + 8 * tid]) = nv;
+        if (blockIdx.x == 0) *reinterpret_cast<uint4*>(q.xn + (int64_t)t * H + 8 * tid) = nv;
+      }
+    }
+    __syncthreads();
+    if (enc) xe = xnl[b * 16 + (tid & 15)];
+    if (has) load_x(16 * L);
+  }
   // 2. A4 (or A8) codes of x (fused): each DPP row of 16 lanes encodes one block (block
   // maximum and code pairs by DPP; the even lanes store one byte of two codes),
   // blocks b, b + 16 * grid, ... (the first element loaded above).  A whole
   // row takes the same branch, so the row operations see all 16 lanes.
   if (kFused) {
     for (int64_t bb = b; bb < nb; bb += (int64_t)16 * gridDim.x) {
-      if (bb != b) xe = q.x[bb * 16 + (tid & 15)];
+      if (bb != b) xe = kNorm ? xnl[bb * 16 + (tid & 15)] : q.x[bb * 16 + (tid & 15)];
       const float v = __uint_as_float(xe << 16);
       const float amax = row16_absmax(v);
       if (q.act8) {  // the W4A8 variant: UE4M3 scale from amax / (127 g), one INT8 code per element
@@ -351,7 +420,8 @@ __global__ __launch_bounds__(256) void k_route_decode(RouteDecodeParams q) {
   if (has) {
     fma_chunk();
     for (int h0 = 16 * L + 2048; h0 < H; h0 += 2048) {
-      load(h0);
+      load_w(h0);
+      load_x(h0);
       fma_chunk();
     }
   }
@@ -737,7 +807,11 @@ bool route_decode_supported(int H, int E, int k, int64_t T) {
 // the FP64 logits and the A4 codes of x; the selection runs in the gate/up
 // kernel's workgroups (routing.hpp)
 hipError_t launch_route_decode(const RouteDecodeParams& q, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
-  return launch_timed(k_route_decode<true>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before, ev_after, q);
+  if (q.pre_norm)
+    return launch_timed(k_route_decode<true, true>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before,
+                        ev_after, q);
+  return launch_timed(k_route_decode<true, false>, dim3((unsigned)((q.E + 1) / 2)), dim3(256), 0, s, ev_before,
+                      ev_after, q);
 }
 
 static float gamma_for_depth(int d) {
@@ -792,7 +866,7 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
     q.E = E;
     q.k = k;
     q.logits = static_cast<double*>(ws);
-    hipLaunchKernelGGL(k_route_decode<false>, dim3((unsigned)((E + 1) / 2)), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((k_route_decode<false, false>), dim3((unsigned)((E + 1) / 2)), dim3(256), 0, s, q);
     p.l64 = q.logits;
     p.mode = kSelF64;
   } else {

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert moe.lib.moe_abi_version() == 3
+    assert moe.lib.moe_abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert moe.strerror(code) and moe.strerror(code) != "unknown error"
     assert moe.strerror(-99) == "unknown error"
@@ -123,6 +123,22 @@ def test_router_mode_gate_and_act_bits_validated():
         moe.lib.moe_workspace_bytes(ctypes.byref(layer(shared=0)), 4096)
     assert moe.lib.moe_pack_router(FAKE, 0, 2048, FAKE, None) == moe.MOE_ESHAPE
     assert moe.lib.moe_pack_router(FAKE, 512, 2048, None, None) == moe.MOE_EINVAL
+
+
+def test_pre_norm_validated():
+    """pre_norm (moe_layer_forward only) takes 0 or 1 and an eps in [0, 1]; it adds the
+    normed input's T * H BF16 to the workspace, checked before anything runs."""
+    def fwd(L, wsb=1 << 30):
+        return moe.lib.moe_layer_forward(ctypes.byref(L), FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, None, FAKE, wsb, None)
+    assert fwd(layer(pre_norm=2, pre_norm_eps=1e-6)) == moe.MOE_EINVAL
+    assert fwd(layer(pre_norm=-1)) == moe.MOE_EINVAL
+    for eps in (-1e-6, 1.5, float("nan")):
+        assert fwd(layer(pre_norm=1, pre_norm_eps=eps)) == moe.MOE_EINVAL
+    assert fwd(layer(pre_norm=1, pre_norm_eps=1e-6), wsb=4 * 2048 * 2 - 1) == moe.MOE_EWORKSPACE
+    base = moe.lib.moe_workspace_bytes(ctypes.byref(layer()), 300)
+    normed = moe.lib.moe_workspace_bytes(ctypes.byref(layer(pre_norm=1, pre_norm_eps=1e-6)), 300)
+    assert normed - base >= 300 * 2048 * 2
 
 
 def test_w4a8_validation_and_workspace():

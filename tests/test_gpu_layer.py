@@ -423,3 +423,31 @@ def test_layer_without_shared_expert(T):
         moe.moe_layer_forward(DL, gh.to_dev(x.view(np.int16)), buf)
         torch.cuda.synchronize()
         assert np.array_equal(buf.out.cpu().numpy().view(np.uint16), g["out"])
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w4a8", "gate"])
+@pytest.mark.parametrize("cfg,T", [(1, 1), (1, 2), (1, 4), (0, 3), (1, 7), (1, 300)])
+def test_pre_norm_matches_norm_then_layer(cfg, T, variant):
+    """pre_norm: moe_layer_forward on x with the norm inside (fused decode: in the router
+    kernel; otherwise the norm kernel first) writes exactly what moe_rms_norm followed by
+    moe_layer_forward writes, with the residual x added in both."""
+    gh.log("case: pre_norm config %d T=%d %s" % (cfg, T, variant))
+    L, DL = layer_for(cfg)
+    if variant == "w4a8":
+        DL = DL.with_act_bits(8)
+    elif variant == "gate":
+        wg = gen.normal_f32_rows(gen.stream_key(gen.BASE_SEED, cfg, 0, gen.TENSOR_SHGATE), np.array([0.02]), L.shape.H)[0]
+        DL = DL.with_shared_gate(gh.to_dev(wg))
+    x = gh.to_dev(gen.make_tokens(cfg, T, step=51).view(np.int16))
+    eps = 1e-6
+    ref = moe.Buffers(DL, T, gh.DEV)
+    n = torch.empty_like(x)
+    moe.moe_rms_norm(x, n, eps=eps)
+    moe.moe_layer_forward(DL, n, ref, residual=x)
+    DN = DL.with_pre_norm(eps)
+    got = moe.Buffers(DN, T, gh.DEV)
+    moe.moe_layer_forward(DN, x, got, residual=x)
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "expert_off", "row2pair", "pair2row", "y_rows", "y_shared", "out"):
+        a, b = getattr(got, key).cpu().numpy(), getattr(ref, key).cpu().numpy()
+        assert np.array_equal(a, b), key
