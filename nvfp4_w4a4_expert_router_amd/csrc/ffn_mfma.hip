@@ -455,14 +455,18 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
   const uint32_t voff0 = (uint32_t)(4 * (lane >> 5) * H) * 4u;
   if (shared && p.sh_gate) {
-    // shared rows are tokens m0 + row: each scaled by its gate (rows past the
-    // segment read the last token's and are dropped by the store's range check)
+    // shared rows are tokens m0 + row: each scaled by its gate, the tile's 128
+    // gates staged in LDS once (rows past the segment read the last token's and
+    // are dropped by the store's range check)
+    __shared__ float gsh[128];
+    if (threadIdx.x < 128) gsh[threadIdx.x] = p.sh_gate[m0 + (int)threadIdx.x < T ? m0 + (int)threadIdx.x : T - 1];
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int dm = 32 * i + 8 * (q >> 2) + (q & 3) + 4 * (lane >> 5);
-        const float gr = p.sh_gate[m0 + dm < T ? m0 + dm : T - 1];
+        const float gr = gsh[dm];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = nt * kBN + bj(j) + (lane & 31);
