@@ -130,25 +130,6 @@ __device__ __forceinline__ uint32_t elem_code_t(float v, const E2M1Thresholds& T
   return mag | (__float_as_uint(v) >> 31 << 3);
 }
 
-// A4 encoding of one 16-element block (global scale g, g6 = 6g): returns the
-// UE4M3 scale code; the 16 E2M1 codes go to *packed, element i in bits
-// 4(i % 8).. of word i / 8 (the low nibble of each byte first).
-__device__ __forceinline__ uint32_t encode_a4_block16(const float (&v)[16], float g, float g6, uint2* packed) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sc = scale_code(amax, g6);
-  const float s = ue4m3_value(sc) * g;
-  uint32_t p0 = 0u, p1 = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p0 |= elem_code(v[i], s) << (4 * i);
-    p1 |= elem_code(v[8 + i], s) << (4 * i);
-  }
-  *packed = make_uint2(p0, p1);
-  return sc;
-}
-
 // ---------------------------------------------------------------- A8 (the W4A8 variant)
 // A8 keeps A4's 16-element blocks and UE4M3 block scale, chosen as
 // RNE(amax / (127 g)) (scale_code with 127 g in place of 6 g: the thresholds
@@ -307,19 +288,11 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-
-// 4-byte store through a buffer resource; offsets at or past the resource's size
-// are dropped (the offset is all in voff: the range check covers it).
-__device__ __forceinline__ void buffer_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
-}
-
-// The same with the non-temporal cache policy (bit 1 of the policy operand on
-// this chip family: `nt`): for output written once and read much later, so it
-// does not displace operands that are being reused in L2.
+// 4-byte store through a buffer resource (offsets at or past the resource's
+// size are dropped: the offset is all in voff, so the range check covers it),
+// with the non-temporal cache policy (bit 1 of the policy operand on this chip
+// family: `nt`): for output written once and read much later, so it does not
+// displace operands that are being reused in L2.
 __device__ __forceinline__ void buffer_store4_nt(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 2);
 }
@@ -361,11 +334,6 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 template <int kCtrl, int kRowMask, bool kZeroOld>
 __device__ __forceinline__ int dpp_mov(int v) {
   return __builtin_amdgcn_update_dpp(kZeroOld ? 0 : v, v, kCtrl, kRowMask, 0xF, true);
-}
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
 }
 
 // max of |v| over each row of 16 lanes, returned in every lane of the row

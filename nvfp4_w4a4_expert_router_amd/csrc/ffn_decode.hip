@@ -123,16 +123,6 @@ struct ReduceScatter {
   }
 };
 
-template <int kG>
-__device__ __forceinline__ void reduce_scatter16(float (&v)[16], int lane) {
-  ReduceScatter<kG, 16>::run(v, lane);
-}
-
-template <int kG>
-__device__ __forceinline__ int scatter_base(int lane) {
-  return ReduceScatter<kG, 16>::base(lane);
-}
-
 // Slot -> expert (the s-th expert with a nonzero count), one round trip.
 __device__ __forceinline__ int active_expert(const int32_t* __restrict__ off, int E, int s, int* row0, int* cnt) {
   const int lane = lane_id();
