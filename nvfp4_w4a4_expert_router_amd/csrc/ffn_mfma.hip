@@ -87,10 +87,27 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
 // 16 B per transfer: 8 A rows or 32 B rows; 64 lanes x 4 B: 64 scale words), so
 // the ring costs no registers and is filled 2 steps ahead.
 constexpr int kStages = 3;
+struct Stage {
+  uint4 a[kBM * 8];
+  uint4 b[kBN * 2];
+  uint32_t s[kBN];
+};
+// The three stages are separate LDS variables, so the compiler can tell that
+// the transfers into one stage and the reads of another do not overlap.  With
+// one array it cannot, and it made every read wait for all transfers in flight
+// (the two steps issued ahead included), which left the matrix cores waiting
+// out a memory round trip every step.  For the same reason the ring's barrier
+// is ring_barrier (common.hpp), not __syncthreads.
 struct Ring {
-  uint4 a[kStages][kBM * 8];
-  uint4 b[kStages][kBN * 2];
-  uint32_t s[kStages][kBN];
+  Stage& st0;
+  Stage& st1;
+  Stage& st2;
+  template <int kS>
+  __device__ __forceinline__ Stage& at() {
+    if constexpr (kS % kStages == 0) return st0;
+    else if constexpr (kS % kStages == 1) return st1;
+    else return st2;
+  }
 };
 
 // One operand set: buffer resources and per-lane byte offsets (a K step at
@@ -141,28 +158,27 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   const int nlive = __builtin_amdgcn_readfirstlane(live_rows > 0 ? 1 : 0);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // n = 1: the prologue repeats step 0
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
-  auto dma = [&](int t, int stage) {
+  auto dma = [&](int t, Stage& S) {
     const uint32_t k0 = kof(t);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.a, (lds_ptr_t)&ring.a[stage][(32 * wave + 8 * c) * 8], 16, O.adma[c],
-                                               k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.a, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
+                                               0);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bq, (lds_ptr_t)&ring.b[stage][(64 * wave + 32 * c) * 2], 16, O.bdma[c],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bq, (lds_ptr_t)&S.b[(64 * wave + 32 * c) * 2], 16, O.bdma[c],
                                                k0 / 2 * O.bmul, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&ring.s[stage][64 * wave], 4, O.sdma,
-                                             k0 / 16 * O.bmul, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&S.s[64 * wave], 4, O.sdma, k0 / 16 * O.bmul, 0, 0);
   };
-  auto compute = [&](int stage) {
+  auto compute = [&](Stage& S) {
     if (nlive == 0) return;
     uint4 bq[2];
     half2_t sv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = bj(j) + (lane & 31);
-      bq[j] = ring.b[stage][r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
-      sv[j] = ue4m3x2_to_half2(ring.s[stage][r] >> (16 * hk));
+      bq[j] = S.b[r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
+      sv[j] = ue4m3x2_to_half2(S.s[r] >> (16 * hk));
     }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
@@ -170,7 +186,7 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 #pragma unroll
       for (int i = 0; i < kRB; ++i) {
         const int row = 32 * i + (lane & 31);
-        a[i] = __builtin_bit_cast(half8_t, ring.a[stage][row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
+        a[i] = __builtin_bit_cast(half8_t, S.a[row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -189,31 +205,26 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
     }
   };
 
-  // vmcnt(7) (expcnt, lgkmcnt untouched): the wave's 7 newest transfers (the step
-  // issued last) may still be in flight; the one before is complete, and the
-  // barrier then publishes it to the other waves
-  auto wait_ring = [&]() { __builtin_amdgcn_s_waitcnt(0xF77); };  // vmcnt 7, expcnt 7, lgkmcnt 15
-  dma(0, 0);
-  dma(1, 1);
-  wait_ring();
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
+  // vmcnt(7): the wave's 7 newest transfers (the step issued last) may still be
+  // in flight; the one before is complete, and the barrier then publishes it
+  // to the other waves
+  dma(0, ring.at<0>());
+  dma(1, ring.at<1>());
+  ring_barrier<7>();
   // step t: transfers for step t + 2 into stage (t + 2) % 3 (last read in step
   // t - 1, before the previous barrier), then the MFMAs of step t.  The last
   // two steps issue no transfers and wait for all of theirs instead.
   auto phase = [&](auto pc, int t) {
     constexpr int P = decltype(pc)::value;  // t % 3
     const bool more = t + 2 < n;  // uniform
-    if (more) dma(t + 2, (P + 2) % kStages);
+    if (more) dma(t + 2, ring.at<P + 2>());
     __builtin_amdgcn_sched_barrier(0);
-    compute(P);
+    compute(ring.at<P>());
     __builtin_amdgcn_sched_barrier(0);
     if (more)
-      wait_ring();
+      ring_barrier<7>();
     else
-      __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt 0, expcnt 7, lgkmcnt 15
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+      ring_barrier<0>();
   };
   int t = 0;
   for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
@@ -232,7 +243,8 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
 // operand.  Codes and scales are written only to the debug dumps.
 __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
                                                         const int4* __restrict__ tile_tab) {
-  __shared__ Ring ring;
+  __shared__ __align__(16) Stage st0, st1, st2;
+  Ring ring{st0, st1, st2};
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = I / 128;
   const int nseg = E + 1;
@@ -402,7 +414,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
 // + 63 of all 128 rows as blocks j = 0, 1.
 __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
                                                       const int4* __restrict__ tile_tab) {
-  __shared__ Ring ring;
+  __shared__ __align__(16) Stage st0, st1, st2;
+  Ring ring{st0, st1, st2};
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = H / kBN;
   const int nseg = E + 1;

@@ -123,12 +123,15 @@ __global__ __launch_bounds__(256) void k_router_round_bf16(const float* __restri
 // of r plus twice (bit 1 xor bit 3), so the MFMA reads of 16 consecutive rows
 // fall in 16 different 16-byte bank groups).  A ring of 3 stages (120 KB with
 // 3 pieces, one workgroup per CU) filled by buffer loads that write LDS
-// directly, two steps ahead.
+// directly, two steps ahead.  The stages are separate LDS variables (so the
+// compiler does not make the reads of one wait for the transfers into
+// another) and the ring's barrier is ring_barrier.
 template <int NP>
-struct RouterRing {
-  uint4 a[RM_S][RM_T * 4];
-  uint4 b[RM_S][NP][RM_E * 4];
+struct RouterStage {
+  uint4 a[RM_T * 4];
+  uint4 b[NP][RM_E * 4];
 };
+static_assert(RM_S == 3, "three stages, selected at compile time");
 
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -143,8 +146,13 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
                                                             const uint16_t* __restrict__ Wp, int T, int H, int E,
                                                             float* __restrict__ logits) {
   static_assert(NP == 1 || NP == 3, "pieces");
-  constexpr int kWaitStep = NP == 3 ? 0xF75 : 0xF73;  // vmcnt(2 + NP), expcnt 7, lgkmcnt 15
-  __shared__ RouterRing<NP> ring;
+  __shared__ __align__(16) RouterStage<NP> rs0, rs1, rs2;
+  auto stage = [&](auto kc) -> RouterStage<NP>& {
+    constexpr int k = decltype(kc)::value % RM_S;
+    if constexpr (k == 0) return rs0;
+    else if constexpr (k == 1) return rs1;
+    else return rs2;
+  };
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   // expert tile major within each XCD's run: one XCD keeps one expert tile's
   // router rows (3 pieces x 128 rows x H) in its L2 while token tiles stream by
@@ -165,16 +173,16 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
   }
   const uint32_t boff = (uint32_t)(e0 + (lane >> 2)) * H * 2u + sw;
   // two A and NP B transfers per wave and step (steps past the last repeat it)
-  auto dma = [&](int t, int st) {
+  auto dma = [&](int t, RouterStage<NP>& S) {
     const uint32_t k0 = (uint32_t)((t < n ? t : n - 1) * RM_K);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&ring.a[st][(32 * wave + 16 * i) * 4], 16, aoff[i],
-                                               k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&S.a[(32 * wave + 16 * i) * 4], 16, aoff[i], k0 * 2, 0,
+                                               0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int q = NP * wave + i, pc = q >> 3, c = q & 7;  // piece, 16-row group
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&ring.b[st][pc][16 * c * 4], 16, boff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&S.b[pc][16 * c * 4], 16, boff,
                                                k0 * 2 + (uint32_t)(pc * E + 16 * c) * H * 2u, 0, 0);
     }
   };
@@ -188,24 +196,25 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
   const int swz = swz_of(r32);
   // vmcnt(2 + NP): the newest step's transfers may be in flight, the one before
   // is complete (the barrier then publishes it)
-  dma(0, 0);
-  dma(1, 1);
-  __builtin_amdgcn_s_waitcnt(kWaitStep);
-  __syncthreads();
-  int st = 0;  // t % 3
-  for (int t = 0; t < n; ++t) {
-    dma(t + 2, st == 0 ? 2 : st - 1);  // stage (t + 2) % 3, last read in step t - 1, before the barrier
+  dma(0, rs0);
+  dma(1, rs1);
+  ring_barrier<2 + NP>();
+  // step t (stage t % 3, a compile-time index): transfers for step t + 2 into
+  // stage (t + 2) % 3, last read in step t - 1, before the barrier
+  auto step = [&](auto pc, int t) {
+    dma(t + 2, stage(IntC<decltype(pc)::value + 2>{}));
+    RouterStage<NP>& S = stage(pc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fresh[j] = floatx16{};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int slot = (2 * hk + s2) ^ swz;
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ring.a[st][(32 * wave + r32) * 4 + slot]);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, S.a[(32 * wave + r32) * 4 + slot]);
 #pragma unroll
-      for (int pc = NP - 1; pc >= 0; --pc)
+      for (int pc2 = NP - 1; pc2 >= 0; --pc2)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, ring.b[st][pc][(32 * j + r32) * 4 + slot]);
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, S.b[pc2][(32 * j + r32) * 4 + slot]);
           fresh[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, fresh[j], 0, 0, 0);
         }
     }
@@ -218,10 +227,14 @@ __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __re
         grp[j] = floatx16{};
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitStep);  // this wave's transfers for step t + 1 are complete
-    __syncthreads();
-    st = st == 2 ? 0 : st + 1;
-  }
+    ring_barrier<2 + NP>();  // this wave's transfers for step t + 1 are complete
+  };
+  int t = 0;
+  for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { step(pc, t + decltype(pc)::value); });
+  const int rem = n - t;
+  static_for<0, 2>([&](auto pc) {
+    if (decltype(pc)::value < rem) step(pc, t + decltype(pc)::value);
+  });
   __builtin_amdgcn_s_waitcnt(0xF70);  // no transfer into LDS outlives the loop
   // lane holds experts 32 j + lane % 32 of tokens 32 w + 8 (q / 4) + 4 (lane / 32) + q % 4
 #pragma unroll
