@@ -116,6 +116,7 @@ struct Ring {
 // the wave's c-th A / B transfer; sdma: the B row whose scales this lane moves.
 struct Operands {
   __amdgpu_buffer_rsrc_t a, bq, bs;
+  __amdgpu_buffer_rsrc_t a0, bq0, bs0;  // the same with no bytes: every access out of range
   uint32_t adma[4], bdma[2], sdma;
   uint32_t bmul;  // B bytes per K step: 32 bmul of codes, 4 bmul of scales
 };
@@ -158,17 +159,23 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   const int nlive = __builtin_amdgcn_readfirstlane(live_rows > 0 ? 1 : 0);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // n = 1: the prologue repeats step 0
   // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
-  auto dma = [&](int t, Stage& S) {
+  // real = false (the last two steps): the same transfers through resources of
+  // no bytes, which read nothing and write zeros into the stage no later step
+  // reads.  Issuing them keeps every step's transfers unconditional: around a
+  // conditional transfer the compiler cannot tell which stage is in flight and
+  // makes the next reads wait for all of them.
+  auto dma = [&](int t, Stage& S, bool real) {
     const uint32_t k0 = kof(t);
+    const __amdgpu_buffer_rsrc_t ra = real ? O.a : O.a0, rq = real ? O.bq : O.bq0, rs = real ? O.bs : O.bs0;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.a, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
                                                0);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bq, (lds_ptr_t)&S.b[(64 * wave + 32 * c) * 2], 16, O.bdma[c],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr_t)&S.b[(64 * wave + 32 * c) * 2], 16, O.bdma[c],
                                                k0 / 2 * O.bmul, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(O.bs, (lds_ptr_t)&S.s[64 * wave], 4, O.sdma, k0 / 16 * O.bmul, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&S.s[64 * wave], 4, O.sdma, k0 / 16 * O.bmul, 0, 0);
   };
   auto compute = [&](Stage& S) {
     if (nlive == 0) return;
@@ -208,23 +215,19 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
   // vmcnt(7): the wave's 7 newest transfers (the step issued last) may still be
   // in flight; the one before is complete, and the barrier then publishes it
   // to the other waves
-  dma(0, ring.at<0>());
-  dma(1, ring.at<1>());
+  dma(0, ring.at<0>(), true);
+  dma(1, ring.at<1>(), true);
   ring_barrier<7>();
   // step t: transfers for step t + 2 into stage (t + 2) % 3 (last read in step
   // t - 1, before the previous barrier), then the MFMAs of step t.  The last
-  // two steps issue no transfers and wait for all of theirs instead.
+  // two steps' transfers read nothing.
   auto phase = [&](auto pc, int t) {
     constexpr int P = decltype(pc)::value;  // t % 3
-    const bool more = t + 2 < n;  // uniform
-    if (more) dma(t + 2, ring.at<P + 2>());
+    dma(t + 2, ring.at<P + 2>(), t + 2 < n);
     __builtin_amdgcn_sched_barrier(0);
     compute(ring.at<P>());
     __builtin_amdgcn_sched_barrier(0);
-    if (more)
-      ring_barrier<7>();
-    else
-      ring_barrier<0>();
+    ring_barrier<7>();
   };
   int t = 0;
   for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   auto bj = [&](int j) { return j == 0 ? wn : 128 + wn; };
   Operands O;
   O.a = buffer_rsrc(p.xh, (uint32_t)T * H * 2u);
+  O.a0 = buffer_rsrc(p.xh, 0u);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     // A row: the token of tile row 32 w + 8 c + lane / 8 (rows past the segment read token 0; dropped)
@@ -279,6 +283,8 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   }
   O.bq = buffer_rsrc(codes, 2u * I * (H / 2));
   O.bs = buffer_rsrc(scales, 2u * I * (H / 16));
+  O.bq0 = buffer_rsrc(codes, 0u);
+  O.bs0 = buffer_rsrc(scales, 0u);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     // B transfer c: ring rows 64 w + 32 c + lane / 2, half (lane % 2) ^ (row / 4 % 2)
@@ -441,12 +447,15 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
   Operands O;
   O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)nrows * I * 2u);
+  O.a0 = buffer_rsrc(p.hh + row0 * I, 0u);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u +
                 (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
   O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
   O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
+  O.bq0 = buffer_rsrc(codes, 0u);
+  O.bs0 = buffer_rsrc(scales, 0u);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int r = 64 * wave + 32 * c + (lane >> 1);
