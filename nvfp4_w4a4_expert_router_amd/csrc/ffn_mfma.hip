@@ -26,6 +26,7 @@
 // its 16-column blocks and stores the dequantized FP16 h.  G2 (down): 128 rows
 // x 256 output columns, K = I; wave w computes columns 64 w .. 64 w + 63.
 #include "common.hpp"
+#include "lds_ring.hpp"
 
 namespace moe {
 
@@ -97,7 +98,7 @@ struct Stage {
 // one array it cannot, and it made every read wait for all transfers in flight
 // (the two steps issued ahead included), which left the matrix cores waiting
 // out a memory round trip every step.  For the same reason the ring's barrier
-// is ring_barrier (common.hpp), not __syncthreads.
+// is ring_barrier (lds_ring.hpp), not __syncthreads.
 struct Ring {
   Stage& st0;
   Stage& st1;

@@ -21,6 +21,7 @@
 // Two experts whose router rows agree wherever x is nonzero get identical
 // logits in both passes, so the tie rule (lower id first) decides.
 #include "common.hpp"
+#include "lds_ring.hpp"
 #include "routing.hpp"
 
 namespace moe {
