@@ -94,6 +94,12 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
 // and group sums the running sum: depth 96 + 8 + H/256.  The terms' absolute
 // sum is at most (1 + 2^-7 + 2^-14) sum_h |x_h W_eh|; the radius takes unit
 // roundoff 2^-23 (any rounding of the MFMA's FP32 adds, not only to nearest).
+// The exact router's pass A takes only the first two pieces: the third is
+// below 2^-14 |w| for every weight, which adds 2^-14 sum_h |x_h W_eh| to the
+// radius (depth 64 + 8 + H/256 for the additions).  Only the candidates
+// depend on the radius; the selection and the weights come from the FP64
+// logits either way, and the radius stays far below the logits' spacing near
+// the k-th value, so there are hardly more candidates for a third less work.
 constexpr int RM_T = 256, RM_E = 128, RM_K = 32, RM_S = 3;  // tokens, experts, K step, ring stages
 
 // W [E][H] FP32 -> Wp [3][E][H] BF16 pieces (truncation; exact split)
@@ -141,12 +147,13 @@ typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 // one MFMA per wave, each A fragment four).  K order inside a step is
 // lane-contiguous (lanes 0..31 supply elements 8s.., lanes 32..63 16+8s.. in
 // MFMA s), the same for both operands.
-// NP: BF16 pieces per router row (3: the exact split; 1: a BF16 router).
+// NP: BF16 pieces per router row (3: the exact split; 2: its first two, the
+// exact router's pass A; 1: a BF16 router).
 template <int NP>
 __global__ __launch_bounds__(512) void k_router_logits_mfma(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ Wp, int T, int H, int E,
                                                             float* __restrict__ logits) {
-  static_assert(NP == 1 || NP == 3, "pieces");
+  static_assert(NP >= 1 && NP <= 3, "pieces");
   __shared__ __align__(16) RouterStage<NP> rs0, rs1, rs2;
   auto stage = [&](auto kc) -> RouterStage<NP>& {
     constexpr int k = decltype(kc)::value % RM_S;
@@ -900,11 +907,18 @@ hipError_t launch_route(const uint16_t* x, const float* W, int64_t T, int H, int
         hipLaunchKernelGGL(k_router_split, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, W, nw, wp);
         pieces = wp;
       }
-      hipLaunchKernelGGL(k_router_logits_mfma<3>, grid, dim3(512), 0, s, x, pieces, (int)T, H, E, lg);
-      // u = 2^-23 (twice the FP32 unit roundoff), and the pieces' 1 + 2^-7 + 2^-14
-      p.gamma = 2.0f * gamma_for_depth(3 * 2 * 16 + 8 + (H / RM_K + 7) / 8) * (1.0f + 0x1p-6f);
+      if (mode == MOE_ROUTER_SPLIT3_F32) {
+        hipLaunchKernelGGL(k_router_logits_mfma<3>, grid, dim3(512), 0, s, x, pieces, (int)T, H, E, lg);
+        p.mode = kSelF32;
+      } else {
+        hipLaunchKernelGGL(k_router_logits_mfma<2>, grid, dim3(512), 0, s, x, pieces, (int)T, H, E, lg);
+        // u = 2^-23 (twice the FP32 unit roundoff), the pieces' 1 + 2^-7, and
+        // the dropped third piece's 2^-14; all inflated by 2^-6
+        p.gamma = (2.0f * gamma_for_depth(2 * 2 * 16 + 8 + (H / RM_K + 7) / 8) * (1.0f + 0x1p-7f) + 0x1p-14f) *
+                  (1.0f + 0x1p-6f);
+        p.mode = kSelRefine;
+      }
       p.l32 = lg;
-      p.mode = mode == MOE_ROUTER_SPLIT3_F32 ? kSelF32 : kSelRefine;
     } else {
       const dim3 tgrid((unsigned)((E + RE - 1) / RE), (unsigned)((T + RT - 1) / RT));
       hipLaunchKernelGGL(k_router_logits_tiled, tgrid, dim3(256), 0, s, x, W, (int)T, H, E, lg);
