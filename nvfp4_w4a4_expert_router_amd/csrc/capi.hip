@@ -434,7 +434,9 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.T = (int)T;
   p.has_shared = L->has_shared;
   const int64_t P = T * L->k;
-  p.n_routed_slots = (int)(P < L->E ? P : L->E);
+  const bool fused_down = down_combine_decode_supported(L->H, L->I, L->k, L->has_shared);
+  p.pair_rows = fused_down ? 1 : 0;  // one routed slot per (token, rank)
+  p.n_routed_slots = (int)(fused_down || P < L->E ? P : L->E);
   p.off = expert_off;
   p.row2pair = row2pair;
   p.x = x;
@@ -465,7 +467,7 @@ int moe_layer_forward(const moe_layer* L, const uint16_t* x, int64_t T, const ui
   p.y_tok = reinterpret_cast<float*>(base + align_up((size_t)T * L->E * sizeof(double)) +
                                      align_up((size_t)T * L->k * sizeof(int4)));
   if ((rc = launch_rc(launch_gateup_decode(p, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr)))) return rc;
-  if (down_combine_decode_supported(L->H, L->I, L->k, L->has_shared)) {
+  if (fused_down) {
     // kernel 3 also combines: one workgroup per (token, 4 output columns)
     p.residual = residual;
     p.out = out;

@@ -592,6 +592,10 @@ struct FfnParams {
   float* y_shared;
   // decode kernels only: the shared expert takes one slot per token
   int shared_split;
+  // fused decode call with the down projection and combine in one kernel:
+  // routed slot s is pair s (token s / k, rank s % k) and h rows are indexed
+  // by pair id (in the workspace; y_rows keep the permuted order)
+  int pair_rows;
   // decode kernels: A4(x) codes [T][H/2] and scales [T][H/16]
   const uint8_t* xq;
   const uint8_t* xs;

@@ -189,6 +189,10 @@ constexpr int kGuCols = 32;  // intermediate columns per workgroup (gate and up 
 // all T tokens from the FP64 logits in LDS (route_select) and takes its slot's
 // entry from it; the grid's last workgroup also publishes the routing outputs
 // (ids, weights, permutation, slot table, shared gate) for the later kernels.
+// kPair (with kTable, when the down projection runs with the combine): routed
+// slot s is the pair s = t k + j (token t's j-th expert), so its workgroup
+// needs only token t's top k (no permutation of the batch), and writes its h
+// row at pair s; an expert chosen by several tokens is streamed once per token.
 constexpr int kJ = kGuCols / 2;  // weight rows per wave: kJ/2 gate, kJ/2 up
 struct GateUpLds {
   half_t xs[kDecMaxT * 2048];  // A4(x) dequantized without g, [T][H]
@@ -201,8 +205,9 @@ union DecodeLds {
   GateUpLds gu;      // from the weight burst on
 };
 
-template <bool kTable, bool kA8>
+template <bool kTable, bool kA8, bool kPair>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_gateup_decode(FfnParams p) {
+  static_assert(kTable || !kPair, "pair slots belong to the fused call");
   __shared__ __align__(16) DecodeLds lds;
   half_t* const xs = lds.gu.xs;
   auto& sct = lds.gu.sct;
@@ -237,7 +242,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     xs2 = *reinterpret_cast<const uint16_t*>(p.xs + (size_t)xt * (H / 16) + xc * 2);
   }
-  if (kTable && !shared) {
+  if (kTable && kPair && !shared) {
+    // wave 0 takes token t's top k (wave_topk512's order: logit descending,
+    // equal logits by id) and publishes its j-th expert
+    const int t = slot / p.k, j = slot % p.k;
+    if (w == 0) {
+      double v[8];
+      int id[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int ee = l + kWave * q;
+        const bool ok = ee < p.E;
+        v[q] = ok ? p.rq.logits[(int64_t)t * p.E + ee] : -INFINITY;
+        id[q] = ok ? ee : 0x7FFFFFFF;
+      }
+      double my_v = 0.0;
+      int my_e = 0;
+      wave_topk512(v, id, p.k, lds.route.ts[0], &my_v, &my_e);
+      if (l == 0) lds.route.wsum[0] = __builtin_amdgcn_readlane(my_e, j);
+    }
+    __syncthreads();
+    ent = make_int4(lds.route.wsum[0], slot, 1, t);
+    __syncthreads();  // the routing's LDS is reused from here on
+  } else if (kTable && !shared) {
     const RouteSel rs = route_select<false>(p.rq, lds.route);
     ent = slot < rs.n_slots ? lds.route.slot[slot] : make_int4(-1, 0, 0, 0);
     __syncthreads();  // the routing's LDS is reused from here on
@@ -294,7 +321,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     else
       decode32_fp16(xq4, xs2, xs + (size_t)xt * H + xc * 32);
   }
-  if (tid < nrows) toks[tid] = shared ? row0 + tid : kTable ? (int)(((unsigned)ent.w >> (8 * tid)) & 0xFFu) : tok;
+  if (tid < nrows)
+    toks[tid] = shared ? row0 + tid : kPair ? ent.w : kTable ? (int)(((unsigned)ent.w >> (8 * tid)) & 0xFFu) : tok;
   // the scale transfers are complete once at most the kJ code loads are in flight
   static_assert(kJ == 16, "vmcnt immediate below");
   __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16, expcnt 7, lgkmcnt 15
@@ -508,7 +536,7 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
   __shared__ float wsh[256 / kLPR];
   // 1. the pair's routing (written by the routing's publishing workgroup)
   int e = 0;
-  int64_t hrow = 0;
+  int64_t hrow = 0, yrow = 0;  // the h row read, the y_rows row written
   float wj = 0.0f, gate = 1.0f;
   if (live) {
     if (shared) {
@@ -516,7 +544,8 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
       if (p.sh_gate) gate = p.sh_gate[t];
     } else {
       e = p.rq.idx[t * k + j];
-      hrow = p.rq.p2r[t * k + j];
+      yrow = p.rq.p2r[t * k + j];
+      hrow = p.pair_rows ? (int64_t)t * k + j : yrow;
       wj = p.rq.w[t * k + j];
     }
   }
@@ -580,7 +609,7 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
       if (shared)
         p.y_shared[(int64_t)t * H + n0 + r] = y;
       else
-        p.y_rows[hrow * H + n0 + r] = y;
+        p.y_rows[yrow * H + n0 + r] = y;
       ycomb[j][r] = y;
     }
   }
@@ -633,11 +662,15 @@ hipError_t launch_gateup_decode(const FfnParams& p, hipStream_t s, hipEvent_t ev
   // the fused call's grid has one more workgroup: it publishes the routing
   const dim3 grid((unsigned)(slots * (p.I / kGuCols) + (p.slot_tab ? 1 : 0)));
   if (p.act8) {
-    if (p.slot_tab) return launch_timed(k_gateup_decode<true, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
-    return launch_timed(k_gateup_decode<false, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+    if (p.slot_tab && p.pair_rows)
+      return launch_timed(k_gateup_decode<true, true, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+    if (p.slot_tab) return launch_timed(k_gateup_decode<true, true, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+    return launch_timed(k_gateup_decode<false, true, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
   }
-  if (p.slot_tab) return launch_timed(k_gateup_decode<true, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
-  return launch_timed(k_gateup_decode<false, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  if (p.slot_tab && p.pair_rows)
+    return launch_timed(k_gateup_decode<true, false, true>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  if (p.slot_tab) return launch_timed(k_gateup_decode<true, false, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
+  return launch_timed(k_gateup_decode<false, false, false>, grid, dim3(256), 0, s, ev_before, ev_after, p);
 }
 
 bool fused_decode_supported(int H, int I, int E, int k, int64_t T) {
