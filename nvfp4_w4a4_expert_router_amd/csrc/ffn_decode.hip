@@ -28,6 +28,15 @@ bool ffn_stream_supported(int H, int I);
 
 namespace {
 
+// A pointer that is the same in every lane, held as a scalar value, in the
+// global address space (so that loads through it are global, not flat, loads).
+template <typename P>
+__device__ __forceinline__ const __attribute__((address_space(1))) P* uniform_ptr(const P* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const __attribute__((address_space(1))) P*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float dot8(uint32_t w, half8_t a, float c) {
   c = __builtin_amdgcn_fdot2(fp4x2<0>(w), half2_t{a[0], a[1]}, c, false);
   c = __builtin_amdgcn_fdot2(fp4x2<1>(w), half2_t{a[2], a[3]}, c, false);
@@ -534,51 +543,70 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
   __shared__ __align__(16) uint8_t sct[256 / kLPR][kDcCols * kSrow];
   __shared__ float ycomb[256 / kLPR][kDcCols];
   __shared__ float wsh[256 / kLPR];
-  // 1. the pair's routing (written by the routing's publishing workgroup)
-  int e = 0;
-  int64_t hrow = 0, yrow = 0;  // the h row read, the y_rows row written
-  float wj = 0.0f, gate = 1.0f;
-  if (live) {
-    if (shared) {
-      hrow = (int64_t)T * k + t;
-      if (p.sh_gate) gate = p.sh_gate[t];
-    } else {
-      e = p.rq.idx[t * k + j];
-      yrow = p.rq.p2r[t * k + j];
-      hrow = p.pair_rows ? (int64_t)t * k + j : yrow;
-      wj = p.rq.w[t * k + j];
-    }
+  // 1. the loads that need no other load, issued together by every lane (at
+  // in-range addresses, so that no branch leaves the wait counts uncertain):
+  // the pair's expert, permuted row and router weight (written by the
+  // routing's publishing workgroup) and the h chunk when its row is known
+  // (the shared row; a routed row with pair rows)
+  const int pid = t * k + j;
+  const bool routed = live && !shared;
+  const int pq = routed ? pid : 0;
+  const int e_ld = p.rq.idx[pq], y_ld = p.rq.p2r[pq];
+  const float w_ld = p.rq.w[pq];
+  const bool h_early = live && (shared || p.pair_rows);
+  half8_t a[4];
+  {
+    const int64_t hrow = shared ? (int64_t)T * k + t : h_early ? (int64_t)pid : 0;
+    const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + hrow * I + 32 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = src[i];
   }
-  const uint8_t* bcodes = shared ? p.sh2.codes : p.w2.codes;
-  const uint8_t* bscales = shared ? p.sh2.scales : p.w2.scales;
-  const float* bg = shared ? p.sh2.gscale : p.w2.gscale;
-  const int64_t row0 = (int64_t)e * H + n0;
-  // 2. loads in the order they are consumed: the rows' block scales (one
-  // 16-byte piece per lane), the h chunk, the gscale, then the code burst
+  __builtin_amdgcn_sched_barrier(0);
+  const int e = routed ? e_ld : 0, yrow = routed ? y_ld : 0;
+  const float wj = routed ? w_ld : 0.0f;
+  // the banks' pointers as wave-uniform values first, then chosen per lane
+  // group (selecting between the two structs would fetch the chosen one's
+  // fields with vector loads from the argument segment)
+  typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
+  typedef const __attribute__((address_space(1))) u32x4* gu32x4_t;
+  const gbytes_t bcodes = shared ? uniform_ptr(p.sh2.codes) : uniform_ptr(p.w2.codes);
+  const gbytes_t bscales = shared ? uniform_ptr(p.sh2.scales) : uniform_ptr(p.w2.scales);
+  const __attribute__((address_space(1))) float* bg = shared ? uniform_ptr(p.sh2.gscale) : uniform_ptr(p.w2.gscale);
+  // (ids are non-negative: zero extension, so nothing waits for the loaded id
+  // before the loads that do not need it are issued)
+  const int64_t row0 = (int64_t)((uint64_t)(uint32_t)e * (uint32_t)H) + n0;
+  // 2. the loads that need the expert, in the order they are consumed: the
+  // rows' block scales (one 16-byte piece per lane), the h chunk (permuted
+  // rows), the gscale, then the code burst
   constexpr int kSPL = (kSPieces + kLPR - 1) / kLPR;  // pieces per lane
   uint4 scv[kSPL];
 #pragma unroll
   for (int i = 0; i < kSPL; ++i) scv[i] = make_uint4(0u, 0u, 0u, 0u);
-  half8_t a[4];
   uint4 q[kDcCols];
   float gsc = 0.0f;
   if (live) {
 #pragma unroll
     for (int i = 0; i < kSPL; ++i)
-      if (c + kLPR * i < kSPieces) scv[i] = *reinterpret_cast<const uint4*>(bscales + row0 * kSrow + 16 * (c + kLPR * i));
-    const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + hrow * I + 32 * c);
+      if (c + kLPR * i < kSPieces) {
+        const u32x4 v = *reinterpret_cast<gu32x4_t>(bscales + row0 * kSrow + 16 * (c + kLPR * i));
+        scv[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    if (!h_early) {
+      const half8_t* src = reinterpret_cast<const half8_t*>(p.hh + (int64_t)yrow * I + 32 * c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = src[i];
-    gsc = bg[e];
+      for (int i = 0; i < 4; ++i) a[i] = src[i];
+    }
+    gsc = bg[(uint32_t)e];
 #pragma unroll
-    for (int r = 0; r < kDcCols; ++r)
-      q[r] = load16_nt(bcodes + (row0 + r) * (I / 2) + 16 * c);
+    for (int r = 0; r < kDcCols; ++r) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(bcodes + (row0 + r) * (I / 2) + 16 * c));
+      q[r] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = half8_t{};
 #pragma unroll
     for (int r = 0; r < kDcCols; ++r) q[r] = make_uint4(0u, 0u, 0u, 0u);
   }
+  const float gate = shared && p.sh_gate ? p.sh_gate[t] : 1.0f;  // used at the end only
   if (j < 256 / kLPR) {
 #pragma unroll
     for (int i = 0; i < kSPL; ++i)
@@ -609,7 +637,7 @@ __global__ __launch_bounds__(256) void k_down_combine_decode(FfnParams p) {
       if (shared)
         p.y_shared[(int64_t)t * H + n0 + r] = y;
       else
-        p.y_rows[yrow * H + n0 + r] = y;
+        p.y_rows[(int64_t)yrow * H + n0 + r] = y;
       ycomb[j][r] = y;
     }
   }
