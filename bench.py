@@ -357,7 +357,7 @@ def main():
             rec["config"]["launch"] = "eager (one host launch per kernel)"
         rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                           "kernel": "k_gateup_decode<true, false>", "algorithmic_bytes_per_launch": round(d["gateup_bytes"]),
+                           "kernel": "k_gateup_decode<true, false, true>", "algorithmic_bytes_per_launch": round(d["gateup_bytes"]),
                            "avg_duration_us": round(d["t_gateup"] * 1e3, 3),
                            "frac_of_copy_bandwidth": round(achieved / copy_gbs, 4)}
 

@@ -100,6 +100,63 @@ __device__ __forceinline__ float pair_sum(float x, float y, bool upper) {
   }
 }
 
+// max(own, lane l ^ m) of a 64-bit value: DPP within a row for m <= 8; for
+// m = 16 and 32 one permlane swap of (v, v) leaves the lane's own value in one
+// result and its partner's in the other, so the max of the two is the same.
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int m>
+__device__ __forceinline__ uint64_t max_with_partner(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  if constexpr (m <= 8) {
+    const uint32_t plo = (uint32_t)__float_as_int(xor_lane<m>(__int_as_float((int)lo)));
+    const uint32_t phi = (uint32_t)__float_as_int(xor_lane<m>(__int_as_float((int)hi)));
+    return umax64(v, ((uint64_t)phi << 32) | plo);
+  } else {
+    static_assert(m == 16 || m == 32, "partner distance");
+    const auto pl = m == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                            : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto ph = m == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                            : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    return umax64(((uint64_t)ph[0] << 32) | pl[0], ((uint64_t)ph[1] << 32) | pl[1]);
+  }
+}
+
+// The expert holding the j-th largest (0-based) of the wave's 512 selection
+// keys (lane l holds experts l + 64 q in key[q]; keys are distinct, since each
+// carries its expert id, so the j-th is the j-th of the top-k order: logit
+// descending, equal logits by lower id).  Registers only: each lane sorts its 8
+// keys (a 19-comparator network), then j + 1 rounds take the wave maximum of
+// the lanes' leading keys (butterfly over the 64 lanes) and the lane that held
+// it drops it.  Every lane returns the same id.
+__device__ __forceinline__ int wave_jth_expert(uint64_t (&key)[8], int j) {
+  auto ce = [&](int a, int b) {
+    const uint64_t x = key[a], y = key[b];
+    key[a] = umax64(x, y);
+    key[b] = x > y ? y : x;
+  };
+  ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+  ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+  ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+  ce(2, 4); ce(3, 5);
+  ce(1, 4); ce(3, 6);
+  ce(1, 2); ce(3, 4); ce(5, 6);
+  for (int r = 0;; ++r) {
+    uint64_t m = key[0];
+    m = max_with_partner<1>(m);
+    m = max_with_partner<2>(m);
+    m = max_with_partner<4>(m);
+    m = max_with_partner<8>(m);
+    m = max_with_partner<16>(m);
+    m = max_with_partner<32>(m);
+    if (r == j) return 1023 - (int)(__builtin_amdgcn_readfirstlane((uint32_t)m) & 0x3FFu);
+    if (key[0] == m) {  // one lane: keys are distinct
+#pragma unroll
+      for (int q = 0; q < 7; ++q) key[q] = key[q + 1];
+      key[7] = 0;  // below every key of a finite or infinite logit
+    }
+  }
+}
+
 // Sum v[0..15] over aligned groups of kG lanes by recursive halving (all steps
 // resolved at compile time; each step adds a lane's kept value and its
 // partner's, so the sums do not depend on how the values move).  Afterwards
@@ -252,27 +309,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     xs2 = *reinterpret_cast<const uint16_t*>(p.xs + (size_t)xt * (H / 16) + xc * 2);
   }
   if (kTable && kPair && !shared) {
-    // wave 0 takes token t's top k (wave_topk512's order: logit descending,
-    // equal logits by id) and publishes its j-th expert
+    // every wave finds token t's j-th expert by itself (registers only, so no
+    // LDS hand-off or barrier): the order of the routing's top k
     const int t = slot / p.k, j = slot % p.k;
-    if (w == 0) {
-      double v[8];
-      int id[8];
+    uint64_t key[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int ee = l + kWave * q;
-        const bool ok = ee < p.E;
-        v[q] = ok ? p.rq.logits[(int64_t)t * p.E + ee] : -INFINITY;
-        id[q] = ok ? ee : 0x7FFFFFFF;
-      }
-      double my_v = 0.0;
-      int my_e = 0;
-      wave_topk512(v, id, p.k, lds.route.ts[0], &my_v, &my_e);
-      if (l == 0) lds.route.wsum[0] = __builtin_amdgcn_readlane(my_e, j);
+    for (int q = 0; q < 8; ++q) {
+      const int ee = l + kWave * q;
+      const bool ok = ee < p.E;
+      key[q] = rank_key(ok ? p.rq.logits[(int64_t)t * p.E + ee] : -INFINITY, ok ? ee : 0x7FFFFFFF);
     }
-    __syncthreads();
-    ent = make_int4(lds.route.wsum[0], slot, 1, t);
-    __syncthreads();  // the routing's LDS is reused from here on
+    ent = make_int4(wave_jth_expert(key, j), slot, 1, t);
   } else if (kTable && !shared) {
     const RouteSel rs = route_select<false>(p.rq, lds.route);
     ent = slot < rs.n_slots ? lds.route.slot[slot] : make_int4(-1, 0, 0, 0);
