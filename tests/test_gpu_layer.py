@@ -270,6 +270,67 @@ def test_layer_forward_matches_separate_calls(cfg, T):
     gh.log("  ", rep.line())
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_fused_decode_exact_ties(T):
+    """Router rows duplicated so that exactly equal FP64 logits sit inside every
+    token's top k (the experts at ranks 0 and 3 get a twin) and at its boundary
+    (the expert at rank k - 3 and its twin end up at ranks k - 1 and k).
+    In the fused decode call every routed gate/up workgroup finds its (token,
+    rank) pair's expert by itself; it must take the lower id first, exactly as
+    the publishing workgroup and the separate calls do, and match the oracle."""
+    import copy
+    cfg = 1
+    L, _ = layer_for(cfg)
+    sh = L.shape
+    x = gen.make_tokens(cfg, T, step=41)
+    res = gen.make_tokens(cfg, T, step=42)
+    gh.log("case: fused decode exact ties T=%d" % T)
+    lg = oracle.router_logits(x, L.router_w)
+    order = np.argsort(-lg, axis=1, kind="stable")
+    busy = set(order[:, :sh.k + 6].reshape(-1).tolist())
+    spare = [e for e in range(sh.E) if e not in busy]
+    rng = np.random.default_rng(7)
+    wr = L.router_w.copy()
+    twins = []
+    for t in range(T):
+        for r in (0, 3, sh.k - 3):
+            a = int(order[t, r])
+            if any(a in tw for tw in twins):
+                continue
+            b = spare.pop(int(rng.integers(len(spare))))
+            wr[b] = wr[a]
+            twins.append((a, b))
+    DLt = gh.device_layer(L, router_w=wr)
+    ref = gh.run_layer(DLt, x, residual=res, dump=())
+    buf = moe.Buffers(DLt, T, gh.DEV)
+    moe.moe_layer_forward(DLt, gh.to_dev(x.view(np.int16)), buf, residual=gh.to_dev(res.view(np.int16)))
+    torch.cuda.synchronize()
+    got = {"idx": buf.topk_idx, "w": buf.topk_w, "off": buf.expert_off, "r2p": buf.row2pair, "p2r": buf.pair2row,
+           "y_rows": buf.y_rows, "y_shared": buf.y_shared, "out": buf.out}
+    for key, tns in got.items():
+        a_ = tns.cpu().numpy()
+        if key == "out":
+            a_ = a_.view(np.uint16)
+        assert np.array_equal(a_, ref[key]), key
+    lg2 = oracle.router_logits(x, wr)
+    n_inside = n_boundary = 0
+    for t in range(T):
+        sel = ref["idx"][t].tolist()
+        for a, b in twins:
+            assert lg2[t, a] == lg2[t, b]
+            lo, hi = min(a, b), max(a, b)
+            if hi in sel:
+                assert lo in sel and sel.index(lo) == sel.index(hi) - 1, (t, a, b, sel)
+                n_inside += 1
+            elif lo in sel:
+                n_boundary += sel.index(lo) == sh.k - 1
+    assert n_inside >= 2 * T and n_boundary >= T, (n_inside, n_boundary)
+    Lt = copy.copy(L)
+    Lt.router_w = wr
+    rep = gh.check_layer(Lt, x, dict(ref, **gh.run_layer(DLt, x, residual=res)), residual=res)
+    gh.log("  ", rep.line(), "tied pairs inside the top k:", n_inside, "at the boundary:", n_boundary)
+
+
 @pytest.mark.parametrize("cfg,T", [(1, 4), (0, 3)])
 def test_fused_path_repeated_calls(cfg, T):
     """Several fused calls on one workspace and one set of outputs: every call
