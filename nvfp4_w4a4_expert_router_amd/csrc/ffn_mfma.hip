@@ -151,66 +151,75 @@ __device__ __forceinline__ int tile_blocks(int live_rows) {
   return live_rows >= kBM ? 4 : live_rows <= 32 ? 1 : (live_rows + 31) / 32;
 }
 
+// The wave's transfers of one K step (element k0) into a ring stage: 4 A, 2 B
+// and 1 scale transfers.  real = false: the same transfers through resources
+// of no bytes, which read nothing and write zeros into the stage (used where
+// no later step reads it).  Issuing them keeps every step's transfers
+// unconditional: around a conditional transfer the compiler cannot tell which
+// stage is in flight and makes the next reads wait for all of them.
+__device__ __forceinline__ void dma_step(const Operands& O, bool real, uint32_t k0, Stage& S) {
+  const int wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t ra = real ? O.a : O.a0, rq = real ? O.bq : O.bq0, rs = real ? O.bs : O.bs0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
+                                             0);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr_t)&S.b[(64 * wave + 32 * c) * 2], 16, O.bdma[c],
+                                             k0 / 2 * O.bmul, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&S.s[64 * wave], 4, O.sdma, k0 / 16 * O.bmul, 0, 0);
+}
+
+// The MFMAs of one K step from a ring stage (layout: see tile_mma).
+template <bool kTransposed, int kRB, typename BRow>
+__device__ __forceinline__ void mma_step(Stage& S, BRow bj, floatx16 (&acc)[4][2]) {
+  const int lane = lane_id();
+  const int hk = lane >> 5;
+  uint4 bq[2];
+  half2_t sv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = bj(j) + (lane & 31);
+    bq[j] = S.b[r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
+    sv[j] = ue4m3x2_to_half2(S.s[r] >> (16 * hk));
+  }
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    half8_t a[4];
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const int row = 32 * i + (lane & 31);
+      a[i] = __builtin_bit_cast(half8_t, S.a[row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const half2_t S2 = half2_t{sv[j][s4 >> 1], sv[j][s4 >> 1]};
+      const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
+      const half2_t c0 = fp4x2<0>(w) * S2, c1 = fp4x2<1>(w) * S2, c2 = fp4x2<2>(w) * S2, c3 = fp4x2<3>(w) * S2;
+      const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {  // rows past live_rows in a block are computed, never stored
+        if (kTransposed)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <bool kTransposed, int kRB, typename BRow>
 __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, int live_rows, Ring& ring, BRow bj,
                                          floatx16 (&acc)[4][2]) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
   const int n = K / kBK;
-  const int hk = lane >> 5;
   const int nlive = __builtin_amdgcn_readfirstlane(live_rows > 0 ? 1 : 0);
   auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };  // n = 1: the prologue repeats step 0
-  // step t into ring stage `stage`: 4 A, 2 B and 1 scale transfers per wave
-  // real = false (the last two steps): the same transfers through resources of
-  // no bytes, which read nothing and write zeros into the stage no later step
-  // reads.  Issuing them keeps every step's transfers unconditional: around a
-  // conditional transfer the compiler cannot tell which stage is in flight and
-  // makes the next reads wait for all of them.
-  auto dma = [&](int t, Stage& S, bool real) {
-    const uint32_t k0 = kof(t);
-    const __amdgpu_buffer_rsrc_t ra = real ? O.a : O.a0, rq = real ? O.bq : O.bq0, rs = real ? O.bs : O.bs0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
-                                               0);
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr_t)&S.b[(64 * wave + 32 * c) * 2], 16, O.bdma[c],
-                                               k0 / 2 * O.bmul, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&S.s[64 * wave], 4, O.sdma, k0 / 16 * O.bmul, 0, 0);
-  };
+  // step t into ring stage `stage` (real = false for the last two steps' transfers)
+  auto dma = [&](int t, Stage& S, bool real) { dma_step(O, real, kof(t), S); };
   auto compute = [&](Stage& S) {
     if (nlive == 0) return;
-    uint4 bq[2];
-    half2_t sv[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = bj(j) + (lane & 31);
-      bq[j] = S.b[r * 2 + (hk ^ (((r >> 2) ^ (r >> 3)) & 1))];
-      sv[j] = ue4m3x2_to_half2(S.s[r] >> (16 * hk));
-    }
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      half8_t a[4];
-#pragma unroll
-      for (int i = 0; i < kRB; ++i) {
-        const int row = 32 * i + (lane & 31);
-        a[i] = __builtin_bit_cast(half8_t, S.a[row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const half2_t S = half2_t{sv[j][s4 >> 1], sv[j][s4 >> 1]};
-        const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
-        const half2_t c0 = fp4x2<0>(w) * S, c1 = fp4x2<1>(w) * S, c2 = fp4x2<2>(w) * S, c3 = fp4x2<3>(w) * S;
-        const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-#pragma unroll
-        for (int i = 0; i < kRB; ++i) {  // rows past live_rows in a block are computed, never stored
-          if (kTransposed)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
-        }
-      }
-    }
+    mma_step<kTransposed, kRB>(S, bj, acc);
   };
 
   // vmcnt(7): the wave's 7 newest transfers (the step issued last) may still be
@@ -237,6 +246,50 @@ __device__ __forceinline__ void tile_mma(const Operands& O, int k_begin, int K, 
     if (decltype(pc)::value < rem) phase(pc, t + decltype(pc)::value);
   });
   __builtin_amdgcn_s_waitcnt(0);  // no transfer into LDS outlives the loop
+}
+
+// field-wise choice between two operand sets (values, so that both stay in
+// registers)
+__device__ __forceinline__ Operands pick(bool c, const Operands& A, const Operands& B) {
+  Operands R;
+  R.a = c ? A.a : B.a;
+  R.bq = c ? A.bq : B.bq;
+  R.bs = c ? A.bs : B.bs;
+  R.a0 = A.a0;
+  R.bq0 = A.bq0;
+  R.bs0 = A.bs0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) R.adma[i] = c ? A.adma[i] : B.adma[i];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) R.bdma[i] = c ? A.bdma[i] : B.bdma[i];
+  R.sdma = c ? A.sdma : B.sdma;
+  R.bmul = c ? A.bmul : B.bmul;
+  return R;
+}
+
+// The K loop of one tile in a workgroup that runs several tiles with one ring:
+// the tile's first two steps are already in flight (issued by the previous
+// tile's last two steps, or by the workgroup's prologue), and its last two
+// steps issue the next tile's first two from On (whose resources hold no bytes
+// when there is no next tile).  kPh: the ring stage of step 0; kNm3 = n % 3,
+// n >= 2 steps from k_begin (the same K range for every tile).  No wait at the
+// end: the next tile's transfers stay in flight through this tile's epilogue.
+template <bool kTransposed, int kRB, int kPh, int kNm3, typename BRow>
+__device__ __forceinline__ void tile_mma_chain(const Operands& O, const Operands& On, int k_begin, int n, Ring& ring,
+                                               BRow bj, floatx16 (&acc)[4][2]) {
+  auto phase = [&](auto pc, int t) {
+    constexpr int P = kPh + decltype(pc)::value;  // stage of step t: (kPh + t) % 3
+    const bool own = t + 2 < n;
+    const uint32_t k0 = (uint32_t)(k_begin + (own ? t + 2 : t + 2 - n) * kBK);
+    dma_step(pick(own, O, On), true, k0, ring.at<P + 2>());
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<kTransposed, kRB>(ring.at<P>(), bj, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier<7>();
+  };
+  int t = 0;
+  for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
+  static_for<0, kNm3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
 }
 
 // ---------------------------------------------------------------- G1
@@ -419,18 +472,21 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
 // ---------------------------------------------------------------- G2
 // Tile: 128 rows x 256 output columns; wave w holds columns nt*256 + 64 w ..
 // + 63 of all 128 rows as blocks j = 0, 1.
-__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
-                                                      const int4* __restrict__ tile_tab) {
-  __shared__ __align__(16) Stage st0, st1, st2;
-  Ring ring{st0, st1, st2};
+struct DownTile {
+  Operands O;
+  float* y;    // the tile's first output row (y_rows in permuted order, or y_shared)
+  int nrows;   // rows of the segment in the tile (1..128)
+  int m0;      // the tile's first row in its segment
+  int nt;      // column tile
+  bool shared;
+};
+
+__device__ __forceinline__ int down_bj(int j) { return 64 * (int)(threadIdx.x >> 6) + 32 * j; }
+
+// Operands and output rows of the work item (row tile te = its tile table
+// entry, column tile nt)
+__device__ __forceinline__ DownTile down_tile(const FfnParams& p, int4 te, int nt) {
   const int H = p.H, I = p.I, T = p.T, E = p.E;
-  const int n_nt = H / kBN;
-  const int nseg = E + 1;
-  const int n_tiles = tile_start[nseg] * n_nt;
-  if ((int)blockIdx.x >= n_tiles) return;
-  const int lt = xcd_tile((int)blockIdx.x, n_tiles);
-  const int mt = lt / n_nt, nt = lt % n_nt;
-  const int4 te = tile_tab[mt];
   const int seg = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
   const int seg_row0 = __builtin_amdgcn_readfirstlane(te.z), seg_rows = __builtin_amdgcn_readfirstlane(te.w);
   const bool shared = seg == E;
@@ -440,49 +496,54 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   const uint8_t* codes = bank.codes + erow * (I / 2);
   const uint8_t* scales = bank.scales + erow * (I / 16);
   const uint32_t qrow = km ? 32u : (uint32_t)(I / 2), srow = km ? 4u : (uint32_t)(I / 16);
-  const float G = (shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  auto bj = [&](int j) { return 64 * wave + 32 * j; };
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  DownTile d;
   // A rows: the tile's rows of hh; rows past the segment read zeros (range check)
   const int64_t row0 = (shared ? (int64_t)T * p.k : (int64_t)seg_row0) + m0;
-  const int nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
-  Operands O;
-  O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)nrows * I * 2u);
-  O.a0 = buffer_rsrc(p.hh + row0 * I, 0u);
+  d.nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
+  d.O.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)d.nrows * I * 2u);
+  d.O.a0 = buffer_rsrc(p.hh + row0 * I, 0u);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u +
-                (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
-  O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
-  O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
-  O.bq0 = buffer_rsrc(codes, 0u);
-  O.bs0 = buffer_rsrc(scales, 0u);
+    d.O.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u +
+                  (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
+  d.O.bq = buffer_rsrc(codes, (uint32_t)H * (I / 2));
+  d.O.bs = buffer_rsrc(scales, (uint32_t)H * (I / 16));
+  d.O.bq0 = buffer_rsrc(codes, 0u);
+  d.O.bs0 = buffer_rsrc(scales, 0u);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = (uint32_t)(nt * kBN + r) * qrow + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
+    d.O.bdma[c] = (uint32_t)(nt * kBN + r) * qrow + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
   }
-  O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * srow;
-  O.bmul = km ? (uint32_t)H : 1u;
-  floatx16 acc[4][2] = {};
-  // K range [kc0, kc1) of I (the full sum: 0, I)
-  switch (tile_blocks(nrows)) {
-    case 1: tile_mma<false, 1>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
-    case 2: tile_mma<false, 2>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
-    case 3: tile_mma<false, 3>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
-    default: tile_mma<false, 4>(O, p.kc0, p.kc1 - p.kc0, nrows, ring, bj, acc); break;
-  }
-  // output rows of the tile through a resource sized to the segment's rows in it
-  // (non-temporal: the combine reads them after every tile is done)
-  float* ybase = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
-  const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(ybase, (uint32_t)nrows * H * 4u);
+  d.O.sdma = (uint32_t)(nt * kBN + 64 * wave + lane) * srow;
+  d.O.bmul = km ? (uint32_t)H : 1u;
+  d.y = shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
+  d.m0 = m0;
+  d.nt = nt;
+  d.shared = shared;
+  return d;
+}
+
+// The tile's output rows through a resource sized to the segment's rows in it
+// (non-temporal: the combine reads them after every tile is done).  G: the
+// expert's FP32 scale times the activation scale.
+__device__ __forceinline__ void down_store(const FfnParams& p, const DownTile& d, float G,
+                                           const floatx16 (&acc)[4][2]) {
+  // H through an empty asm statement: in a loop over tiles the compiler
+  // would otherwise compute the 128 store offsets of every lane once, before
+  // the loop, and keep them in registers it does not have
+  int H = p.H;
+  asm volatile("" : "+s"(H));
+  const int T = p.T, lane = lane_id();
+  const __amdgpu_buffer_rsrc_t y_r = buffer_rsrc(d.y, (uint32_t)d.nrows * H * 4u);
   const uint32_t voff0 = (uint32_t)(4 * (lane >> 5) * H) * 4u;
-  if (shared && p.sh_gate) {
+  if (d.shared && p.sh_gate) {
     // shared rows are tokens m0 + row: each scaled by its gate, the tile's 128
     // gates staged in LDS once (rows past the segment read the last token's and
     // are dropped by the store's range check)
     __shared__ float gsh[128];
-    if (threadIdx.x < 128) gsh[threadIdx.x] = p.sh_gate[m0 + (int)threadIdx.x < T ? m0 + (int)threadIdx.x : T - 1];
+    if (threadIdx.x < 128) gsh[threadIdx.x] = p.sh_gate[d.m0 + (int)threadIdx.x < T ? d.m0 + (int)threadIdx.x : T - 1];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -492,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
         const float gr = gsh[dm];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = nt * kBN + bj(j) + (lane & 31);
+          const int n = d.nt * kBN + down_bj(j) + (lane & 31);
           buffer_store4_nt(__float_as_uint((G * acc[i][j][q]) * gr), y_r,
                            voff0 + (uint32_t)((dm - 4 * (lane >> 5)) * H * 4) + (uint32_t)(n * 4));
         }
@@ -503,13 +564,194 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = nt * kBN + bj(j) + (lane & 31);
+      const int n = d.nt * kBN + down_bj(j) + (lane & 31);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int dm = 32 * i + 8 * (q >> 2) + (q & 3);
         buffer_store4_nt(__float_as_uint(G * acc[i][j][q]), y_r, voff0 + (uint32_t)(dm * H * 4) + (uint32_t)(n * 4));
       }
     }
+}
+
+// One work item per workgroup (the K ranges of one step: a K-split partial).
+__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                      const int4* __restrict__ tile_tab) {
+  __shared__ __align__(16) Stage st0, st1, st2;
+  Ring ring{st0, st1, st2};
+  const int n_nt = p.H / kBN;
+  const int n_tiles = tile_start[p.E + 1] * n_nt;
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int lt = xcd_tile((int)blockIdx.x, n_tiles);
+  const int4 te = tile_tab[lt / n_nt];
+  const DownTile d = down_tile(p, te, lt % n_nt);
+  const int seg = __builtin_amdgcn_readfirstlane(te.x);
+  const float G = (d.shared ? p.sh2.gscale[0] : p.w2.gscale[seg]) * p.g_mid;
+  floatx16 acc[4][2] = {};
+  // K range [kc0, kc1) of I (the full sum: 0, I)
+  switch (tile_blocks(d.nrows)) {
+    case 1: tile_mma<false, 1>(d.O, p.kc0, p.kc1 - p.kc0, d.nrows, ring, down_bj, acc); break;
+    case 2: tile_mma<false, 2>(d.O, p.kc0, p.kc1 - p.kc0, d.nrows, ring, down_bj, acc); break;
+    case 3: tile_mma<false, 3>(d.O, p.kc0, p.kc1 - p.kc0, d.nrows, ring, down_bj, acc); break;
+    default: tile_mma<false, 4>(d.O, p.kc0, p.kc1 - p.kc0, d.nrows, ring, down_bj, acc); break;
+  }
+  down_store(p, d, G, acc);
+}
+
+// The same work items with a grid of two workgroups per CU (K ranges of at
+// least two steps, routed and shared banks in the same layout).  XCD x
+// (= blockIdx % 8) takes the same contiguous run of work items as in
+// k_down_mfma, and its gx workgroups take every gx-th item of it, so the items
+// in flight on an XCD stay neighbours (shared A rows and weights in its L2).
+// The LDS ring runs on from one item into the next: an item's last two steps
+// transfer the next item's first two, so the next item's first transfers and
+// set-up overlap this item's last MFMAs and its row stores instead of
+// following them.  The tile table entry and the expert scale of an item are
+// read an item ahead by vector loads (a scalar load in flight would make every
+// LDS read of the K loop wait for it: both count on one counter).  A lane's
+// transfer offsets are the same for every item (the column tile moves the B
+// resources' base), so an item adds only scalar state.  kNm3 = steps per item
+// mod 3: the ring stage of an item's first step advances by it from item to
+// item, so the item loop is unrolled three times and every stage index is a
+// compile-time value.
+struct ChainItem {
+  __amdgpu_buffer_rsrc_t a, bq, bs;  // A rows, the column tile's B codes and scales
+  float* y;                          // the item's first output row
+  int nrows, m0, nt;
+  bool shared;
+};
+
+template <int kNm3>
+__global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const int32_t* __restrict__ tile_start,
+                                                            const int4* __restrict__ tile_tab) {
+  __shared__ __align__(16) Stage st0, st1, st2;
+  Ring ring{st0, st1, st2};
+  const int H = p.H, I = p.I, E = p.E;
+  const int n_nt = H / kBN;
+  const int n_mt = tile_start[E + 1];
+  const int n_tiles = n_mt * n_nt;
+  const int x = (int)blockIdx.x & 7, gx = (int)gridDim.x >> 3;
+  const int q = n_tiles >> 3, r = n_tiles & 7;
+  const int run0 = x * q + (x < r ? x : r), end = run0 + q + (x < r ? 1 : 0);
+  int lt = run0 + ((int)blockIdx.x >> 3);
+  if (lt >= end) return;
+  const int n = (p.kc1 - p.kc0) / kBK;
+  const bool km = p.w2k.codes != nullptr;  // the shared bank's layout is the same
+  const uint8_t* const rq = km ? p.w2k.codes : p.w2.codes;
+  const uint8_t* const rs = km ? p.w2k.scales : p.w2.scales;
+  const uint8_t* const sq = km ? p.sh2k.codes : p.sh2.codes;
+  const uint8_t* const ss = km ? p.sh2k.scales : p.sh2.scales;
+  const uint32_t qrow = km ? 32u : (uint32_t)(I / 2), srow = km ? 4u : (uint32_t)(I / 16);
+  const uint32_t bmul = km ? (uint32_t)H : 1u;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  // the lane's transfer offsets (every item)
+  Operands L;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    L.adma[c] = (uint32_t)(32 * wave + 8 * c + (lane >> 3)) * I * 2u + (uint32_t)((lane & 7) ^ (lane >> 3) ^ (c & 1)) * 16u;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int rr = 64 * wave + 32 * c + (lane >> 1);
+    L.bdma[c] = (uint32_t)rr * qrow + (uint32_t)((lane & 1) ^ (((rr >> 2) ^ (rr >> 3)) & 1)) * 16u;
+  }
+  L.sdma = (uint32_t)(64 * wave + lane) * srow;
+  L.bmul = bmul;
+  const __amdgpu_buffer_rsrc_t null_r = buffer_rsrc(p.hh, 0u);
+  L.a0 = null_r;
+  L.bq0 = null_r;
+  L.bs0 = null_r;
+  const __amdgpu_buffer_rsrc_t tt_r = buffer_rsrc(tile_tab, (uint32_t)n_mt * 16u);
+  const __amdgpu_buffer_rsrc_t gw_r = buffer_rsrc(p.w2.gscale, (uint32_t)E * 4u);
+  const __amdgpu_buffer_rsrc_t gs_r = buffer_rsrc(p.sh2.gscale, 4u);
+  // item l's resources and output rows from its table entry te (uniform)
+  auto make_item = [&](int4 te, int l) {
+    const int seg = te.x, m0 = te.y, seg_row0 = te.z, seg_rows = te.w, nt = l % n_nt;
+    ChainItem it;
+    it.shared = seg == E;
+    it.m0 = m0;
+    it.nt = nt;
+    it.nrows = seg_rows - m0 < kBM ? seg_rows - m0 : kBM;
+    const int64_t row0 = (it.shared ? (int64_t)p.T * p.k : (int64_t)seg_row0) + m0;
+    it.a = buffer_rsrc(p.hh + row0 * I, (uint32_t)it.nrows * I * 2u);
+    const int64_t erow = it.shared ? 0 : (int64_t)seg * H;  // the expert's first row in the bank
+    const uint32_t cq = (uint32_t)(nt * kBN) * qrow, cs = (uint32_t)(nt * kBN) * srow;
+    it.bq = buffer_rsrc((it.shared ? sq : rq) + erow * (I / 2) + cq, (uint32_t)H * (I / 2) - cq);
+    it.bs = buffer_rsrc((it.shared ? ss : rs) + erow * (I / 16) + cs, (uint32_t)H * (I / 16) - cs);
+    it.y = it.shared ? p.y_shared + (int64_t)m0 * H : p.y_rows + (int64_t)(seg_row0 + m0) * H;
+    return it;
+  };
+  auto with = [&](const ChainItem& it) {
+    Operands O = L;
+    O.a = it.a;
+    O.bq = it.bq;
+    O.bs = it.bs;
+    return O;
+  };
+  // the table entry of item l (l < end) by a vector load; uniform() reads it
+  // out where it is used, so that no wait follows the load
+  auto entry = [&](int l) { return __builtin_amdgcn_raw_buffer_load_b128(tt_r, 0u, (uint32_t)(l / n_nt) * 16u, 0); };
+  auto uniform = [](u32x4 v) {
+    return make_int4(__builtin_amdgcn_readfirstlane((int)v.x), __builtin_amdgcn_readfirstlane((int)v.y),
+                     __builtin_amdgcn_readfirstlane((int)v.z), __builtin_amdgcn_readfirstlane((int)v.w));
+  };
+  // the FP32 scale of the segment of table entry te (uniform), by a vector load
+  auto gscale = [&](int4 te) {
+    const bool sh = te.x == E;
+    return __builtin_amdgcn_raw_buffer_load_b32(sh ? gs_r : gw_r, 0u, sh ? 0u : (uint32_t)te.x * 4u, 0);
+  };
+  const int4 te0 = uniform(entry(lt));
+  ChainItem cur = make_item(te0, lt);
+  float G = __uint_as_float(__builtin_amdgcn_readfirstlane(gscale(te0))) * p.g_mid;
+  int lt1 = lt + gx;
+  u32x4 te1 = entry(lt1 < end ? lt1 : lt);
+  dma_step(with(cur), true, (uint32_t)p.kc0, ring.at<0>());
+  dma_step(with(cur), true, (uint32_t)(p.kc0 + kBK), ring.at<1>());
+  ring_barrier<7>();
+  // one item at ring phase kPh; false when it was the workgroup's last
+  auto item = [&](auto ph) -> bool {
+    constexpr int kPh = decltype(ph)::value;
+    const bool has1 = lt1 < end;
+    const int lt2 = lt1 + gx;
+    const int4 t1 = uniform(te1);  // loaded an item ago
+    // loads for the next items, issued before this item's first transfers
+    // (its first barrier then covers them)
+    const u32x4 te2 = entry(lt2 < end ? lt2 : lt);
+    const uint32_t g1 = gscale(t1);
+    __builtin_amdgcn_sched_barrier(0);
+    ChainItem nxt = make_item(t1, lt1);
+    Operands On = with(nxt);
+    if (!has1) {
+      On.a = null_r;
+      On.bq = null_r;
+      On.bs = null_r;
+    }
+    const Operands O = with(cur);
+    floatx16 acc[4][2] = {};
+    switch (tile_blocks(cur.nrows)) {
+      case 1: tile_mma_chain<false, 1, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
+      case 2: tile_mma_chain<false, 2, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
+      case 3: tile_mma_chain<false, 3, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
+      default: tile_mma_chain<false, 4, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
+    }
+    DownTile d;
+    d.y = cur.y;
+    d.nrows = cur.nrows;
+    d.m0 = cur.m0;
+    d.nt = cur.nt;
+    d.shared = cur.shared;
+    down_store(p, d, G, acc);
+    cur = nxt;
+    G = __uint_as_float(__builtin_amdgcn_readfirstlane(g1)) * p.g_mid;
+    lt = lt1;
+    lt1 = lt2;
+    te1 = te2;
+    return has1;
+  };
+  for (;;) {
+    if (!item(IntC<0>{})) break;
+    if (!item(IntC<kNm3>{})) break;
+    if (!item(IntC<(2 * kNm3) % 3>{})) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no transfer into LDS outlives the workgroup
 }
 
 // ---------------------------------------------------------------- launchers
@@ -564,6 +806,21 @@ hipError_t launch_pack_kmajor(const uint8_t* codes, const uint8_t* scales, int n
   return hipGetLastError();
 }
 
+// Workgroups of a chained kernel: two per CU (what its LDS ring allows), at
+// most one per work item, a multiple of 8 (the XCDs take workgroups in turn).
+static int chain_grid(int64_t items) {
+  static int cus[16] = {};  // per device; every thread that fills it writes the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int c = dev < 16 ? cus[dev] : 0;
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    if (dev < 16) cus[dev] = c;
+  }
+  const int64_t g = items < 2 * (int64_t)c ? items : 2 * (int64_t)c;
+  return (int)((g + 7) / 8 * 8);
+}
+
 hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t s, hipEvent_t* ev) {
   const int64_t max_tiles = mfma_max_tiles(p.T, p.k, p.E, p.has_shared);
   int4* tile_tab = reinterpret_cast<int4*>(tile_start + tile_tab_offset(p.E));
@@ -573,8 +830,16 @@ hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t 
   e = launch_timed(k_gateup_mfma, dim3((unsigned)(max_tiles * (p.I / 128))), dim3(256), 0, s, ev ? ev[2] : nullptr,
                    ev ? ev[3] : nullptr, p, (const int32_t*)tile_start, (const int4*)tile_tab);
   if (e != hipSuccess) return e;
-  return launch_timed(k_down_mfma, dim3((unsigned)(max_tiles * (p.H / kBN))), dim3(256), 0, s, ev ? ev[4] : nullptr,
-                      ev ? ev[5] : nullptr, p, (const int32_t*)tile_start, (const int4*)tile_tab);
+  const int64_t items = max_tiles * (p.H / kBN);
+  const int n = (p.kc1 - p.kc0) / kBK;
+  // the chained kernel: at least two K steps per item, both banks in one layout
+  if (n < 2 || (p.w2k.codes != nullptr) != (p.sh2k.codes != nullptr))
+    return launch_timed(k_down_mfma, dim3((unsigned)items), dim3(256), 0, s, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr,
+                        p, (const int32_t*)tile_start, (const int4*)tile_tab);
+  const dim3 g((unsigned)chain_grid(items));
+  auto k = n % 3 == 0 ? k_down_mfma_chain<0> : n % 3 == 1 ? k_down_mfma_chain<1> : k_down_mfma_chain<2>;
+  return launch_timed(k, g, dim3(256), 0, s, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr, p,
+                      (const int32_t*)tile_start, (const int4*)tile_tab);
 }
 
 }  // namespace moe

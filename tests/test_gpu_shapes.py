@@ -6,6 +6,10 @@ reach (every kernel the library can launch is compared with the oracle somewhere
     generic expert kernels (k_ffn_gateup, k_ffn_down) at 3, 20 and 300 tokens,
     the tiled FP32 router pass with the general selection kernel, and K-split
     partials of the down projection on the generic kernels;
+  * K-split partials on the matrix-core path (H 2048, I 512, 40 tokens) over 3, 1
+    and 5 K steps per tile: the chained down kernel at each of its three ring
+    phase patterns (steps mod 3 = 0 and 2 here, 1 in the split-K rounding check)
+    and the one-item kernel for a single step;
   * more than 512 experts: 1,024 experts at 4 tokens (the FP64 router with the
     serial top-k over 16 logits per lane, the one-workgroup permutation over 1,024
     experts, the decode kernels' slot search) and at 300 tokens (the matrix-core
@@ -62,6 +66,17 @@ def test_generic_kernels_krange(T, kb):
     gh.log("case: generic kernels K-split H=288 I=96 T=%d blocks %s" % (T, kb))
     L, DL = layer_for("odd", ODD, 0)
     x = gen.make_tokens(0, T, step=32, H=ODD.H)
+    g = gh.run_layer(DL, x, dump=("xq", "xs", "hq", "hs"))
+    part = gh.run_krange(DL, x, kb[0], kb[1])
+    rep = gh.check_krange(L, x, g, part, kb[0], kb[1])
+    gh.log("  ", rep.line())
+
+
+@pytest.mark.parametrize("kb", [(0, 12), (4, 8), (8, 28)])
+def test_mfma_krange(kb):
+    gh.log("case: matrix-core K-split H=2048 I=512 T=40 blocks %s" % (kb,))
+    L, DL = layer_for("dec", gen.SHAPES[1], 1)
+    x = gen.make_tokens(1, 40, step=34)
     g = gh.run_layer(DL, x, dump=("xq", "xs", "hq", "hs"))
     part = gh.run_krange(DL, x, kb[0], kb[1])
     rep = gh.check_krange(L, x, g, part, kb[0], kb[1])
