@@ -270,15 +270,28 @@ __device__ __forceinline__ Operands pick(bool c, const Operands& A, const Operan
 // The K loop of one tile in a workgroup that runs several tiles with one ring:
 // the tile's first two steps are already in flight (issued by the previous
 // tile's last two steps, or by the workgroup's prologue), and its last two
-// steps issue the next tile's first two from On (whose resources hold no bytes
-// when there is no next tile).  kPh: the ring stage of step 0; kNm3 = n % 3,
-// n >= 2 steps from k_begin (the same K range for every tile).  No wait at the
-// end: the next tile's transfers stay in flight through this tile's epilogue.
-template <bool kTransposed, int kRB, int kPh, int kNm3, typename BRow>
-__device__ __forceinline__ void tile_mma_chain(const Operands& O, const Operands& On, int k_begin, int n, Ring& ring,
+// steps issue the next tile's first two.  make_on() returns the next tile's
+// operands (resources of no bytes when there is none); it runs after the
+// first step's barrier, so loads issued before this loop for it have
+// completed by then.  kPh: the ring stage of step 0; kNm3 = n % 3, n >= 3
+// steps from k_begin (the same K range for every tile).  No wait at the end:
+// the next tile's transfers stay in flight through this tile's epilogue.
+template <bool kTransposed, int kRB, int kPh, int kNm3, typename BRow, typename MakeOn>
+__device__ __forceinline__ void tile_mma_chain(const Operands& O, MakeOn make_on, int k_begin, int n, Ring& ring,
                                                BRow bj, floatx16 (&acc)[4][2]) {
+  // (an empty statement that differs per kRB: without it the compiler hoists
+  // the identical first transfers of the kRB variants above the branch that
+  // picks one, and then makes every variant but one wait for all transfers)
+  asm volatile("; kRB %0" ::"n"(kRB));
+  dma_step(O, true, (uint32_t)(k_begin + 2 * kBK), ring.at<kPh + 2>());
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<kTransposed, kRB>(ring.at<kPh>(), bj, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  ring_barrier<7>();
+  const Operands On = make_on();
+  // steps t = 1 + 3 m + pc: stage (kPh + 1 + pc) % 3
   auto phase = [&](auto pc, int t) {
-    constexpr int P = kPh + decltype(pc)::value;  // stage of step t: (kPh + t) % 3
+    constexpr int P = kPh + 1 + decltype(pc)::value;
     const bool own = t + 2 < n;
     const uint32_t k0 = (uint32_t)(k_begin + (own ? t + 2 : t + 2 - n) * kBK);
     dma_step(pick(own, O, On), true, k0, ring.at<P + 2>());
@@ -287,9 +300,9 @@ __device__ __forceinline__ void tile_mma_chain(const Operands& O, const Operands
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier<7>();
   };
-  int t = 0;
+  int t = 1;
   for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
-  static_for<0, kNm3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
+  static_for<0, (kNm3 + 2) % 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
 }
 
 // ---------------------------------------------------------------- G1
@@ -573,7 +586,8 @@ __device__ __forceinline__ void down_store(const FfnParams& p, const DownTile& d
     }
 }
 
-// One work item per workgroup (the K ranges of one step: a K-split partial).
+// One work item per workgroup (K ranges of one or two steps: K-split partials;
+// banks in different layouts).
 __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
                                                       const int4* __restrict__ tile_tab) {
   __shared__ __align__(16) Stage st0, st1, st2;
@@ -598,7 +612,7 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
 }
 
 // The same work items with a grid of two workgroups per CU (K ranges of at
-// least two steps, routed and shared banks in the same layout).  XCD x
+// least three steps, routed and shared banks in the same layout).  XCD x
 // (= blockIdx % 8) takes the same contiguous run of work items as in
 // k_down_mfma, and its gx workgroups take every gx-th item of it, so the items
 // in flight on an XCD stay neighbours (shared A rows and weights in its L2).
@@ -717,20 +731,23 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const i
     const u32x4 te2 = entry(lt2 < end ? lt2 : lt);
     const uint32_t g1 = gscale(t1);
     __builtin_amdgcn_sched_barrier(0);
-    ChainItem nxt = make_item(t1, lt1);
-    Operands On = with(nxt);
-    if (!has1) {
-      On.a = null_r;
-      On.bq = null_r;
-      On.bs = null_r;
-    }
+    const ChainItem nxt = make_item(t1, lt1);
+    auto make_on = [&] {
+      Operands On = with(nxt);
+      if (!has1) {
+        On.a = null_r;
+        On.bq = null_r;
+        On.bs = null_r;
+      }
+      return On;
+    };
     const Operands O = with(cur);
     floatx16 acc[4][2] = {};
     switch (tile_blocks(cur.nrows)) {
-      case 1: tile_mma_chain<false, 1, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
-      case 2: tile_mma_chain<false, 2, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
-      case 3: tile_mma_chain<false, 3, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
-      default: tile_mma_chain<false, 4, kPh, kNm3>(O, On, p.kc0, n, ring, down_bj, acc); break;
+      case 1: tile_mma_chain<false, 1, kPh, kNm3>(O, make_on, p.kc0, n, ring, down_bj, acc); break;
+      case 2: tile_mma_chain<false, 2, kPh, kNm3>(O, make_on, p.kc0, n, ring, down_bj, acc); break;
+      case 3: tile_mma_chain<false, 3, kPh, kNm3>(O, make_on, p.kc0, n, ring, down_bj, acc); break;
+      default: tile_mma_chain<false, 4, kPh, kNm3>(O, make_on, p.kc0, n, ring, down_bj, acc); break;
     }
     DownTile d;
     d.y = cur.y;
@@ -832,8 +849,8 @@ hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t 
   if (e != hipSuccess) return e;
   const int64_t items = max_tiles * (p.H / kBN);
   const int n = (p.kc1 - p.kc0) / kBK;
-  // the chained kernel: at least two K steps per item, both banks in one layout
-  if (n < 2 || (p.w2k.codes != nullptr) != (p.sh2k.codes != nullptr))
+  // the chained kernel: at least three K steps per item, both banks in one layout
+  if (n < 3 || (p.w2k.codes != nullptr) != (p.sh2k.codes != nullptr))
     return launch_timed(k_down_mfma, dim3((unsigned)items), dim3(256), 0, s, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr,
                         p, (const int32_t*)tile_start, (const int4*)tile_tab);
   const dim3 g((unsigned)chain_grid(items));
