@@ -37,8 +37,10 @@ constexpr int kBM = 128, kBN = 256, kBK = 64;  // tile rows, tile B rows (column
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 
-// The tile table follows tile_start ([E + 2] int32) in the workspace, 16-byte aligned.
-__host__ __device__ inline int tile_tab_offset(int E) { return (E + 2 + 3) / 4 * 4; }
+// In the workspace: tile_start ([E + 2] int32), the chained kernels' work
+// counters (kCounters int32), then the tile table, 16-byte aligned.
+constexpr int kCounters = 16;
+__host__ __device__ inline int tile_tab_offset(int E) { return (E + 2 + kCounters + 3) / 4 * 4; }
 
 }  // namespace
 
@@ -66,6 +68,7 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
     __syncthreads();
   }
   if (tid <= E + 1) tile_start[tid] = tid > 0 ? part[tid - 1] : 0;
+  if (tid < kCounters) tile_start[E + 2 + tid] = 0;  // the work counters start at zero
   const int total = part[E];
   for (int mt = tid; mt < total; mt += 1024) {
     int lo = 0, hi = E;  // first segment whose inclusive tile count exceeds mt
@@ -636,7 +639,8 @@ struct ChainItem {
 
 template <int kNm3>
 __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const int32_t* __restrict__ tile_start,
-                                                            const int4* __restrict__ tile_tab) {
+                                                            const int4* __restrict__ tile_tab,
+                                                            int32_t* __restrict__ counters) {
   __shared__ __align__(16) Stage st0, st1, st2;
   Ring ring{st0, st1, st2};
   const int H = p.H, I = p.I, E = p.E;
@@ -648,6 +652,12 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const i
   const int run0 = x * q + (x < r ? x : r), end = run0 + q + (x < r ? 1 : 0);
   int lt = run0 + ((int)blockIdx.x >> 3);
   if (lt >= end) return;
+  // a workgroup's first three items are lt, lt + gx, lt + 2 gx; after those
+  // it takes the XCD's next item from a counter, so the items in flight stay
+  // consecutive and a slow item delays only its own workgroup
+  __shared__ int next_slot;
+  int32_t* const ctr = counters + x;
+  const int dyn0 = run0 + 3 * gx;
   const int n = (p.kc1 - p.kc0) / kBK;
   const bool km = p.w2k.codes != nullptr;  // the shared bank's layout is the same
   const uint8_t* const rq = km ? p.w2k.codes : p.w2.codes;
@@ -715,8 +725,13 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const i
   const int4 te0 = uniform(entry(lt));
   ChainItem cur = make_item(te0, lt);
   float G = __uint_as_float(__builtin_amdgcn_readfirstlane(gscale(te0))) * p.g_mid;
-  int lt1 = lt + gx;
-  u32x4 te1 = entry(lt1 < end ? lt1 : lt);
+  int lt1 = lt + gx, lt2 = lt1 + gx;
+  int4 te1 = uniform(entry(lt1 < end ? lt1 : lt));
+  // a zero the compiler cannot see through: with a uniform address it would
+  // widen the one-lane atomic below to a wave-wide one whose result it waits
+  // for at once
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
   dma_step(with(cur), true, (uint32_t)p.kc0, ring.at<0>());
   dma_step(with(cur), true, (uint32_t)(p.kc0 + kBK), ring.at<1>());
   ring_barrier<7>();
@@ -724,15 +739,24 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const i
   auto item = [&](auto ph) -> bool {
     constexpr int kPh = decltype(ph)::value;
     const bool has1 = lt1 < end;
-    const int lt2 = lt1 + gx;
-    const int4 t1 = uniform(te1);  // loaded an item ago
+    const int4 t1 = te1;
     // loads for the next items, issued before this item's first transfers
-    // (its first barrier then covers them)
-    const u32x4 te2 = entry(lt2 < end ? lt2 : lt);
-    const uint32_t g1 = gscale(t1);
+    // (its first barrier then covers them), and the item after them from the
+    // counter (one lane; the value goes to the other waves through LDS).  All
+    // three are read out after the first step's barrier (make_on), where the
+    // compiler knows that they have completed.
+    const u32x4 te2v = entry(lt2 < end ? lt2 : lt);
+    const uint32_t g1v = gscale(t1);
+    int got;  // set and read by thread 0 only (no merge that would wait for the atomic here)
+    if (threadIdx.x == 0) got = __hip_atomic_fetch_add(ctr + zero, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_sched_barrier(0);
     const ChainItem nxt = make_item(t1, lt1);
+    int4 te2;
+    float g1;
     auto make_on = [&] {
+      if (threadIdx.x == 0) next_slot = dyn0 + got;  // read after the next barriers, at the item's end
+      te2 = uniform(te2v);
+      g1 = __uint_as_float(__builtin_amdgcn_readfirstlane(g1v));
       Operands On = with(nxt);
       if (!has1) {
         On.a = null_r;
@@ -757,9 +781,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma_chain(FfnParams p, const i
     d.shared = cur.shared;
     down_store(p, d, G, acc);
     cur = nxt;
-    G = __uint_as_float(__builtin_amdgcn_readfirstlane(g1)) * p.g_mid;
+    G = g1 * p.g_mid;
     lt = lt1;
     lt1 = lt2;
+    lt2 = __builtin_amdgcn_readfirstlane(next_slot);
     te1 = te2;
     return has1;
   };
@@ -856,7 +881,7 @@ hipError_t launch_ffn_mfma(const FfnParams& p, int32_t* tile_start, hipStream_t 
   const dim3 g((unsigned)chain_grid(items));
   auto k = n % 3 == 0 ? k_down_mfma_chain<0> : n % 3 == 1 ? k_down_mfma_chain<1> : k_down_mfma_chain<2>;
   return launch_timed(k, g, dim3(256), 0, s, ev ? ev[4] : nullptr, ev ? ev[5] : nullptr, p,
-                      (const int32_t*)tile_start, (const int4*)tile_tab);
+                      (const int32_t*)tile_start, (const int4*)tile_tab, tile_start + p.E + 2);
 }
 
 }  // namespace moe
