@@ -12,9 +12,9 @@
  *   [R1] capy-flash README v0.5.4 (spark.entire.vc), "What it does": routed
  *        experts partitioned by expert id; experts not resident computed with
  *        the GPU's W4A4 activation quantization.
- *   [R2] capy-flash README v0.5.4, "Serve": the CPU path quantizes activations
- *        like the GPU path (W4A4), so the output does not depend on where an
- *        expert ran.
+ *   [R2] capy-flash README v0.5.4, "Serve": host-side experts encode their
+ *        activations to 4 bits exactly as the GPU kernels do (W4A4), which
+ *        makes an expert's result independent of the device that ran it.
  *   [R3] capy-flash README v0.5.4, synthetic test-artifact script: 512 NVFP4
  *        experts, top-10 routed plus a shared expert.
  *   [A1] Richland article, "What shipped": 48 MoE layers, 512 experts, 10

@@ -380,17 +380,25 @@ def test_pack_kmajor_layout():
 @pytest.mark.parametrize("cfg,T", [(0, 300), (2, 4096)])
 def test_kmajor_copies_give_identical_results(cfg, T):
     """The matrix-core kernels read the row-major banks or their K-step-major copies
-    with the same arithmetic: every output is bit-identical, and so is the split-K
+    with the same arithmetic: every output is bit-identical (also with the routed
+    banks in one layout and the shared banks in the other), and so is the split-K
     partial of the down projection."""
     gh.log("case: config %d T=%d, row-major vs K-step-major weights" % (cfg, T))
     L, DLk = layer_for(cfg)
     assert DLk.desc.w13k.codes is not None
     DLr = gh.device_layer(L, kmajor=False)
+    # routed banks K-step-major, shared banks row-major (the matrix-core
+    # kernels that take one layout for both are then not used)
+    DLm = gh.device_layer(L)
+    DLm.desc.sh13k = moe.Bank()
+    DLm.desc.sh2k = moe.Bank()
     x = gen.make_tokens(cfg, T, step=11)
     a = gh.run_layer(DLr, x, dump=("hq", "hs"))
     b = gh.run_layer(DLk, x, dump=("hq", "hs"))
+    m = gh.run_layer(DLm, x, dump=("hq", "hs"))
     for key in ("y_rows", "y_shared", "out", "hq", "hs"):
         assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(m[key], b[key]), key
     half = L.shape.I // 32
     xd = gh.to_dev(x.view(np.int16))
     outs = []
