@@ -8,7 +8,9 @@ work in between (other layer calls on the same weights, and the graph's
 outputs overwritten with garbage), and compares every replay's routing,
 weights and output bits with the eager results.  Cases: the fused decode call
 at 1 and 4 tokens; the four separate calls at 20 tokens (weight-streaming
-kernels) and at 300 tokens (matrix-core kernels).
+kernels) and at 300 tokens (matrix-core kernels: the one-tile down kernel on
+the small shape, the persistent down kernel with its work counters on the
+decode shape).
 """
 import numpy as np
 import pytest
@@ -38,7 +40,7 @@ def _snapshot(bufs):
              b.out.cpu().numpy().view(np.uint16).copy()) for b in bufs]
 
 
-@pytest.mark.parametrize("cfg,T,fused", [(1, 1, True), (1, 4, True), (1, 20, False), (0, 300, False)])
+@pytest.mark.parametrize("cfg,T,fused", [(1, 1, True), (1, 4, True), (1, 20, False), (0, 300, False), (1, 300, False)])
 def test_graph_replays_match_eager(cfg, T, fused):
     gh.log("case: HIP graph, config %d T=%d %s" % (cfg, T, "moe_layer_forward" if fused else "four calls"))
     L = gen.make_layer(cfg)
