@@ -81,7 +81,8 @@ __global__ __launch_bounds__(1024) void k_tile_map(const int32_t* __restrict__ o
   }
 }
 
-// LDS ring of kStages K steps.  Each stage holds the tile's A rows (128 rows x 64
+// LDS ring of kStages K steps (the down GEMM's; the gate/up ring holds only A,
+// see StageA).  Each stage holds the tile's A rows (128 rows x 64
 // FP16 = 128 B, as 8 chunks of 16 B; chunk c of row r sits in slot
 // c ^ (r % 8) ^ (r / 8 % 2), so that the MFMA reads of 16 consecutive rows hit 16
 // different 16-byte bank groups), the step's 32 B of codes of each of the 256 B
@@ -308,6 +309,120 @@ __device__ __forceinline__ void tile_mma_chain(const Operands& O, MakeOn make_on
   static_for<0, (kNm3 + 2) % 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
 }
 
+
+// The gate/up GEMM's ring holds only A: each lane's B codes (16 B per column
+// block) and scale words go straight from memory into registers, three
+// register sets for the three steps in flight.  A wave's B rows are its own
+// (no other wave reads them), so staging them in LDS only added LDS traffic
+// (a fifth of the ring's writes and reads); the ring then takes 48 KB.
+struct StageA {
+  uint4 a[kBM * 8];
+};
+struct RingA {
+  StageA& st0;
+  StageA& st1;
+  StageA& st2;
+  template <int kS>
+  __device__ __forceinline__ StageA& at() {
+    if constexpr (kS % kStages == 0) return st0;
+    else if constexpr (kS % kStages == 1) return st1;
+    else return st2;
+  }
+};
+struct OperandsR {
+  __amdgpu_buffer_rsrc_t a, bq, bs;
+  __amdgpu_buffer_rsrc_t a0, bq0, bs0;
+  uint32_t adma[4];
+  uint32_t boff[2], soff[2];  // the lane's B code and scale word offsets, column blocks j = 0, 1
+  uint32_t bmul;
+};
+
+// mma_step with B from registers: bq[j] the lane's 16 code bytes of column
+// block j, sc[j] the step's four scale codes of its B row
+template <bool kTransposed, int kRB>
+__device__ __forceinline__ void mma_step_r(StageA& S, const uint4 (&bq)[2], const uint32_t (&sc)[2],
+                                           floatx16 (&acc)[4][2]) {
+  const int lane = lane_id();
+  const int hk = lane >> 5;
+  half2_t sv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sv[j] = ue4m3x2_to_half2(sc[j] >> (16 * hk));
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    half8_t a[4];
+#pragma unroll
+    for (int i = 0; i < kRB; ++i) {
+      const int row = 32 * i + (lane & 31);
+      a[i] = __builtin_bit_cast(half8_t, S.a[row * 8 + ((4 * hk + s4) ^ (lane & 7) ^ ((lane >> 3) & 1))]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const half2_t S2 = half2_t{sv[j][s4 >> 1], sv[j][s4 >> 1]};
+      const uint32_t w = s4 == 0 ? bq[j].x : s4 == 1 ? bq[j].y : s4 == 2 ? bq[j].z : bq[j].w;
+      const half2_t c0 = fp4x2<0>(w) * S2, c1 = fp4x2<1>(w) * S2, c2 = fp4x2<2>(w) * S2, c3 = fp4x2<3>(w) * S2;
+      const half8_t b = half8_t{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+#pragma unroll
+      for (int i = 0; i < kRB; ++i) {
+        if (kTransposed)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a[i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// tile_mma with the A-only ring: per step and wave 4 A transfers into LDS and
+// 4 B loads into registers (the last two steps' through resources of no
+// bytes, as in tile_mma), one barrier per step after the wave's 8 newest
+// loads at most are left in flight.
+template <bool kTransposed, int kRB>
+__device__ __forceinline__ void tile_mma_r(const OperandsR& O, int k_begin, int K, RingA& ring,
+                                           floatx16 (&acc)[4][2]) {
+  const int n = K / kBK;
+  const int wave = threadIdx.x >> 6;
+  auto kof = [&](int t) { return (uint32_t)(k_begin + (t < n ? t : n - 1) * kBK); };
+  uint4 bq[3][2];
+  uint32_t sc[3][2];
+  auto dma = [&](int t, StageA& S, bool real) {
+    const uint32_t k0 = kof(t);
+    const __amdgpu_buffer_rsrc_t ra = real ? O.a : O.a0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)&S.a[(32 * wave + 8 * c) * 8], 16, O.adma[c], k0 * 2, 0,
+                                               0);
+  };
+  auto loadb = [&](int t, uint4 (&q)[2], uint32_t (&s)[2], bool real) {
+    const uint32_t k0 = kof(t);
+    const __amdgpu_buffer_rsrc_t rq = real ? O.bq : O.bq0, rs = real ? O.bs : O.bs0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) q[j] = buffer_load16(rq, O.boff[j], k0 / 2 * O.bmul);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) s[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, O.soff[j], k0 / 16 * O.bmul, 0);
+  };
+  dma(0, ring.at<0>(), true);
+  loadb(0, bq[0], sc[0], true);
+  dma(1, ring.at<1>(), true);
+  loadb(1, bq[1], sc[1], true);
+  ring_barrier<8>();
+  auto phase = [&](auto pc, int t) {
+    constexpr int P = decltype(pc)::value;
+    dma(t + 2, ring.at<P + 2>(), t + 2 < n);
+    loadb(t + 2, bq[(P + 2) % 3], sc[(P + 2) % 3], t + 2 < n);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step_r<kTransposed, kRB>(ring.at<P>(), bq[P], sc[P], acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier<8>();
+  };
+  int t = 0;
+  for (; t + 3 <= n; t += 3) static_for<0, 3>([&](auto pc) { phase(pc, t + decltype(pc)::value); });
+  const int rem = n - t;
+  static_for<0, 2>([&](auto pc) {
+    if (decltype(pc)::value < rem) phase(pc, t + decltype(pc)::value);
+  });
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 // ---------------------------------------------------------------- G1
 // Tile: 128 rows x (128 gate + 128 up) columns; wave w holds h columns
 // nt*128 + 32 w .. + 31 of all 128 rows as gate block j = 0 and up block j = 1,
@@ -316,8 +431,8 @@ __device__ __forceinline__ void tile_mma_chain(const Operands& O, MakeOn make_on
 // operand.  Codes and scales are written only to the debug dumps.
 __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32_t* __restrict__ tile_start,
                                                         const int4* __restrict__ tile_tab) {
-  __shared__ __align__(16) Stage st0, st1, st2;
-  Ring ring{st0, st1, st2};
+  __shared__ __align__(16) StageA st0, st1, st2;
+  RingA ring{st0, st1, st2};
   const int H = p.H, I = p.I, T = p.T, E = p.E;
   const int n_nt = I / 128;
   const int nseg = E + 1;
@@ -341,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   // ring B row r: gate column nt*128 + r (r < 128), up column I + nt*128 + r - 128
   auto wrow = [&](int r) { return (uint32_t)(r < 128 ? nt * 128 + r : I + nt * 128 + (r - 128)); };
   auto bj = [&](int j) { return j == 0 ? wn : 128 + wn; };
-  Operands O;
+  OperandsR O;
   O.a = buffer_rsrc(p.xh, (uint32_t)T * H * 2u);
   O.a0 = buffer_rsrc(p.xh, 0u);
 #pragma unroll
@@ -356,19 +471,18 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mfma(FfnParams p, const int32
   O.bq0 = buffer_rsrc(codes, 0u);
   O.bs0 = buffer_rsrc(scales, 0u);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    // B transfer c: ring rows 64 w + 32 c + lane / 2, half (lane % 2) ^ (row / 4 % 2)
-    const int r = 64 * wave + 32 * c + (lane >> 1);
-    O.bdma[c] = wrow(r) * qrow + (uint32_t)((lane & 1) ^ (((r >> 2) ^ (r >> 3)) & 1)) * 16u;
+  for (int j = 0; j < 2; ++j) {
+    const int r = bj(j) + (lane & 31);
+    O.boff[j] = wrow(r) * qrow + (uint32_t)(lane >> 5) * 16u;
+    O.soff[j] = wrow(r) * srow;
   }
-  O.sdma = wrow(64 * wave + lane) * srow;
   O.bmul = km ? 2u * I : 1u;
   floatx16 acc[4][2] = {};
   switch (tile_blocks(seg_rows - m0)) {
-    case 1: tile_mma<true, 1>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
-    case 2: tile_mma<true, 2>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
-    case 3: tile_mma<true, 3>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
-    default: tile_mma<true, 4>(O, 0, H, seg_rows - m0, ring, bj, acc); break;
+    case 1: tile_mma_r<true, 1>(O, 0, H, ring, acc); break;
+    case 2: tile_mma_r<true, 2>(O, 0, H, ring, acc); break;
+    case 3: tile_mma_r<true, 3>(O, 0, H, ring, acc); break;
+    default: tile_mma_r<true, 4>(O, 0, H, ring, acc); break;
   }
   // Epilogue.  acc[i][j] is transposed: lane l holds row m = 32 i + l % 32
   // and h columns c(q) = nt*128 + wn + 8 (q / 4) + 4 (l / 32) + q % 4, so
