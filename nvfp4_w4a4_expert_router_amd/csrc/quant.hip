@@ -41,12 +41,14 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const uint32_t sc = scale_code(amax, g6);
   const float sv = ue4m3_value(sc);
-  const float s = sv * g;
+  // the block's seven threshold products once, then three comparisons per
+  // element (elem_code's thresholds and tie rules; scale code 0 encodes zeros)
+  const E2M1Thresholds Tb = e2m1_thresholds(sc ? sv * g : __builtin_inff());
   uint32_t packed[2] = {0u, 0u};
   uint32_t c[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    c[i] = elem_code(v[i], s);
+    c[i] = elem_code_t(v[i], Tb);
     packed[i >> 3] |= c[i] << (4 * (i & 7));
   }
   reinterpret_cast<uint2*>(codes)[b] = make_uint2(packed[0], packed[1]);
