@@ -731,8 +731,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnParams p, const int32_t
 // The same work items with a grid of two workgroups per CU (K ranges of at
 // least three steps, routed and shared banks in the same layout).  XCD x
 // (= blockIdx % 8) takes the same contiguous run of work items as in
-// k_down_mfma, and its gx workgroups take every gx-th item of it, so the items
-// in flight on an XCD stay neighbours (shared A rows and weights in its L2).
+// k_down_mfma; its gx workgroups start on the run's first 3 gx items (every
+// gx-th), then take the next item of the run from the XCD's counter, so the
+// items in flight on an XCD stay neighbours (shared A rows and weights in its
+// L2) and a slow item delays only its own workgroup.
 // The LDS ring runs on from one item into the next: an item's last two steps
 // transfer the next item's first two, so the next item's first transfers and
 // set-up overlap this item's last MFMAs and its row stores instead of
