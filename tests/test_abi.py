@@ -283,3 +283,16 @@ def test_package_refuses_to_load_without_the_library(tmp_path):
             "else:\n    print('loaded')\n") % str(tmp_path)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert "refused:" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
+
+
+def test_noalloc_token_bound():
+    """The allocation-free entry point's stated bound: its 64 MiB array holds the
+    workspace of 3,391 tokens at the decode shape, and 3,392 tokens are refused with
+    MOE_EWORKSPACE before anything touches the GPU."""
+    L = layer()
+    cap = moe.lib.moe_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    assert moe.lib.moe_workspace_bytes(ctypes.byref(L), 3391) <= cap < moe.lib.moe_workspace_bytes(ctypes.byref(L), 3392)
+    rc = moe.lib.moe_layer_forward_noalloc(ctypes.byref(L), FAKE, 3392, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, None, None)
+    assert rc == moe.MOE_EWORKSPACE
