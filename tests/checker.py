@@ -261,7 +261,7 @@ def _bf16_order(bits):
 
 
 def check_output(out_g_bits, out64, out16_o, rep: Report, v32=None, rel_l2_tol=2e-3, maxabs_rel=1e-2):
-    """The layer output against the oracle (SURVEY-style checker item 5).
+    """The layer output against the oracle: the output bars of the checker.
 
     out_g_bits: the GPU's BF16 output; out64 / out16_o: the oracle's FP64 value and
     its BF16 rounding; v32: the GPU's FP32 sum before its rounding (residual
